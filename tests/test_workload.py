@@ -1,0 +1,59 @@
+"""The seeded input generator: determinism, shapes, and the recipe's structure."""
+import torch
+
+from sparse_asymmetric_head_amd import workload as wl
+
+
+def test_configs_shapes():
+    c = wl.CONFIGS
+    assert [x.l_kv for x in c] == [1024, 32768, 131072, 131072, 65536]
+    assert [(x.h_q, x.h_k, x.h_v) for x in c] == [(4, 1, 2), (32, 4, 16), (32, 4, 16), (12, 1, 4),
+                                                  (32, 2, 32)]
+    assert [x.N for x in c] == [64, 256, 512, 512, 1024]
+    assert [x.R for x in c] == [1, 16, 16, 32, 64]
+    assert c[2].layers == 16 and c[4].heavy_tail
+
+
+def test_deterministic_and_seeded():
+    cfg = wl.CONFIGS[0]
+    a = wl.make_layer(cfg, 0)
+    b = wl.make_layer(cfg, 0)
+    c = wl.make_layer(cfg, 1)
+    for k in ("Q", "K", "V"):
+        assert torch.equal(a[k], b[k])
+        assert a[k].dtype == torch.bfloat16 and a[k].is_contiguous()
+    assert not torch.equal(a["K"], c["K"])
+    assert a["Q"].shape == (8, 1, 4, 64) and a["K"].shape == (1, 1, 1024, 64)
+    assert a["V"].shape == (1, 2, 1024, 64)
+
+
+def test_planted_keys_near_group_mean():
+    cfg = wl.CONFIGS[0]
+    x = wl.make_layer(cfg, 0)
+    q0 = x["Q"][0, 0].float()  # [h_q][d]
+    qbar = q0.mean(0)
+    K = x["K"][0, 0].float()
+    dist = (K - qbar[None]).norm(dim=1)
+    close = (dist < 0.3 * 64 ** 0.5 * 2.0).sum().item()
+    assert close == cfg.planted  # exactly the planted rows are near the group mean
+
+
+def test_query_drift_scale():
+    cfg = wl.CONFIGS[0]
+    Q = wl.make_layer(cfg, 0)["Q"].float()
+    step = (Q[1:] - Q[:-1]).std().item()
+    assert 0.03 < step < 0.08
+    assert 1.6 < Q[0].std().item() < 2.4
+
+
+def test_heavy_tail_planted():
+    x = wl.make_random(1, 4, 1, 2, 64, 512, seed=3, planted=64, heavy_tail=True)
+    assert x["K"].shape == (1, 1, 512, 64)
+    assert torch.isfinite(x["K"].float()).all()
+
+
+def test_dense_layer_shapes():
+    cfg = wl.CONFIGS[1].with_(l_kv=256)
+    x = wl.make_dense_layer(cfg, 0)
+    assert x["K"].shape == (1, 8, 256, 64) and x["V"].shape == (1, 8, 256, 64)
+    assert x["Q"].shape == (1, 32, 64)
