@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: microseconds per SAGA + Atop-N decode-attention step and achieved
+HBM bandwidth at 128K context on one MI355X.
+
+A step is one decode token through all layers of the workload: for each layer,
+the score/compare/compact pass over the key cache (with the exact threshold
+refresh on every R-th step) and the sparse softmax + gather-PV.  Inputs are
+seeded synthetic tensors already resident in HBM.  The dense full-attention
+GQA kernel runs on its own cache in the same process, and the fp64 CPU oracle
+is timed on a bounded sample on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "µs per decode-attention step and achieved HBM GB/s at 128K ctx, 1 MI355X"
+PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama32-1b-128k-16L")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--kernel-timing-steps", type=int, default=8)
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the SAGA decode step here runs on a single "
+              "MI355X with no collectives; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+    from sparse_asymmetric_head_amd import saga
+    from sparse_asymmetric_head_amd import workload as wl
+
+    saga.lib()  # fails loudly when the HIP library is missing
+    cfg = next((c for c in wl.CONFIGS if c.name == args.config), None)
+    if cfg is None:
+        print(f"unknown config {args.config}", file=sys.stderr)
+        return 2
+    ci = wl.config_index(cfg)
+    B, h_q, h_k, h_v, d, l_kv, N, R, T, L = (cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv,
+                                              cfg.N, cfg.R, cfg.steps, cfg.layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {cfg.name}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv} N={N} "
+        f"R={R} layers={L}")
+
+    # ------------------------------------------------------------ inputs
+    layers = [wl.make_layer(cfg, l, device=dev, cfg_index=ci) for l in range(L)]
+    Qall = torch.stack([x["Q"] for x in layers], dim=1).contiguous()  # [T][L][B][h_q][d]
+    Ks = [x["K"] for x in layers]
+    Vs = [x["V"] for x in layers]
+    torch.cuda.synchronize()
+    log("inputs generated")
+
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N), dev)
+    taus = torch.zeros(L, B, h_q, dtype=torch.float32, device=dev)
+    Os = torch.empty(L, B, h_q, d, dtype=torch.float32, device=dev)
+    cnts = torch.empty(L, B, h_q, dtype=torch.int32, device=dev)
+    qbuf = torch.empty(L, B, h_q, d, dtype=torch.bfloat16, device=dev)
+
+    def layer_pass(refresh: bool):
+        for l in range(L):
+            saga.saga_decode_step(qbuf[l], Ks[l], Vs[l], N, taus[l], refresh, Os[l], cnts[l], ws)
+
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        qbuf.copy_(Qall[0])
+        layer_pass(True)  # eager first call: loads the kernels
+        layer_pass(False)
+    stream.synchronize()
+    graphs = {}
+    if not args.no_graph:
+        for refresh in (True, False):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                layer_pass(refresh)
+            graphs[refresh] = g
+        log("graphs captured")
+
+    def step(t: int):
+        qbuf.copy_(Qall[t % T])
+        refresh = (t % R) == 0
+        if graphs:
+            graphs[refresh].replay()
+        else:
+            layer_pass(refresh)
+
+    sel_counts = []
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            step(t)
+        stream.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t_wall0 = time.perf_counter()
+        ev0.record(stream)
+        for t in range(args.warmup, args.warmup + args.steps):
+            step(t)
+        ev1.record(stream)
+        stream.synchronize()
+        t_wall1 = time.perf_counter()
+        gpu_ms = ev0.elapsed_time(ev1)
+        wall_ms = (t_wall1 - t_wall0) * 1e3
+        sel_counts.append(cnts.float().mean().item())
+    ms_per_step = max(gpu_ms, wall_ms) / args.steps
+    us_per_step = ms_per_step * 1e3
+    log(f"timed {args.steps} steps: {us_per_step:.1f} us/step (events {gpu_ms:.3f} ms, "
+        f"wall {wall_ms:.3f} ms)")
+
+    # ------------------------------------------------------------ kernel timing pass
+    # HIP events around every launch of the dominant kernel (the streaming
+    # compare-and-compact pass), on the stream it runs on.
+    kt = []
+    with torch.cuda.stream(stream):
+        pairs = []
+        for t in range(args.kernel_timing_steps):
+            qbuf.copy_(Qall[(args.warmup + args.steps + t) % T])
+            for l in range(L):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                saga.saga_select(qbuf[l], Ks[l], h_v, N, taus[l], False, ws, stream)
+                b.record(stream)
+                saga.saga_attend(Vs[l], B, h_q, h_k, N, Os[l], cnts[l], ws, stream)
+                pairs.append((a, b))
+        stream.synchronize()
+        kt = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    sel_us = sum(kt) / len(kt)
+    mean_count = sum(sel_counts) / len(sel_counts)
+
+    k_bytes = B * h_k * l_kv * d * 2
+    q_bytes = B * h_q * d * 2
+    tau_bytes = B * h_q * 4
+    o_bytes = B * h_q * d * 4
+    v_bytes = B * h_q * mean_count * d * 2
+    select_alg = k_bytes + q_bytes + tau_bytes
+    step_alg = L * (k_bytes + q_bytes + tau_bytes + o_bytes + v_bytes)
+    achieved = select_alg / (sel_us * 1e-6)
+    log(f"select kernel {sel_us:.2f} us/launch -> {achieved / 1e9:.0f} GB/s")
+
+    # ------------------------------------------------------------ dense baseline
+    dense = None
+    if cfg.dense_h_kv and not args.no_dense:
+        del layers
+        dl = [wl.make_dense_layer(cfg, l, device=dev, cfg_index=ci) for l in range(L)]
+        hk = cfg.dense_h_kv
+        dws = torch.empty(saga.saga_dense_workspace_bytes(B, h_q, hk, d, l_kv), dtype=torch.uint8,
+                          device=dev)
+        dO = torch.empty(L, B, h_q, d, dtype=torch.float32, device=dev)
+
+        def dense_pass():
+            for l in range(L):
+                saga.saga_dense_gqa_baseline(dl[l]["Q"], dl[l]["K"], dl[l]["V"], dO[l], dws)
+
+        with torch.cuda.stream(stream):
+            dense_pass()
+            stream.synchronize()
+            dg = None
+            if not args.no_graph:
+                dg = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(dg, stream=stream):
+                    dense_pass()
+            run = dg.replay if dg is not None else dense_pass
+            for _ in range(args.warmup):
+                run()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(args.steps):
+                run()
+            e1.record(stream)
+            stream.synchronize()
+            w1 = time.perf_counter()
+        dense_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3
+        dense_bytes = L * (2 * B * hk * l_kv * d * 2 + q_bytes + o_bytes)
+        dense = {"h_kv": hk, "us_per_step": round(dense_us, 2),
+                 "hbm_gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+                 "speedup_saga_vs_dense": round(dense_us / us_per_step, 3)}
+        log(f"dense GQA h_kv={hk}: {dense_us:.1f} us/step, speedup {dense_us / us_per_step:.2f}x")
+        del dl
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        lib = oracle.load()
+        S = max(1, min(args.cpu_sample_layers, L))
+        t_ref = t_two = 0.0
+        for l in range(S):
+            x = wl.make_layer(cfg, l, device=dev, cfg_index=ci, steps=2)
+            Qh, Kh, Vh = (oracle._u16(x[k]) for k in ("Q", "K", "V"))
+            del x
+            c0 = time.perf_counter()
+            oracle.trajectory(Qh[:1], Kh, Vh, h_k, h_v, N, R, lib=lib)
+            c1 = time.perf_counter()
+            oracle.trajectory(Qh[:2], Kh, Vh, h_k, h_v, N, R, lib=lib)
+            c2 = time.perf_counter()
+            t_ref += c1 - c0
+            t_two += c2 - c1
+        t_ref /= S
+        t_norm = max(t_two / S - t_ref, 0.0)
+        cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
+        cpu = {"value": round(cpu_us, 1), "unit": "us/step", "cores": oracle.num_threads(lib),
+               "kind": "oracle",
+               "sample": (f"{S} of {L} layers x (1 refresh step + 1 non-refresh step) of "
+                          f"{cfg.name}, per-layer costs amortised over R={R} and scaled to "
+                          f"{L} layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s "
+                          f"per layer-step)")}
+        log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(us_per_step, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "h_q": h_q, "h_k": h_k, "h_v": h_v, "d": d,
+                   "l_kv": l_kv, "N": N, "R": R, "layers": L, "global_batch": B,
+                   "seq_len": l_kv, "parallelism": "single-gpu"},
+        "hbm_gbps": round(step_alg / (us_per_step * 1e-6) / 1e9, 1),
+        "us_per_layer_step": round(us_per_step / L, 3),
+        "mean_survivors_per_row": round(mean_count, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_select (score + compare + compact)",
+                     "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+                     "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg},
+        "dense_gqa": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

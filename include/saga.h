@@ -1,0 +1,160 @@
+/*
+ * saga.h -- C ABI of the SAGA + Atop-N sparse decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("More Value per Key: Asymmetric Sparse Attention for Faster
+ * LLM Decoding", picx.dev summary):
+ *   - scores A = q K^T / sqrt(d) over h_k key heads        (eqs. 2-4)
+ *   - keep the entries of each score row with A >= tau,     (Methodology >
+ *     tau being the row's N-th largest score                 Atop-N, item 1;
+ *                                                            eq. 6)
+ *   - tau recomputed exactly once every R decode steps      (Atop-N, item 2)
+ *     and reused in between
+ *   - O = softmax(A[S]) V[S] over the survivors S, read     (Atop-N, eq. 7;
+ *     from h_v value heads, h_k <= h_v <= h_q                SAGA Architecture)
+ * Head map (the pages give none; this library's reading): query head j
+ * reads key head floor(j*h_k/h_q) and value head floor(j*h_v/h_q).
+ *
+ * Conventions for every entry point below:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *     16-byte aligned.  Layouts (row-major, innermost last):
+ *       Q   bf16  [B][h_q][d]          one decode step's queries
+ *       K   bf16  [B][h_k][l_kv][d]    key cache   (h_kv heads for dense)
+ *       V   bf16  [B][h_v][l_kv][d]    value cache (h_kv heads for dense)
+ *       tau fp32  [B][h_q]             per-row threshold (same units as A)
+ *       O   fp32  [B][h_q][d]          attention output
+ *       counts int32 [B][h_q]          |S| per row
+ *   - ws / ws_bytes: caller-owned device workspace of at least the size the
+ *     matching *_workspace_bytes() call returns.  Before its first use a
+ *     workspace must be cleared once with saga_workspace_init(); every call
+ *     leaves its internal counters back at zero, so no further clearing is
+ *     needed.  Calls that share one workspace must not overlap in time
+ *     (use one workspace per stream).
+ *   - hip_stream: a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued asynchronously; the library never allocates, frees or
+ *     synchronizes.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative saga_status and enqueues nothing.
+ *     Launch failures are reported as SAGA_ERR_HIP.
+ *   - Supported: d in {64, 128}; 1 <= h_k <= h_v <= h_q; h_q/h_k rounded up
+ *     <= 64; 1 <= N <= l_kv; l_kv * d * 2 < 2^31; B*h_q < 2^20.
+ */
+#ifndef SAGA_H
+#define SAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum saga_status {
+    SAGA_OK = 0,
+    SAGA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, inconsistent sizes */
+    SAGA_ERR_UNSUPPORTED = -2, /* valid for the method but outside the supported shapes */
+    SAGA_ERR_WORKSPACE = -3,   /* ws_bytes smaller than required */
+    SAGA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} saga_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *saga_status_string(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int saga_version(void);
+
+/* Bytes of workspace saga_decode_step / saga_refresh_threshold need for this
+ * shape (0 when the shape is invalid or unsupported).  Pure host function. */
+size_t saga_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N);
+
+/* Bytes of workspace saga_dense_gqa_baseline needs (0 when invalid). */
+size_t saga_dense_workspace_bytes(int B, int h_q, int h_kv, int d, int64_t l_kv);
+
+/* Zero the workspace's internal counters (enqueued on hip_stream with a fill
+ * kernel, so it may be captured in a HIP graph).  Call once per workspace. */
+int saga_workspace_init(void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Exact threshold refresh (Atop-N item 2; eq. 6):
+ *   tau[b][j] := the N-th largest of A[b][j][0..l_kv), A = q K^T / sqrt(d)
+ * computed in fp32 (bf16 products, fp32 accumulation, -0 canonicalised to
+ * +0), i.e. element N-1 of the row sorted in descending order, ties kept.
+ * The fp32 scores are left in the workspace (see saga_workspace_layout).
+ */
+int saga_refresh_threshold(const void *Q, const void *K, int B, int h_q, int h_k, int d,
+                           int64_t l_kv, int64_t N, float *tau, void *ws, size_t ws_bytes,
+                           void *hip_stream);
+
+/*
+ * One Atop-N decode step (Atop-N items 1-2, eq. 7):
+ *   if refresh != 0: tau is first recomputed from this step's scores exactly
+ *                    as saga_refresh_threshold does (tau is then an output);
+ *   S[b][j]   := { t : A[b][j][t] >= tau[b][j] }  (no cap on |S|);
+ *   O[b][j]   := sum_{t in S} softmax_S(A[b][j])_t * V[b][vh(j)][t]  (fp32),
+ *                or all zeros when S is empty;
+ *   counts[b][j] := |S|  (counts may be NULL).
+ * N is the row rank the refresh selects and sizes internal buffers.
+ */
+int saga_decode_step(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                     int h_v, int d, int64_t l_kv, int64_t N, float *tau, int refresh, float *O,
+                     int32_t *counts, void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * The two halves of saga_decode_step, for callers that want the selection on
+ * its own or time the stages separately.  saga_decode_step(...) is exactly
+ * saga_select(...) followed by saga_attend(...) on the same workspace.
+ *
+ * saga_select: (refresh as in saga_decode_step) scores, compare with tau and
+ *   compact the survivors S into the workspace's segments (layout below).
+ * saga_attend: O and counts from the segments the preceding saga_select on
+ *   this workspace left, for the same shape (eq. 7).
+ */
+int saga_select(const void *Q, const void *K, int B, int h_q, int h_k, int h_v, int d,
+                int64_t l_kv, int64_t N, float *tau, int refresh, void *ws, size_t ws_bytes,
+                void *hip_stream);
+
+int saga_attend(const void *V, int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N,
+                float *O, int32_t *counts, void *ws, size_t ws_bytes, void *hip_stream);
+
+/*
+ * Dense full-attention GQA decode, the in-run baseline (eqs. 2-4):
+ *   O[b][j] := softmax(q K_g^T / sqrt(d)) V_g,  g = floor(j*h_kv/h_q),
+ * with K, V both [B][h_kv][l_kv][d] bf16; fp32 output.
+ */
+int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, int h_q,
+                            int h_kv, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
+                            void *hip_stream);
+
+/* Where the last call left its intermediate results inside the workspace
+ * (byte offsets from ws), for inspection and testing. */
+typedef struct saga_ws_layout {
+    size_t bytes;          /* total workspace size (= saga_workspace_bytes) */
+    size_t scores_off;     /* fp32 [B*h_q][scores_ld]: scores of the last refresh */
+    int64_t scores_ld;     /* row stride of the scores, in elements (>= l_kv) */
+    size_t seg_count_off;  /* int32 [B*h_q][n_seg]: survivors per (row, segment) */
+    size_t seg_maxkey_off; /* uint32 [B*h_q][n_seg]: order key of each segment's max score */
+    size_t seg_off;        /* int32 [B*h_q][n_seg][seg_cap]: survivor positions t */
+    size_t seg_score_off;  /* fp32 [B*h_q][n_seg][seg_cap]: their scores */
+    int64_t chunk_len;     /* cache positions per streaming block */
+    int64_t n_chunk;       /* blocks per key-head row: ceil(l_kv / chunk_len) */
+    int64_t n_seg;         /* segments per row (n_chunk * 4) */
+    int64_t seg_cap;       /* capacity of one segment (chunk_len / 4) */
+} saga_ws_layout;
+
+/* Fill *out for this shape.  Returns SAGA_OK or a negative status. */
+int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N,
+                          saga_ws_layout *out);
+
+/*
+ * Expand the survivor segments of the last saga_decode_step on this
+ * workspace into a byte mask: mask[b][j][t] = 1 if t was in S[b][j], else 0.
+ * mask is a device pointer of B*h_q*l_kv bytes.  Enqueued on hip_stream.
+ */
+int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k, int h_v, int d,
+                        int64_t l_kv, int64_t N, uint8_t *mask, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGA_H */

@@ -1,0 +1,425 @@
+// saga.hip -- C-ABI host library for SAGA + Atop-N decode attention on
+// MI355X (gfx950).  Validates arguments, lays out the caller's workspace,
+// and enqueues the kernels of saga_kernels.hpp on the caller's stream.
+// Declarations and the contract of every entry point: include/saga.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/saga.h"
+#include "saga_kernels.hpp"
+
+namespace {
+
+using namespace saga;
+
+constexpr int kTargetSelectBlocks = 512;  // streaming blocks per step (2 per CU)
+constexpr int64_t kChunkUnit = 256;       // chunk_len granularity (positions)
+constexpr int64_t kHistBlock = 8192;      // positions per histogram/collect block
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+    int B, h_q, h_k, h_v, d;
+    int64_t l_kv, N;
+    int rows, gmax, nt;
+    int64_t chunk_len;
+    int n_chunk, n_sub;
+    int64_t sub_cap;
+    int pw;
+    int64_t ld_a;
+    int hist_bpr;
+    // byte offsets into the workspace
+    size_t off_ticket, off_hist, off_state, counters_end;
+    size_t off_partial, off_seg_count, off_seg_maxkey, off_seg_t, off_seg_s, off_scores, off_cand;
+    size_t total;
+};
+
+int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N) {
+    if (B < 1 || h_q < 1 || h_k < 1 || h_v < 1 || l_kv < 1 || N < 1) return SAGA_ERR_INVALID_ARG;
+    if (h_k > h_v || h_v > h_q) return SAGA_ERR_INVALID_ARG;
+    if (N > l_kv) return SAGA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
+    if (ceil_div(h_q, h_k) > 64) return SAGA_ERR_UNSUPPORTED;
+    if (l_kv * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
+    if ((int64_t)B * h_q >= (int64_t(1) << 20)) return SAGA_ERR_UNSUPPORTED;
+    return SAGA_OK;
+}
+
+int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, Plan *p) {
+    int st = check_shape(B, h_q, h_k, h_v, d, l_kv, N);
+    if (st != SAGA_OK) return st;
+    memset(p, 0, sizeof *p);
+    p->B = B, p->h_q = h_q, p->h_k = h_k, p->h_v = h_v, p->d = d, p->l_kv = l_kv, p->N = N;
+    p->rows = B * h_q;
+    p->gmax = (int)ceil_div(h_q, h_k);
+    p->nt = p->gmax <= 16 ? 1 : (p->gmax <= 32 ? 2 : 4);
+    // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
+    // pairs, and at most kMaxSub/kWaves chunks per row.
+    const int64_t pairs = (int64_t)B * h_k;
+    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), kChunkUnit) * kChunkUnit;
+    const int64_t cl_min = ceil_div(ceil_div(l_kv, kMaxSub / kWaves), kChunkUnit) * kChunkUnit;
+    if (cl < cl_min) cl = cl_min;
+    if (cl < kChunkUnit) cl = kChunkUnit;
+    p->chunk_len = cl;
+    p->n_chunk = (int)ceil_div(l_kv, cl);
+    p->n_sub = p->n_chunk * kWaves;
+    p->sub_cap = cl / kWaves;
+    int64_t pw = ceil_div(N, 64);
+    p->pw = (int)(pw < 1 ? 1 : (pw > 64 ? 64 : pw));
+    p->ld_a = ceil_div(l_kv, 64) * 64;
+    p->hist_bpr = (int)ceil_div(l_kv, kHistBlock);
+
+    const size_t rows = (size_t)p->rows;
+    size_t o = 0;
+    p->off_ticket = o;
+    o = align_up(o + rows * sizeof(uint32_t));
+    p->off_hist = o;
+    o = align_up(o + rows * kHistBins * sizeof(uint32_t));
+    p->off_state = o;
+    o = align_up(o + rows * 4 * sizeof(uint32_t));
+    p->counters_end = o;
+    p->off_partial = o;
+    o = align_up(o + rows * (size_t)p->pw * (d + 4) * sizeof(float));
+    p->off_seg_count = o;
+    o = align_up(o + rows * (size_t)p->n_sub * sizeof(int32_t));
+    p->off_seg_maxkey = o;
+    o = align_up(o + rows * (size_t)p->n_sub * sizeof(uint32_t));
+    const size_t seg_elems = rows * (size_t)p->n_sub * (size_t)p->sub_cap;
+    p->off_seg_t = o;
+    o = align_up(o + seg_elems * sizeof(int32_t));
+    p->off_seg_s = o;
+    o = align_up(o + seg_elems * sizeof(float));
+    p->off_scores = o;
+    o = align_up(o + rows * (size_t)p->ld_a * sizeof(float));
+    p->off_cand = o;
+    o = align_up(o + rows * (size_t)l_kv * sizeof(uint32_t));
+    p->total = o;
+    return SAGA_OK;
+}
+
+struct DensePlan {
+    int rows, gmax;
+    int64_t chunk_len;
+    int n_chunk;
+    size_t total;
+};
+
+int make_dense_plan(int B, int h_q, int h_kv, int d, int64_t l_kv, DensePlan *p) {
+    if (B < 1 || h_q < 1 || h_kv < 1 || h_kv > h_q || l_kv < 1) return SAGA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
+    if (ceil_div(h_q, h_kv) > 16) return SAGA_ERR_UNSUPPORTED;
+    if (l_kv * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
+    if ((int64_t)B * h_q >= (int64_t(1) << 20)) return SAGA_ERR_UNSUPPORTED;
+    p->rows = B * h_q;
+    p->gmax = (int)ceil_div(h_q, h_kv);
+    const int64_t pairs = (int64_t)B * h_kv;
+    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), kChunkUnit) * kChunkUnit;
+    const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kChunkUnit) * kChunkUnit;
+    if (cl < cl_min) cl = cl_min;
+    if (cl < kChunkUnit) cl = kChunkUnit;
+    p->chunk_len = cl;
+    p->n_chunk = (int)ceil_div(l_kv, cl);
+    p->total = align_up((size_t)p->rows * p->n_chunk * (d + 4) * sizeof(float));
+    return SAGA_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
+
+template <int D, int NT, bool MAT>
+void launch_select_t(const SelectArgs &a, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((k_select<D, NT, MAT>), dim3(blocks), dim3(kThreads), 0, s, a);
+}
+
+template <bool MAT>
+void launch_select(const Plan &p, const SelectArgs &a, hipStream_t s) {
+    const int blocks = p.B * p.h_k * p.n_chunk;
+    if (p.d == 64) {
+        if (p.nt == 1) launch_select_t<64, 1, MAT>(a, blocks, s);
+        else if (p.nt == 2) launch_select_t<64, 2, MAT>(a, blocks, s);
+        else launch_select_t<64, 4, MAT>(a, blocks, s);
+    } else {
+        if (p.nt == 1) launch_select_t<128, 1, MAT>(a, blocks, s);
+        else if (p.nt == 2) launch_select_t<128, 2, MAT>(a, blocks, s);
+        else launch_select_t<128, 4, MAT>(a, blocks, s);
+    }
+}
+
+SelectArgs select_args(const Plan &p, const void *Q, const void *K, const float *tau, char *ws) {
+    SelectArgs a;
+    a.Q = (const uint16_t *)Q;
+    a.K = (const uint16_t *)K;
+    a.tau = tau;
+    a.A = (float *)(ws + p.off_scores);
+    a.ld_a = p.ld_a;
+    a.B = p.B, a.h_q = p.h_q, a.h_k = p.h_k;
+    a.n_chunk = p.n_chunk;
+    a.l_kv = p.l_kv, a.chunk_len = p.chunk_len;
+    a.scale = (float)(1.0 / sqrt((double)p.d));
+    a.seg_t = (int32_t *)(ws + p.off_seg_t);
+    a.seg_s = (float *)(ws + p.off_seg_s);
+    a.seg_count = (int32_t *)(ws + p.off_seg_count);
+    a.seg_maxkey = (uint32_t *)(ws + p.off_seg_maxkey);
+    a.n_sub = p.n_sub;
+    a.sub_cap = p.sub_cap;
+    return a;
+}
+
+// Refresh: score pass writing fp32 A, then the exact radix select -> tau.
+int run_refresh(const Plan &p, const void *Q, const void *K, float *tau, char *ws,
+                hipStream_t s) {
+    SelectArgs sa = select_args(p, Q, K, nullptr, ws);
+    launch_select<true>(p, sa, s);
+    RadixArgs ra;
+    ra.A = (const float *)(ws + p.off_scores);
+    ra.ld_a = p.ld_a, ra.l_kv = p.l_kv, ra.N = p.N;
+    ra.rows = p.rows;
+    ra.bpr = p.hist_bpr;
+    ra.blk_len = kHistBlock;
+    ra.hist = (uint32_t *)(ws + p.off_hist);
+    ra.state = (uint32_t *)(ws + p.off_state);
+    ra.cand = (uint32_t *)(ws + p.off_cand);
+    ra.tau = tau;
+    hipLaunchKernelGGL(k_hist, dim3(p.rows * p.hist_bpr), dim3(kThreads), 0, s, ra);
+    hipLaunchKernelGGL(k_select1, dim3(p.rows), dim3(kThreads), 0, s, ra);
+    hipLaunchKernelGGL(k_collect, dim3(p.rows * p.hist_bpr), dim3(kThreads), 0, s, ra);
+    hipLaunchKernelGGL(k_select_final, dim3(p.rows), dim3(kThreads), 0, s, ra);
+    return launch_status();
+}
+
+int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws, hipStream_t s) {
+    AttendArgs aa;
+    aa.seg_t = (const int32_t *)(ws + p.off_seg_t);
+    aa.seg_s = (const float *)(ws + p.off_seg_s);
+    aa.seg_count = (const int32_t *)(ws + p.off_seg_count);
+    aa.seg_maxkey = (const uint32_t *)(ws + p.off_seg_maxkey);
+    aa.n_sub = p.n_sub;
+    aa.sub_cap = p.sub_cap;
+    aa.V = (const uint16_t *)V;
+    aa.B = p.B, aa.h_q = p.h_q, aa.h_v = p.h_v;
+    aa.l_kv = p.l_kv;
+    aa.pw = p.pw;
+    aa.partial = (float *)(ws + p.off_partial);
+    aa.ticket = (uint32_t *)(ws + p.off_ticket);
+    aa.O = O;
+    aa.counts = counts;
+    const int blocks = p.rows * p.pw;
+    if (p.d == 64)
+        hipLaunchKernelGGL(k_attend<64>, dim3(blocks), dim3(kThreads), 0, s, aa);
+    else
+        hipLaunchKernelGGL(k_attend<128>, dim3(blocks), dim3(kThreads), 0, s, aa);
+    return launch_status();
+}
+
+// Selection half of a step: refresh (score pass writing A, radix select,
+// compaction of A >= tau) or the streaming compare-and-compact pass.
+int run_select(const Plan &p, const void *Q, const void *K, float *tau, int refresh, char *w,
+               hipStream_t s) {
+    if (refresh) {
+        int st = run_refresh(p, Q, K, tau, w, s);
+        if (st != SAGA_OK) return st;
+        CompactArgs ca;
+        ca.A = (const float *)(w + p.off_scores);
+        ca.ld_a = p.ld_a, ca.l_kv = p.l_kv, ca.chunk_len = p.chunk_len;
+        ca.n_chunk = p.n_chunk;
+        ca.tau = tau;
+        ca.seg_t = (int32_t *)(w + p.off_seg_t);
+        ca.seg_s = (float *)(w + p.off_seg_s);
+        ca.seg_count = (int32_t *)(w + p.off_seg_count);
+        ca.seg_maxkey = (uint32_t *)(w + p.off_seg_maxkey);
+        ca.n_sub = p.n_sub;
+        ca.sub_cap = p.sub_cap;
+        hipLaunchKernelGGL(k_compact, dim3(p.rows * p.n_chunk), dim3(kThreads), 0, s, ca);
+    } else {
+        SelectArgs sa = select_args(p, Q, K, tau, w);
+        launch_select<false>(p, sa, s);
+    }
+    return launch_status();
+}
+
+int check_ws(const Plan &p, const void *ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, kAlign)) return SAGA_ERR_INVALID_ARG;
+    if (ws_bytes < p.total) return SAGA_ERR_WORKSPACE;
+    return SAGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *saga_status_string(int status) {
+    switch (status) {
+        case SAGA_OK: return "SAGA_OK";
+        case SAGA_ERR_INVALID_ARG: return "SAGA_ERR_INVALID_ARG";
+        case SAGA_ERR_UNSUPPORTED: return "SAGA_ERR_UNSUPPORTED";
+        case SAGA_ERR_WORKSPACE: return "SAGA_ERR_WORKSPACE";
+        case SAGA_ERR_HIP: return "SAGA_ERR_HIP";
+        default: return "SAGA_ERR_UNKNOWN";
+    }
+}
+
+int saga_version(void) { return 100; }
+
+size_t saga_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N) {
+    Plan p;
+    return make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p) == SAGA_OK ? p.total : 0;
+}
+
+size_t saga_dense_workspace_bytes(int B, int h_q, int h_kv, int d, int64_t l_kv) {
+    DensePlan p;
+    return make_dense_plan(B, h_q, h_kv, d, l_kv, &p) == SAGA_OK ? p.total : 0;
+}
+
+int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N,
+                          saga_ws_layout *out) {
+    if (!out) return SAGA_ERR_INVALID_ARG;
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    out->bytes = p.total;
+    out->scores_off = p.off_scores;
+    out->scores_ld = p.ld_a;
+    out->seg_count_off = p.off_seg_count;
+    out->seg_maxkey_off = p.off_seg_maxkey;
+    out->seg_off = p.off_seg_t;
+    out->seg_score_off = p.off_seg_s;
+    out->chunk_len = p.chunk_len;
+    out->n_chunk = p.n_chunk;
+    out->n_seg = p.n_sub;
+    out->seg_cap = p.sub_cap;
+    return SAGA_OK;
+}
+
+int saga_workspace_init(void *ws, size_t ws_bytes, void *hip_stream) {
+    if (!ws || !aligned(ws, kAlign) || ws_bytes == 0 || ws_bytes % 4) return SAGA_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const int64_t n = (int64_t)(ws_bytes / 4);
+    int blocks = (int)(ceil_div(n, kThreads) < 4096 ? ceil_div(n, kThreads) : 4096);
+    hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(kThreads), 0, s, (uint32_t *)ws, n, 0u);
+    return launch_status();
+}
+
+int saga_refresh_threshold(const void *Q, const void *K, int B, int h_q, int h_k, int d,
+                           int64_t l_kv, int64_t N, float *tau, void *ws, size_t ws_bytes,
+                           void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_k, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !tau || !aligned(Q, 16) || !aligned(K, 16) || !aligned(tau, 4))
+        return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    return run_refresh(p, Q, K, tau, (char *)ws, (hipStream_t)hip_stream);
+}
+
+int saga_select(const void *Q, const void *K, int B, int h_q, int h_k, int h_v, int d,
+                int64_t l_kv, int64_t N, float *tau, int refresh, void *ws, size_t ws_bytes,
+                void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !tau || !aligned(Q, 16) || !aligned(K, 16) || !aligned(tau, 4))
+        return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    return run_select(p, Q, K, tau, refresh, (char *)ws, (hipStream_t)hip_stream);
+}
+
+int saga_attend(const void *V, int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N,
+                float *O, int32_t *counts, void *ws, size_t ws_bytes, void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!V || !O || !aligned(V, 16) || !aligned(O, 4) || (counts && !aligned(counts, 4)))
+        return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    return run_attend(p, V, O, counts, (char *)ws, (hipStream_t)hip_stream);
+}
+
+int saga_decode_step(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                     int h_v, int d, int64_t l_kv, int64_t N, float *tau, int refresh, float *O,
+                     int32_t *counts, void *ws, size_t ws_bytes, void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !V || !tau || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(tau, 4) || !aligned(O, 4) || (counts && !aligned(counts, 4)))
+        return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    char *w = (char *)ws;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if ((st = run_select(p, Q, K, tau, refresh, w, s)) != SAGA_OK) return st;
+    return run_attend(p, V, O, counts, w, s);
+}
+
+int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, int h_q,
+                            int h_kv, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
+                            void *hip_stream) {
+    DensePlan p;
+    int st = make_dense_plan(B, h_q, h_kv, d, l_kv, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !V || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(O, 4))
+        return SAGA_ERR_INVALID_ARG;
+    if (!ws || !aligned(ws, kAlign)) return SAGA_ERR_INVALID_ARG;
+    if (ws_bytes < p.total) return SAGA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)hip_stream;
+    DenseArgs a;
+    a.Q = (const uint16_t *)Q, a.K = (const uint16_t *)K, a.V = (const uint16_t *)V;
+    a.B = B, a.h_q = h_q, a.h_kv = h_kv;
+    a.n_chunk = p.n_chunk;
+    a.l_kv = l_kv, a.chunk_len = p.chunk_len;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    a.partial = (float *)ws;
+    const int blocks = B * h_kv * p.n_chunk;
+#define SAGA_DENSE(DD, GG) \
+    hipLaunchKernelGGL((k_dense<DD, GG>), dim3(blocks), dim3(kThreads), 0, s, a)
+    if (d == 64) {
+        if (p.gmax <= 4) SAGA_DENSE(64, 4);
+        else if (p.gmax <= 8) SAGA_DENSE(64, 8);
+        else SAGA_DENSE(64, 16);
+    } else {
+        if (p.gmax <= 4) SAGA_DENSE(128, 4);
+        else if (p.gmax <= 8) SAGA_DENSE(128, 8);
+        else SAGA_DENSE(128, 16);
+    }
+#undef SAGA_DENSE
+    DenseMergeArgs m;
+    m.partial = (const float *)ws;
+    m.n_chunk = p.n_chunk;
+    m.O = O;
+    if (d == 64)
+        hipLaunchKernelGGL(k_dense_merge<64>, dim3(p.rows), dim3(kThreads), 0, s, m);
+    else
+        hipLaunchKernelGGL(k_dense_merge<128>, dim3(p.rows), dim3(kThreads), 0, s, m);
+    return launch_status();
+}
+
+int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k, int h_v, int d,
+                        int64_t l_kv, int64_t N, uint8_t *mask, void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!mask) return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const char *w = (const char *)ws;
+    const int64_t n = (int64_t)p.rows * l_kv;
+    int blocks = (int)(ceil_div(n, kThreads) < 4096 ? ceil_div(n, kThreads) : 4096);
+    hipLaunchKernelGGL(k_fill_u8, dim3(blocks), dim3(kThreads), 0, s, mask, n, (uint8_t)0);
+    MaskArgs ma;
+    ma.seg_t = (const int32_t *)(w + p.off_seg_t);
+    ma.seg_count = (const int32_t *)(w + p.off_seg_count);
+    ma.n_sub = p.n_sub;
+    ma.sub_cap = p.sub_cap;
+    ma.l_kv = l_kv;
+    ma.mask = mask;
+    hipLaunchKernelGGL(k_mask, dim3(p.rows * p.n_sub), dim3(kThreads), 0, s, ma);
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// saga_device.hpp -- device-side building blocks shared by the SAGA kernels
+// (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saga {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Order-preserving map of an fp32 value to an unsigned key: a < b as floats
+// (finite, -0 treated as its own bit pattern) iff key(a) < key(b) as integers.
+__device__ __forceinline__ uint32_t fkey(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of m strictly below this lane.
+__device__ __forceinline__ int mbcnt_lt(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// bf16 pair packed in a 32-bit word -> two floats (exact widening).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    for (int o = 32; o > 0; o >>= 1) {
+        uint32_t w = __shfl_xor(v, o);
+        v = v > w ? v : w;
+    }
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// First query head of key head g's group: ceil(g*h_q/h_k), so that
+// floor(j*h_k/h_q) == g  <=>  group_lo(g) <= j < group_lo(g+1).
+__device__ __forceinline__ int group_lo(int g, int h_q, int h_k) {
+    return (int)(((int64_t)g * h_q + h_k - 1) / h_k);
+}
+
+}  // namespace saga

@@ -1,0 +1,238 @@
+"""Thin Python binding of the SAGA C ABI (include/saga.h).
+
+Argument marshalling only: shapes are read off torch tensors, device pointers
+and the current HIP stream are passed through ctypes, status codes become
+exceptions.  Every step of the computation runs in the HIP library
+(``lib/libsaga.so``); if that library is missing this module raises -- there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libsaga.so")
+
+SAGA_OK = 0
+SAGA_ERR_INVALID_ARG = -1
+SAGA_ERR_UNSUPPORTED = -2
+SAGA_ERR_WORKSPACE = -3
+SAGA_ERR_HIP = -4
+
+EXPORTS = (
+    "saga_status_string", "saga_version", "saga_workspace_bytes", "saga_dense_workspace_bytes",
+    "saga_workspace_init", "saga_refresh_threshold", "saga_decode_step",
+    "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
+    "saga_attend",
+)
+
+
+class SagaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [
+        ("bytes", ctypes.c_size_t),
+        ("scores_off", ctypes.c_size_t),
+        ("scores_ld", ctypes.c_int64),
+        ("seg_count_off", ctypes.c_size_t),
+        ("seg_maxkey_off", ctypes.c_size_t),
+        ("seg_off", ctypes.c_size_t),
+        ("seg_score_off", ctypes.c_size_t),
+        ("chunk_len", ctypes.c_int64),
+        ("n_chunk", ctypes.c_int64),
+        ("n_seg", ctypes.c_int64),
+        ("seg_cap", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib(path: str | None = None):
+    """Load libsaga.so (raises FileNotFoundError when it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} not found: build it with `python -m sparse_asymmetric_head_amd.build`")
+    L = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.saga_status_string.argtypes = [i32]
+    L.saga_status_string.restype = ctypes.c_char_p
+    L.saga_version.restype = i32
+    L.saga_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i64, i64]
+    L.saga_workspace_bytes.restype = sz
+    L.saga_dense_workspace_bytes.argtypes = [i32, i32, i32, i32, i64]
+    L.saga_dense_workspace_bytes.restype = sz
+    L.saga_workspace_init.argtypes = [vp, sz, vp]
+    L.saga_workspace_init.restype = i32
+    L.saga_refresh_threshold.argtypes = [vp, vp, i32, i32, i32, i32, i64, i64, vp, vp, sz, vp]
+    L.saga_refresh_threshold.restype = i32
+    L.saga_decode_step.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, vp, i32, vp,
+                                   vp, vp, sz, vp]
+    L.saga_decode_step.restype = i32
+    L.saga_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, i64, vp, i32, vp, sz, vp]
+    L.saga_select.restype = i32
+    L.saga_attend.argtypes = [vp, i32, i32, i32, i32, i32, i64, i64, vp, vp, vp, sz, vp]
+    L.saga_attend.restype = i32
+    L.saga_dense_gqa_baseline.argtypes = [vp, vp, vp, i32, i32, i32, i32, i64, vp, vp, sz, vp]
+    L.saga_dense_gqa_baseline.restype = i32
+    L.saga_workspace_layout.argtypes = [i32, i32, i32, i32, i32, i64, i64,
+                                        ctypes.POINTER(WsLayout)]
+    L.saga_workspace_layout.restype = i32
+    L.saga_selection_mask.argtypes = [vp, sz, i32, i32, i32, i32, i32, i64, i64, vp, vp]
+    L.saga_selection_mask.restype = i32
+    if path is None:
+        _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().saga_status_string(int(status)).decode()
+
+
+def _check(st: int, where: str) -> None:
+    if st != SAGA_OK:
+        raise SagaError(st, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ----------------------------------------------------------------- workspace
+
+def saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N) -> int:
+    return int(lib().saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
+
+
+def saga_dense_workspace_bytes(B, h_q, h_kv, d, l_kv) -> int:
+    return int(lib().saga_dense_workspace_bytes(B, h_q, h_kv, d, l_kv))
+
+
+def saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, N) -> WsLayout:
+    out = WsLayout()
+    _check(lib().saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, N, ctypes.byref(out)),
+           "saga_workspace_layout")
+    return out
+
+
+def saga_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check(lib().saga_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "saga_workspace_init")
+
+
+def alloc_workspace(nbytes: int, device="cuda", stream=None) -> torch.Tensor:
+    """A device byte buffer of nbytes (rounded up to 256), initialised for use."""
+    n = (int(nbytes) + 255) // 256 * 256
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    saga_workspace_init(ws, stream)
+    return ws
+
+
+def _dims(Q, K, V=None):
+    if Q.dtype != torch.bfloat16 or K.dtype != torch.bfloat16:
+        raise TypeError("Q and K must be bfloat16")
+    if Q.dim() != 3 or K.dim() != 4:
+        raise ValueError("Q must be [B][h_q][d] and K [B][h_k][l_kv][d]")
+    B, h_q, d = Q.shape
+    if K.shape[0] != B or K.shape[3] != d:
+        raise ValueError("Q and K disagree on B or d")
+    if V is not None:
+        if V.dtype != torch.bfloat16 or V.dim() != 4:
+            raise TypeError("V must be bfloat16 [B][h_v][l_kv][d]")
+        if V.shape[0] != B or V.shape[2] != K.shape[2] or V.shape[3] != d:
+            raise ValueError("V disagrees with K")
+    for t in (Q, K, V):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return B, h_q, d
+
+
+# ----------------------------------------------------------------- entry points
+
+def saga_refresh_threshold(Q, K, N: int, tau, ws, stream=None) -> None:
+    B, h_q, d = _dims(Q, K)
+    h_k, l_kv = K.shape[1], K.shape[2]
+    _check(lib().saga_refresh_threshold(_ptr(Q), _ptr(K), B, h_q, h_k, d, l_kv, int(N),
+                                        _ptr(tau), _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_refresh_threshold")
+
+
+def saga_decode_step(Q, K, V, N: int, tau, refresh: bool, O, counts=None, ws=None,
+                     stream=None) -> None:
+    B, h_q, d = _dims(Q, K, V)
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    if ws is None:
+        raise ValueError("a workspace is required (alloc_workspace)")
+    _check(lib().saga_decode_step(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv, int(N),
+                                  _ptr(tau), 1 if refresh else 0, _ptr(O), _ptr(counts),
+                                  _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_decode_step")
+
+
+def saga_select(Q, K, h_v: int, N: int, tau, refresh: bool, ws, stream=None) -> None:
+    B, h_q, d = _dims(Q, K)
+    h_k, l_kv = K.shape[1], K.shape[2]
+    _check(lib().saga_select(_ptr(Q), _ptr(K), B, h_q, h_k, int(h_v), d, l_kv, int(N), _ptr(tau),
+                             1 if refresh else 0, _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_select")
+
+
+def saga_attend(V, B: int, h_q: int, h_k: int, N: int, O, counts, ws, stream=None) -> None:
+    if V.dtype != torch.bfloat16 or V.dim() != 4 or not V.is_contiguous():
+        raise TypeError("V must be contiguous bfloat16 [B][h_v][l_kv][d]")
+    h_v, l_kv, d = V.shape[1], V.shape[2], V.shape[3]
+    _check(lib().saga_attend(_ptr(V), int(B), int(h_q), int(h_k), h_v, d, l_kv, int(N), _ptr(O),
+                             _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_attend")
+
+
+def saga_dense_gqa_baseline(Q, K, V, O, ws, stream=None) -> None:
+    B, h_q, d = _dims(Q, K, V)
+    h_kv, l_kv = K.shape[1], K.shape[2]
+    _check(lib().saga_dense_gqa_baseline(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_kv, d, l_kv,
+                                         _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_dense_gqa_baseline")
+
+
+def saga_selection_mask(ws, B, h_q, h_k, h_v, d, l_kv, N, mask, stream=None) -> None:
+    _check(lib().saga_selection_mask(_ptr(ws), ws.numel(), B, h_q, h_k, h_v, d, l_kv, int(N),
+                                     _ptr(mask), _stream(stream)),
+           "saga_selection_mask")
+
+
+# ----------------------------------------------------------------- conveniences
+
+class Decoder:
+    """Holds a workspace and the per-row threshold for one (shape, N) and runs
+    Atop-N decode steps with a refresh every R calls (the first call refreshes)."""
+
+    def __init__(self, B, h_q, h_k, h_v, d, l_kv, N, R, device="cuda"):
+        self.shape = (B, h_q, h_k, h_v, d, l_kv)
+        self.N, self.R, self.t = int(N), int(R), 0
+        self.ws = alloc_workspace(saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N), device)
+        self.tau = torch.zeros(B, h_q, dtype=torch.float32, device=device)
+        self.O = torch.empty(B, h_q, d, dtype=torch.float32, device=device)
+        self.counts = torch.empty(B, h_q, dtype=torch.int32, device=device)
+
+    def step(self, Q, K, V, stream=None):
+        refresh = (self.t % self.R) == 0
+        saga_decode_step(Q, K, V, self.N, self.tau, refresh, self.O, self.counts, self.ws, stream)
+        self.t += 1
+        return self.O

@@ -1,0 +1,164 @@
+"""The C-ABI library: it loads, exports every entry point include/saga.h
+declares, and validates arguments on the host (no GPU needed: an invalid call
+returns its status before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saga.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(saga_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_asymmetric_head_amd import saga
+
+    if not os.path.exists(saga.LIB_PATH):
+        from sparse_asymmetric_head_amd import build
+
+        build.build()
+    return saga.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("saga_decode_step", "saga_refresh_threshold", "saga_dense_gqa_baseline",
+              "saga_workspace_bytes", "saga_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from sparse_asymmetric_head_amd import saga
+
+    names = declared_functions()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in saga.h but not exported"
+    assert set(names) == set(saga.EXPORTS)
+
+
+def test_status_strings(L):
+    from sparse_asymmetric_head_amd import saga
+
+    assert saga.status_string(0) == "SAGA_OK"
+    assert saga.status_string(-1) == "SAGA_ERR_INVALID_ARG"
+    assert saga.status_string(-3) == "SAGA_ERR_WORKSPACE"
+    assert saga.status_string(12345) == "SAGA_ERR_UNKNOWN"
+    assert L.saga_version() >= 100
+
+
+SHAPES = [
+    (1, 4, 1, 2, 64, 1024, 64),
+    (1, 32, 4, 16, 64, 32768, 256),
+    (1, 32, 4, 16, 64, 131072, 512),
+    (4, 12, 1, 4, 128, 131072, 512),
+    (16, 32, 2, 32, 128, 65536, 1024),
+    (2, 6, 4, 5, 64, 1000, 7),      # non-integer group ratio, ragged length
+    (1, 64, 1, 8, 128, 333, 333),   # 64 query heads per key head, N = l_kv
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_workspace_layout_consistent(L, shape):
+    from sparse_asymmetric_head_amd import saga
+
+    B, h_q, h_k, h_v, d, l_kv, N = shape
+    nbytes = saga.saga_workspace_bytes(*shape)
+    assert nbytes > 0 and nbytes % 256 == 0
+    lay = saga.saga_workspace_layout(*shape)
+    assert lay.bytes == nbytes
+    assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
+    assert lay.n_seg == 4 * lay.n_chunk and lay.seg_cap * 4 == lay.chunk_len
+    assert lay.scores_ld >= l_kv and lay.scores_ld % 4 == 0
+    rows = B * h_q
+    regions = sorted([
+        (lay.seg_count_off, rows * lay.n_seg * 4),
+        (lay.seg_maxkey_off, rows * lay.n_seg * 4),
+        (lay.seg_off, rows * lay.n_seg * lay.seg_cap * 4),
+        (lay.seg_score_off, rows * lay.n_seg * lay.seg_cap * 4),
+        (lay.scores_off, rows * lay.scores_ld * 4),
+    ])
+    for (o1, n1), (o2, _) in zip(regions, regions[1:]):
+        assert o1 % 256 == 0 and o1 + n1 <= o2
+    assert regions[-1][0] + regions[-1][1] <= nbytes
+    # h_v does not change the layout (the refresh call uses h_v = h_k)
+    assert saga.saga_workspace_bytes(B, h_q, h_k, h_k, d, l_kv, N) == nbytes
+
+
+def test_invalid_shapes_rejected(L):
+    f = L.saga_workspace_bytes
+    assert f(1, 4, 1, 2, 64, 1024, 64) > 0
+    assert f(0, 4, 1, 2, 64, 1024, 64) == 0       # B < 1
+    assert f(1, 4, 3, 2, 64, 1024, 64) == 0       # h_k > h_v
+    assert f(1, 4, 1, 8, 64, 1024, 64) == 0       # h_v > h_q
+    assert f(1, 4, 1, 2, 96, 1024, 64) == 0       # d unsupported
+    assert f(1, 4, 1, 2, 64, 1024, 0) == 0        # N < 1
+    assert f(1, 4, 1, 2, 64, 1024, 1025) == 0     # N > l_kv
+    assert f(1, 130, 2, 2, 64, 1024, 64) == 0     # group of 65 query heads
+    assert f(1, 4, 1, 2, 128, 1 << 23, 64) == 0   # cache rows beyond 2^31 bytes
+    assert L.saga_dense_workspace_bytes(1, 32, 8, 64, 4096) > 0
+    assert L.saga_dense_workspace_bytes(1, 32, 1, 64, 4096) == 0  # group of 32 > 16
+
+
+def test_entry_points_validate_before_launch(L):
+    """All of these are rejected on the host, so they run without a GPU."""
+    from sparse_asymmetric_head_amd import saga
+
+    B, h_q, h_k, h_v, d, l_kv, N = 1, 4, 1, 2, 64, 1024, 64
+    need = saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N)
+    fake = ctypes.c_void_p(0x10000)        # aligned, never dereferenced
+    mis = ctypes.c_void_p(0x10008)         # misaligned
+    ds = L.saga_decode_step
+    args = [fake, fake, fake, B, h_q, h_k, h_v, d, l_kv, N, fake, 0, fake, None, fake, need, None]
+    bad = list(args); bad[0] = None
+    assert ds(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[1] = mis
+    assert ds(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[15] = need - 256
+    assert ds(*bad) == saga.SAGA_ERR_WORKSPACE
+    bad = list(args); bad[14] = mis
+    assert ds(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[7] = 80
+    assert ds(*bad) == saga.SAGA_ERR_UNSUPPORTED
+    bad = list(args); bad[9] = l_kv + 1
+    assert ds(*bad) == saga.SAGA_ERR_INVALID_ARG
+    rt = L.saga_refresh_threshold
+    assert rt(fake, None, B, h_q, h_k, d, l_kv, N, fake, fake, need, None) == \
+        saga.SAGA_ERR_INVALID_ARG
+    assert rt(fake, fake, B, h_q, h_k, d, l_kv, N, fake, fake, 0, None) == saga.SAGA_ERR_WORKSPACE
+    dn = L.saga_dense_gqa_baseline
+    dneed = L.saga_dense_workspace_bytes(1, 32, 8, 64, 4096)
+    assert dn(fake, fake, fake, 1, 32, 8, 64, 4096, None, fake, dneed, None) == \
+        saga.SAGA_ERR_INVALID_ARG
+    assert dn(fake, fake, fake, 1, 32, 8, 64, 4096, fake, fake, dneed - 256, None) == \
+        saga.SAGA_ERR_WORKSPACE
+    assert L.saga_workspace_init(None, 1024, None) == saga.SAGA_ERR_INVALID_ARG
+    assert L.saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, N, None) == \
+        saga.SAGA_ERR_INVALID_ARG
+    assert L.saga_selection_mask(fake, need, B, h_q, h_k, h_v, d, l_kv, N, None, None) == \
+        saga.SAGA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_without_library(tmp_path):
+    from sparse_asymmetric_head_amd import saga
+
+    with pytest.raises(FileNotFoundError):
+        saga.lib(str(tmp_path / "missing.so"))
+
+
+def test_product_path_does_not_import_oracle():
+    """The HIP path and its binding never reach the CPU oracle."""
+    pkg = os.path.join(ROOT, "sparse_asymmetric_head_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src, f
+                assert "saga_oracle" not in src and "sao_" not in src, f

@@ -1,0 +1,269 @@
+"""HIP path vs the fp64 oracle, through the C ABI.  Needs an MI355X.
+
+Small cases run whole trajectories against the oracle element by element;
+the full-size workloads (32K/128K context, batch 16) compare sampled rows the
+oracle computes one by one, in the launch configuration the benchmark uses
+(the library picks it from the shape)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (OUT_RTOL, bits, check_selection, check_tau_bits, read_mask, read_scores,
+                         rel_err, require_gpu, run_gpu_trajectory)
+from sparse_asymmetric_head_amd import saga
+from sparse_asymmetric_head_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def full_check(Q, K, V, N, R, tag=""):
+    T, B, h_q, d = Q.shape
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    print(f"[parity] {tag} B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv} N={N} R={R} T={T}",
+          flush=True)
+    g = run_gpu_trajectory(Q, K, V, N, R)
+    Qh, Kh, Vh = bits(Q), bits(K), bits(V)
+    ref = oracle.trajectory(Qh, Kh, Vh, h_k, h_v, N, R, want_mask=True)
+    flips = 0
+    for t in range(T):
+        A = oracle.scores(Qh[t], Kh, h_k)
+        if t % R == 0:
+            S = g["scores"][t].reshape(B, h_q, l_kv)
+            scale = np.maximum(1.0, np.abs(A).max(axis=-1, keepdims=True))
+            assert (np.abs(S - A) <= 1e-5 * scale).all(), f"scores t={t}"
+            for b in range(B):
+                for j in range(h_q):
+                    check_tau_bits(S[b, j], g["tau"][t][b, j], N, f"t={t} b={b} j={j}")
+        m = g["mask"][t]
+        for b in range(B):
+            for j in range(h_q):
+                flips += check_selection(m[b, j], A[b, j], ref["tau"][t, b, j], f"t={t} b={b} j={j}")
+        assert np.array_equal(g["count"][t], m.sum(-1)), f"counts t={t}"
+        Og, cg = oracle.given_mask(Qh[t], Kh, Vh, h_k, h_v, m)
+        assert np.array_equal(cg, g["count"][t])
+        assert rel_err(g["O"][t], Og) <= OUT_RTOL, f"output t={t}: {rel_err(g['O'][t], Og)}"
+        agree = (m == ref["mask"][t]).all(-1)
+        if agree.any():
+            assert rel_err(g["O"][t][agree], ref["O"][t][agree]) <= OUT_RTOL
+    return flips
+
+
+def test_tiny_config_full_trajectory():
+    cfg = wl.CONFIGS[0]
+    x = wl.make_layer(cfg, 0, device="cuda")
+    full_check(x["Q"], x["K"], x["V"], cfg.N, cfg.R, "tiny")
+
+
+SMALL = [
+    # B, h_q, h_k, h_v, d, l_kv, N, R, T, planted
+    (2, 6, 4, 5, 64, 3001, 37, 3, 7, 8),       # non-integer head ratio, ragged tail
+    (1, 12, 1, 4, 128, 5000, 100, 4, 6, 32),   # Qwen-like group of 12
+    (2, 32, 2, 32, 128, 4100, 64, 5, 6, 32),   # group of 16, one value head per query
+    (1, 40, 1, 8, 64, 2500, 50, 2, 3, 16),     # group of 40 (four N-tiles)
+    (1, 24, 1, 24, 128, 1800, 30, 2, 3, 16),   # group of 24 (two N-tiles)
+    (1, 8, 8, 8, 64, 777, 20, 2, 3, 4),        # MHA: h_k = h_v = h_q
+    (1, 8, 2, 2, 64, 1500, 1500, 1, 2, 0),     # N = l_kv: dense GQA
+    (1, 4, 1, 2, 64, 300, 1, 1, 2, 0),         # N = 1
+    (3, 4, 2, 3, 128, 17, 5, 2, 3, 2),         # l_kv shorter than one tile
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+def test_small_trajectories(case):
+    B, h_q, h_k, h_v, d, l_kv, N, R, T, P = case
+    x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=hash(case) % 10007, device="cuda",
+                       steps=T, planted=P, drift=0.05)
+    full_check(x["Q"], x["K"], x["V"], N, R, "small")
+
+
+def test_llama_32k_full_trajectory():
+    cfg = wl.CONFIGS[1]
+    x = wl.make_layer(cfg, 0, device="cuda")
+    flips = full_check(x["Q"], x["K"], x["V"], cfg.N, cfg.R, cfg.name)
+    print(f"[parity] {cfg.name}: boundary flips within the band: {flips}", flush=True)
+
+
+def sampled_check(cfg, layer, steps, rows):
+    x = wl.make_layer(cfg, layer, device="cuda")
+    Q, K, V = x["Q"], x["K"], x["V"]
+    T, B, h_q, d = Q.shape
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    N, R = cfg.N, cfg.R
+    print(f"[parity] {cfg.name} layer={layer} steps={steps} rows={rows}", flush=True)
+    need = set(steps)
+    g = run_gpu_trajectory(Q, K, V, N, R, mask_steps=need,
+                           score_steps={R * (t // R) for t in steps})
+    Qh = bits(Q)
+    for row in rows:
+        b, j = divmod(row, h_q)
+        kh, vh = (j * h_k) // h_q, (j * h_v) // h_q
+        Kr = bits(K[b, kh])[None, None]
+        Vr = bits(V[b, vh])
+        for t in steps:
+            tr = R * (t // R)
+            a_tr = oracle.scores(Qh[tr, b, j][None, None], Kr, 1)[0, 0]
+            tau_ref = oracle.nth_largest(a_tr, N)
+            a_t = oracle.scores(Qh[t, b, j][None, None], Kr, 1)[0, 0] if t != tr else a_tr
+            if t == tr:
+                s = g["scores"][t][row]
+                assert np.abs(s - a_t).max() <= 1e-5 * max(1.0, np.abs(a_t).max())
+                check_tau_bits(s, g["tau"][t][b, j], N, f"{cfg.name} t={t} row={row}")
+            m = g["mask"][t][b, j]
+            check_selection(m, a_t, tau_ref, f"{cfg.name} t={t} row={row}")
+            assert g["count"][t][b, j] == m.sum()
+            o_ref, c_ref = oracle.attend_row(a_t, m, Vr)
+            assert c_ref == g["count"][t][b, j]
+            err = rel_err(g["O"][t][b, j][None], o_ref[None])
+            assert err <= OUT_RTOL, f"{cfg.name} t={t} row={row}: {err}"
+    del x, Q, K, V
+    torch.cuda.empty_cache()
+
+
+def test_llama_128k_16_layers_sampled():
+    cfg = wl.CONFIGS[2]
+    for layer in (0, 7, 15):
+        sampled_check(cfg, layer, steps=[0, 16, 33, 63], rows=[0, 9, 22, 31])
+
+
+def test_qwen_128k_sampled():
+    cfg = wl.CONFIGS[3]
+    sampled_check(cfg, 0, steps=[0, 31, 32, 63], rows=[0, 13, 30, 47])
+
+
+def test_stress_batch16_sampled():
+    cfg = wl.CONFIGS[4]
+    sampled_check(cfg, 0, steps=[0, 63, 64, 127], rows=[0, 3 * 32 + 17, 15 * 32 + 31, 8 * 32 + 5])
+
+
+# ------------------------------------------------------------------ edge cases
+
+def _step(Q, K, V, N, tau, refresh):
+    B, h_q, d = Q.shape
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
+    O = torch.empty(B, h_q, d, dtype=torch.float32, device="cuda")
+    cnt = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+    saga.saga_decode_step(Q, K, V, N, tau, refresh, O, cnt, ws)
+    torch.cuda.synchronize()
+    return O, cnt, ws
+
+
+def test_stale_tau_extremes():
+    x = wl.make_random(2, 8, 2, 4, 64, 2000, seed=11, device="cuda")
+    Q, K, V = x["Q"][0], x["K"], x["V"]
+    tau = torch.full((2, 8), 1e30, dtype=torch.float32, device="cuda")
+    O, cnt, _ = _step(Q, K, V, 10, tau, False)
+    assert (cnt == 0).all() and (O == 0).all()  # empty selection -> zero output
+    tau.fill_(-1e30)
+    O, cnt, _ = _step(Q, K, V, 10, tau, False)
+    assert (cnt == 2000).all()
+    Qh, Kh, Vh = bits(Q), bits(K), bits(V)
+    ref = oracle.given_mask(Qh, Kh, Vh, 2, 4, np.ones((2, 8, 2000), np.uint8))[0]
+    assert rel_err(O.cpu().numpy().astype(np.float64), ref) <= OUT_RTOL
+
+
+def test_ties_at_threshold():
+    """Duplicated key rows give exactly equal scores; all ties at tau are kept."""
+    x = wl.make_random(1, 4, 1, 2, 64, 1024, seed=12, device="cuda")
+    K = x["K"].clone()
+    K[0, 0, 512:768] = K[0, 0, 256:512]   # every score in 256..767 appears twice
+    K[0, 0, 100:110] = K[0, 0, 99]        # ten-way tie
+    Q, V, N = x["Q"][0], x["V"], 7
+    tau = torch.zeros(1, 4, dtype=torch.float32, device="cuda")
+    O, cnt, ws = _step(Q, K, V, N, tau, True)
+    S = read_scores(ws, (1, 4, 1, 2, 64, 1024), N)
+    m = read_mask(ws, (1, 4, 1, 2, 64, 1024), N)
+    for j in range(4):
+        check_tau_bits(S[j], tau[0, j].item(), N, f"j={j}")
+        assert np.array_equal(m[0, j].astype(bool), S[j] >= np.float32(tau[0, j].item()))
+        assert cnt[0, j].item() == (S[j] >= np.float32(tau[0, j].item())).sum()
+    assert np.array_equal(S[:, 512:768], S[:, 256:512])
+
+
+def test_negative_zero_scores_canonical():
+    """Key rows of -0.0 give score +0.0 (bit pattern 0), never -0.0."""
+    x = wl.make_random(1, 4, 1, 2, 64, 256, seed=13, device="cuda")
+    K = x["K"].clone()
+    K[0, 0, :64] = -0.0
+    tau = torch.zeros(1, 4, dtype=torch.float32, device="cuda")
+    _, _, ws = _step(x["Q"][0], K, x["V"], 200, tau, True)
+    S = read_scores(ws, (1, 4, 1, 2, 64, 256), 200)
+    assert (S[:, :64].view(np.uint32) == 0).all()
+
+
+def test_refresh_threshold_entry_point():
+    x = wl.make_random(2, 12, 3, 6, 128, 6000, seed=14, device="cuda", planted=20)
+    Q, K = x["Q"][0], x["K"]
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(2, 12, 3, 3, 128, 6000, 300))
+    tau = torch.zeros(2, 12, dtype=torch.float32, device="cuda")
+    saga.saga_refresh_threshold(Q, K, 300, tau, ws)
+    torch.cuda.synchronize()
+    S = read_scores(ws, (2, 12, 3, 3, 128, 6000), 300)
+    A = oracle.scores(bits(Q), bits(K), 3)
+    for r in range(24):
+        check_tau_bits(S[r], tau.view(-1)[r].item(), 300, f"row={r}")
+        assert abs(tau.view(-1)[r].item() - oracle.nth_largest(A.reshape(24, -1)[r], 300)) < 1e-4
+
+
+def test_deterministic_and_workspace_reuse():
+    """Same inputs, same workspace, twice: bitwise identical tau, counts, output
+    and selection (internal counters return to zero after every call)."""
+    x = wl.make_random(1, 32, 4, 16, 64, 20000, seed=15, device="cuda", steps=6, planted=64)
+    a = run_gpu_trajectory(x["Q"], x["K"], x["V"], 128, 3)
+    b = run_gpu_trajectory(x["Q"], x["K"], x["V"], 128, 3)
+    for t in range(6):
+        assert np.array_equal(a["tau"][t].view(np.uint32), b["tau"][t].view(np.uint32))
+        assert np.array_equal(a["count"][t], b["count"][t])
+        assert np.array_equal(a["mask"][t], b["mask"][t])
+        assert np.array_equal(a["O"][t], b["O"][t])
+
+
+# ------------------------------------------------------------------ dense baseline
+
+DENSE = [
+    # B, h_q, h_kv, d, l_kv
+    (1, 32, 8, 64, 5000),
+    (2, 12, 2, 128, 3333),
+    (1, 8, 8, 64, 100),
+    (3, 6, 4, 128, 17),
+    (1, 16, 1, 64, 2049),
+]
+
+
+def _dense(Q, K, V):
+    B, h_q, d = Q.shape
+    h_kv, l_kv = K.shape[1], K.shape[2]
+    ws = torch.empty(saga.saga_dense_workspace_bytes(B, h_q, h_kv, d, l_kv), dtype=torch.uint8,
+                     device="cuda")
+    O = torch.empty(B, h_q, d, dtype=torch.float32, device="cuda")
+    saga.saga_dense_gqa_baseline(Q, K, V, O, ws)
+    torch.cuda.synchronize()
+    return O.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", DENSE, ids=[str(c) for c in DENSE])
+def test_dense_gqa_small(case):
+    B, h_q, h_kv, d, l_kv = case
+    x = wl.make_random(B, h_q, h_kv, h_kv, d, l_kv, seed=hash(case) % 9973, device="cuda",
+                       planted=8)
+    O = _dense(x["Q"][0], x["K"], x["V"])
+    ref = oracle.dense(bits(x["Q"][0]), bits(x["K"]), bits(x["V"]))
+    assert rel_err(O, ref) <= OUT_RTOL
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3])
+def test_dense_gqa_full_size(ci):
+    cfg = wl.CONFIGS[ci]
+    x = wl.make_dense_layer(cfg, 0, device="cuda")
+    print(f"[parity] dense {cfg.name} h_kv={cfg.dense_h_kv}", flush=True)
+    O = _dense(x["Q"], x["K"], x["V"])
+    ref = oracle.dense(bits(x["Q"]), bits(x["K"]), bits(x["V"]))
+    assert rel_err(O, ref) <= OUT_RTOL
+    del x
+    torch.cuda.empty_cache()
