@@ -137,24 +137,37 @@ def main() -> int:
         f"wall {wall_ms:.3f} ms)")
 
     # ------------------------------------------------------------ kernel timing pass
-    # HIP events around every launch of the dominant kernel (the streaming
-    # compare-and-compact pass), on the stream it runs on.
-    kt = []
+    # The dominant kernel (the streaming score/compare/compact pass) timed
+    # with HIP events on the stream it runs on: a graph of its launches over
+    # all layers (non-refresh), replayed back to back; per-launch time =
+    # elapsed / launches.  (Events around single launches would add several
+    # microseconds of event overhead to each.)
+    reps = max(1, args.kernel_timing_steps)
     with torch.cuda.stream(stream):
-        pairs = []
-        for t in range(args.kernel_timing_steps):
-            qbuf.copy_(Qall[(args.warmup + args.steps + t) % T])
+        qbuf.copy_(Qall[(args.warmup + args.steps) % T])
+
+        def select_pass():
             for l in range(L):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
                 saga.saga_select(qbuf[l], Ks[l], h_v, N, taus[l], False, ws, stream)
-                b.record(stream)
-                saga.saga_attend(Vs[l], B, h_q, h_k, N, Os[l], cnts[l], ws, stream)
-                pairs.append((a, b))
+
+        select_pass()
         stream.synchronize()
-        kt = [a.elapsed_time(b) * 1e3 for a, b in pairs]
-    sel_us = sum(kt) / len(kt)
+        sg = None
+        if not args.no_graph:
+            sg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(sg, stream=stream):
+                select_pass()
+        run_sel = sg.replay if sg is not None else select_pass
+        run_sel()
+        stream.synchronize()
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        k0.record(stream)
+        for _ in range(reps):
+            run_sel()
+        k1.record(stream)
+        stream.synchronize()
+    sel_us = k0.elapsed_time(k1) * 1e3 / (reps * L)
     mean_count = sum(sel_counts) / len(sel_counts)
 
     k_bytes = B * h_k * l_kv * d * 2

@@ -105,8 +105,9 @@ int saga_decode_step(const void *Q, const void *K, const void *V, int B, int h_q
  * saga_select(...) followed by saga_attend(...) on the same workspace.
  *
  * saga_select: (refresh as in saga_decode_step) scores, compare with tau and
- *   compact the survivors S into the workspace's segments (layout below).
- * saga_attend: O and counts from the segments the preceding saga_select on
+ *   compact the survivors S into the workspace's segment records (layout
+ *   below).
+ * saga_attend: O and counts from the records the preceding saga_select on
  *   this workspace left, for the same shape (eq. 7).
  */
 int saga_select(const void *Q, const void *K, int B, int h_q, int h_k, int h_v, int d,
@@ -131,14 +132,15 @@ typedef struct saga_ws_layout {
     size_t bytes;          /* total workspace size (= saga_workspace_bytes) */
     size_t scores_off;     /* fp32 [B*h_q][scores_ld]: scores of the last refresh */
     int64_t scores_ld;     /* row stride of the scores, in elements (>= l_kv) */
-    size_t seg_count_off;  /* int32 [B*h_q][n_seg]: survivors per (row, segment) */
-    size_t seg_maxkey_off; /* uint32 [B*h_q][n_seg]: order key of each segment's max score */
-    size_t seg_off;        /* int32 [B*h_q][n_seg][seg_cap]: survivor positions t */
-    size_t seg_score_off;  /* fp32 [B*h_q][n_seg][seg_cap]: their scores */
+    size_t seg_off;        /* int32 [B*h_q][n_seg][seg_words]: survivor records, each
+                              { count, order key of the max score, then (t, score bits)
+                              pairs }; segment k of a row covers cache positions
+                              [c*chunk_len + w*seg_cap, ... + seg_cap), c = k/4, w = k%4 */
+    int64_t seg_words;     /* int32 words per record (multiple of 16) */
     int64_t chunk_len;     /* cache positions per streaming block */
     int64_t n_chunk;       /* blocks per key-head row: ceil(l_kv / chunk_len) */
     int64_t n_seg;         /* segments per row (n_chunk * 4) */
-    int64_t seg_cap;       /* capacity of one segment (chunk_len / 4) */
+    int64_t seg_cap;       /* positions covered by one segment (chunk_len / 4) */
 } saga_ws_layout;
 
 /* Fill *out for this shape.  Returns SAGA_OK or a negative status. */

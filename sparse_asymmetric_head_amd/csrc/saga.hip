@@ -15,9 +15,12 @@ namespace {
 
 using namespace saga;
 
-constexpr int kTargetSelectBlocks = 512;  // streaming blocks per step (2 per CU)
+#ifndef SAGA_SELECT_BLOCKS
+#define SAGA_SELECT_BLOCKS 512
+#endif
+constexpr int kTargetSelectBlocks = SAGA_SELECT_BLOCKS;  // streaming blocks per launch
 constexpr int64_t kChunkUnit = 256;       // chunk_len granularity (positions)
-constexpr int64_t kHistBlock = 8192;      // positions per histogram/collect block
+constexpr int64_t kHistBlock = kHistBlockMax;  // positions per histogram/collect block
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -30,12 +33,12 @@ struct Plan {
     int64_t chunk_len;
     int n_chunk, n_sub;
     int64_t sub_cap;
-    int pw;
     int64_t ld_a;
     int hist_bpr;
     // byte offsets into the workspace
-    size_t off_ticket, off_hist, off_state, counters_end;
-    size_t off_partial, off_seg_count, off_seg_maxkey, off_seg_t, off_seg_s, off_scores, off_cand;
+    size_t off_hist, off_state, counters_end;
+    int64_t seg_w;
+    size_t off_seg, off_scores, off_cand;
     size_t total;
 };
 
@@ -69,31 +72,19 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->n_sub = p->n_chunk * kWaves;
     p->sub_cap = cl / kWaves;
-    int64_t pw = ceil_div(N, 64);
-    p->pw = (int)(pw < 1 ? 1 : (pw > 64 ? 64 : pw));
     p->ld_a = ceil_div(l_kv, 64) * 64;
     p->hist_bpr = (int)ceil_div(l_kv, kHistBlock);
 
     const size_t rows = (size_t)p->rows;
     size_t o = 0;
-    p->off_ticket = o;
-    o = align_up(o + rows * sizeof(uint32_t));
     p->off_hist = o;
     o = align_up(o + rows * kHistBins * sizeof(uint32_t));
     p->off_state = o;
     o = align_up(o + rows * 4 * sizeof(uint32_t));
     p->counters_end = o;
-    p->off_partial = o;
-    o = align_up(o + rows * (size_t)p->pw * (d + 4) * sizeof(float));
-    p->off_seg_count = o;
-    o = align_up(o + rows * (size_t)p->n_sub * sizeof(int32_t));
-    p->off_seg_maxkey = o;
-    o = align_up(o + rows * (size_t)p->n_sub * sizeof(uint32_t));
-    const size_t seg_elems = rows * (size_t)p->n_sub * (size_t)p->sub_cap;
-    p->off_seg_t = o;
-    o = align_up(o + seg_elems * sizeof(int32_t));
-    p->off_seg_s = o;
-    o = align_up(o + seg_elems * sizeof(float));
+    p->seg_w = seg_words(p->sub_cap);
+    p->off_seg = o;
+    o = align_up(o + rows * (size_t)p->n_sub * (size_t)p->seg_w * sizeof(int32_t));
     p->off_scores = o;
     o = align_up(o + rows * (size_t)p->ld_a * sizeof(float));
     p->off_cand = o;
@@ -162,12 +153,10 @@ SelectArgs select_args(const Plan &p, const void *Q, const void *K, const float 
     a.n_chunk = p.n_chunk;
     a.l_kv = p.l_kv, a.chunk_len = p.chunk_len;
     a.scale = (float)(1.0 / sqrt((double)p.d));
-    a.seg_t = (int32_t *)(ws + p.off_seg_t);
-    a.seg_s = (float *)(ws + p.off_seg_s);
-    a.seg_count = (int32_t *)(ws + p.off_seg_count);
-    a.seg_maxkey = (uint32_t *)(ws + p.off_seg_maxkey);
+    a.seg = (int32_t *)(ws + p.off_seg);
     a.n_sub = p.n_sub;
     a.sub_cap = p.sub_cap;
+    a.seg_w = p.seg_w;
     return a;
 }
 
@@ -193,32 +182,26 @@ int run_refresh(const Plan &p, const void *Q, const void *K, float *tau, char *w
     return launch_status();
 }
 
-int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws, hipStream_t s) {
+int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws,
+               hipStream_t s) {
     AttendArgs aa;
-    aa.seg_t = (const int32_t *)(ws + p.off_seg_t);
-    aa.seg_s = (const float *)(ws + p.off_seg_s);
-    aa.seg_count = (const int32_t *)(ws + p.off_seg_count);
-    aa.seg_maxkey = (const uint32_t *)(ws + p.off_seg_maxkey);
+    aa.seg = (const int32_t *)(ws + p.off_seg);
     aa.n_sub = p.n_sub;
-    aa.sub_cap = p.sub_cap;
+    aa.seg_w = p.seg_w;
     aa.V = (const uint16_t *)V;
     aa.B = p.B, aa.h_q = p.h_q, aa.h_v = p.h_v;
     aa.l_kv = p.l_kv;
-    aa.pw = p.pw;
-    aa.partial = (float *)(ws + p.off_partial);
-    aa.ticket = (uint32_t *)(ws + p.off_ticket);
     aa.O = O;
     aa.counts = counts;
-    const int blocks = p.rows * p.pw;
     if (p.d == 64)
-        hipLaunchKernelGGL(k_attend<64>, dim3(blocks), dim3(kThreads), 0, s, aa);
+        hipLaunchKernelGGL(k_attend<64>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
     else
-        hipLaunchKernelGGL(k_attend<128>, dim3(blocks), dim3(kThreads), 0, s, aa);
+        hipLaunchKernelGGL(k_attend<128>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
     return launch_status();
 }
 
-// Selection half of a step: refresh (score pass writing A, radix select,
-// compaction of A >= tau) or the streaming compare-and-compact pass.
+// Selection half of a step: scores, compare with tau (after an exact refresh
+// when asked), compaction into the segments and the per-chunk partials.
 int run_select(const Plan &p, const void *Q, const void *K, float *tau, int refresh, char *w,
                hipStream_t s) {
     if (refresh) {
@@ -229,12 +212,10 @@ int run_select(const Plan &p, const void *Q, const void *K, float *tau, int refr
         ca.ld_a = p.ld_a, ca.l_kv = p.l_kv, ca.chunk_len = p.chunk_len;
         ca.n_chunk = p.n_chunk;
         ca.tau = tau;
-        ca.seg_t = (int32_t *)(w + p.off_seg_t);
-        ca.seg_s = (float *)(w + p.off_seg_s);
-        ca.seg_count = (int32_t *)(w + p.off_seg_count);
-        ca.seg_maxkey = (uint32_t *)(w + p.off_seg_maxkey);
+        ca.seg = (int32_t *)(w + p.off_seg);
         ca.n_sub = p.n_sub;
         ca.sub_cap = p.sub_cap;
+        ca.seg_w = p.seg_w;
         hipLaunchKernelGGL(k_compact, dim3(p.rows * p.n_chunk), dim3(kThreads), 0, s, ca);
     } else {
         SelectArgs sa = select_args(p, Q, K, tau, w);
@@ -285,10 +266,8 @@ int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv,
     out->bytes = p.total;
     out->scores_off = p.off_scores;
     out->scores_ld = p.ld_a;
-    out->seg_count_off = p.off_seg_count;
-    out->seg_maxkey_off = p.off_seg_maxkey;
-    out->seg_off = p.off_seg_t;
-    out->seg_score_off = p.off_seg_s;
+    out->seg_off = p.off_seg;
+    out->seg_words = p.seg_w;
     out->chunk_len = p.chunk_len;
     out->n_chunk = p.n_chunk;
     out->n_seg = p.n_sub;
@@ -412,10 +391,10 @@ int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k
     int blocks = (int)(ceil_div(n, kThreads) < 4096 ? ceil_div(n, kThreads) : 4096);
     hipLaunchKernelGGL(k_fill_u8, dim3(blocks), dim3(kThreads), 0, s, mask, n, (uint8_t)0);
     MaskArgs ma;
-    ma.seg_t = (const int32_t *)(w + p.off_seg_t);
-    ma.seg_count = (const int32_t *)(w + p.off_seg_count);
+    ma.seg = (const int32_t *)(w + p.off_seg);
     ma.n_sub = p.n_sub;
     ma.sub_cap = p.sub_cap;
+    ma.seg_w = p.seg_w;
     ma.l_kv = l_kv;
     ma.mask = mask;
     hipLaunchKernelGGL(k_mask, dim3(p.rows * p.n_sub), dim3(kThreads), 0, s, ma);

@@ -65,6 +65,31 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
     return v;
 }
 
+// Block-wide exclusive scan of v over the NW*64 threads of a block; returns
+// the prefix, *total receives the sum.  Uses red[NW] of LDS; contains two
+// barriers, so every thread of the block must call it.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int *red, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        before += (w < wave) ? red[w] : 0;
+        tot += red[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
 // First query head of key head g's group: ceil(g*h_q/h_k), so that
 // floor(j*h_k/h_q) == g  <=>  group_lo(g) <= j < group_lo(g+1).
 __device__ __forceinline__ int group_lo(int g, int h_q, int h_k) {

@@ -12,29 +12,56 @@
 // Kernel map (one decode step):
 //   k_select<.., false>  stream K once per key head, MFMA scores for all query
 //                        heads of the group, compare with tau, compact the
-//                        survivors through LDS into per-(row, sub-chunk)
-//                        segments.                       [HBM-bound, hot]
-//   k_attend             per row: max and count from the segment headers,
-//                        softmax weights, gather of the survivors' V rows,
-//                        fp32 accumulation, deterministic cross-block merge.
+//                        survivors through LDS into per-(row, segment)
+//                        records.                         [HBM-bound, hot]
+//   k_attend             per row: read the segment records, build the row's
+//                        survivor list in LDS, softmax weights, gather of the
+//                        survivors' V rows, fp32 accumulation, O.
 // Refresh (every R steps) instead runs:
 //   k_select<.., true>   same score pass, writes fp32 A
 //   k_hist / k_select1 / k_collect / k_select_final   exact radix select
-//   k_compact            A >= tau into the same segments, then k_attend.
+//   k_compact            A >= tau into the same records, then k_attend.
 // Dense GQA baseline: k_dense (split-KV online softmax) + k_dense_merge.
+//
+// Segment records: the survivors of one (row, segment) -- a segment is one
+// wave's share of a block's cache positions -- are stored as int32 words
+//   [0] count, [1] order key of their largest score, [2+2i] position t_i,
+//   [3+2i] bits of score s_i,
+// padded to a multiple of 16 words, so that the first 64 bytes hold the
+// count and the first seven survivors.
 #pragma once
 
 #include "saga_device.hpp"
 
 namespace saga {
 
+#ifndef SAGA_PREFETCH
+#define SAGA_PREFETCH 1  // k_select: load the next tiles before scoring the current ones
+#endif
+#ifndef SAGA_NT_LOADS
+#define SAGA_NT_LOADS 1  // k_select: non-temporal (streaming) loads of the key cache
+#endif
+
 constexpr int kWaves = 4;     // waves per workgroup of the streaming kernels
 constexpr int kThreads = kWaves * kWave;
 constexpr int kCapW = 32;     // LDS staging slots per (wave, query head)
-constexpr int kMaxSub = 4096; // max segments per row
+constexpr int kMaxSub = 1024; // max segments per row
 constexpr int kHistBins = 2048;
+constexpr int kHistBlockMax = 8192;  // positions per histogram/collect block
+constexpr int kRecHead = 7;   // survivors held in a record's first 64 bytes
+
+// Words per segment record for a segment capacity of cap survivors.
+__host__ __device__ constexpr int64_t seg_words(int64_t cap) { return (2 + 2 * cap + 15) / 16 * 16; }
 
 // ------------------------------------------------------------------ select
+
+__device__ __forceinline__ u32x4 ld_k(const void *p) {
+#if SAGA_NT_LOADS
+    return ld16_stream(p);
+#else
+    return ld16(p);
+#endif
+}
 
 struct SelectArgs {
     const uint16_t *Q;   // bf16 [B][h_q][D]
@@ -46,12 +73,9 @@ struct SelectArgs {
     int n_chunk;
     int64_t l_kv, chunk_len;
     float scale;
-    int32_t *seg_t;      // [rows][n_sub][sub_cap]
-    float *seg_s;
-    int32_t *seg_count;  // [rows][n_sub]
-    uint32_t *seg_maxkey;
+    int32_t *seg;        // [rows][n_sub][seg_w] records
     int n_sub;
-    int64_t sub_cap;
+    int64_t sub_cap, seg_w;
 };
 
 // One workgroup = (batch b, key head g, chunk of cache positions).  Each wave
@@ -62,13 +86,15 @@ struct SelectArgs {
 // query operand uses the same permutation of the d axis, so each lane issues
 // 16-byte loads and the whole tile is a contiguous 16*d*2-byte block.
 // Output: lane l holds rows 4*(l/16)+r, r = 0..3, of query head l%16.
+// Survivors are ranked per (wave, head) with ballots (deterministic order:
+// tile, then row, then lane), staged in LDS and flushed to the wave's
+// segment record of that head.
 template <int D, int NT, bool MATERIALIZE>
 __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     constexpr int KS = D / 32;             // MFMA k-steps per row
     constexpr int U = (D == 64) ? 4 : 2;   // tiles per wave iteration (128 B per lane)
     constexpr int QW = D / 4;              // elements of a row per lane quarter
-    __shared__ int32_t st_t[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
-    __shared__ float st_s[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
+    __shared__ int2 st[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 15, lq = lane >> 4;
@@ -110,28 +136,35 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
             const int j = j_lo + nt * 16 + ln;
             if (j < j_hi) {
-                const int64_t base =
-                    (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.sub_cap + flushed[nt];
-                for (int i = lq; i < staged[nt]; i += 4) {
-                    a.seg_t[base + i] = st_t[wave][nt * 16 + ln][i];
-                    a.seg_s[base + i] = st_s[wave][nt * 16 + ln][i];
-                }
+                int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
+                for (int i = lq; i < staged[nt]; i += 4) rec[1 + flushed[nt] + i] = st[wave][nt * 16 + ln][i];
             }
             flushed[nt] += staged[nt];
             staged[nt] = 0;
         }
     };
 
-    for (int64_t t0 = t_begin + wave * 16 * U; t0 < t_end; t0 += kWaves * 16 * U) {
-        u32x4 kr[U][KS];
+    // K tiles of one wave iteration; the next iteration's tiles are loaded
+    // before the current ones are scored so that loads stay in flight.
+    auto load_tiles = [&](u32x4 (&kr)[U][KS], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = t0 + u * 16 + ln;
             const uint16_t *kp = Kb + row * D + lq * QW;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-                kr[u][s] = (row < t_end) ? ld16_stream(kp + s * 8) : u32x4{0u, 0u, 0u, 0u};
+                kr[u][s] = (row < t_end) ? ld_k(kp + s * 8) : u32x4{0u, 0u, 0u, 0u};
         }
+    };
+    constexpr int64_t kStride = kWaves * 16 * U;
+    u32x4 kr[U][KS];
+    int64_t t0 = t_begin + wave * 16 * U;
+    if (t0 < t_end) load_tiles(kr, t0);
+    for (; t0 < t_end; t0 += kStride) {
+#if SAGA_PREFETCH
+        u32x4 kn[U][KS];
+        if (t0 + kStride < t_end) load_tiles(kn, t0 + kStride);
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tr = t0 + u * 16 + lq * 4;  // position of acc[0]
@@ -172,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                             if (pr[r]) {
                                 const int rank = staged[nt] + before +
                                                  __popcll(m[r] & head_mask & lt_mask);
-                                st_t[wave][nt * 16 + ln][rank] = (int32_t)(tr + r);
-                                st_s[wave][nt * 16 + ln][rank] = sc[r];
+                                st[wave][nt * 16 + ln][rank] =
+                                    int2{(int)(tr + r), __float_as_int(sc[r])};
                                 const uint32_t k = fkey(sc[r]);
                                 mkey[nt] = mkey[nt] > k ? mkey[nt] : k;
                             }
@@ -193,8 +226,16 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                 }
             }
         }
+#if SAGA_PREFETCH
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kr[u][s] = kn[u][s];
+#else
+        if (t0 + kStride < t_end) load_tiles(kr, t0 + kStride);
+#endif
     }
-    if (!MATERIALIZE) {
+    if constexpr (!MATERIALIZE) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         flush();
 #pragma unroll
@@ -206,9 +247,8 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
             mk = mk > o ? mk : o;
             const int j = j_lo + nt * 16 + ln;
             if (lq == 0 && j < j_hi) {
-                const int64_t h = ((int64_t)b * a.h_q + j) * a.n_sub + sub;
-                a.seg_count[h] = flushed[nt];
-                a.seg_maxkey[h] = mk;
+                int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
+                rec[0] = int2{flushed[nt], (int)mk};
             }
         }
     }
@@ -217,92 +257,73 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 // ------------------------------------------------------------------ attend
 
 struct AttendArgs {
-    const int32_t *seg_t;
-    const float *seg_s;
-    const int32_t *seg_count;
-    const uint32_t *seg_maxkey;
+    const int32_t *seg;  // [rows][n_sub][seg_w] records
     int n_sub;
-    int64_t sub_cap;
-    const uint16_t *V;  // bf16 [B][h_v][l_kv][D]
+    int64_t seg_w;
+    const uint16_t *V;   // bf16 [B][h_v][l_kv][D]
     int B, h_q, h_v;
     int64_t l_kv;
-    int pw;             // workgroups per row
-    float *partial;     // [rows][pw][D + 4]
-    uint32_t *ticket;   // [rows]
-    float *O;           // [rows][D]
-    int32_t *counts;    // [rows] or null
+    float *O;            // [rows][D]
+    int32_t *counts;     // [rows] or null
 };
 
-// Block-wide exclusive scan of v over kThreads threads; returns the prefix,
-// *total receives the sum.  Uses red[kWaves] of LDS.
-__device__ __forceinline__ int block_excl_scan(int v, int *red, int *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) red[wave] = x;
-    __syncthreads();
-    int before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        before += (w < wave) ? red[w] : 0;
-        tot += red[w];
-    }
-    __syncthreads();
-    *total = tot;
-    return before + x - v;
-}
+constexpr int kAttendWaves = 8;
+constexpr int kAttendThreads = kAttendWaves * kWave;
+constexpr int kAttendWin = 4096;  // survivors staged in LDS per window
+constexpr int kSegPerThread = kMaxSub / kAttendThreads;
 
-// One workgroup = (row, slice w of that row's survivors).  Every slice uses
-// the row's exact maximum over the survivors (from the segment headers), so
-// slice partials (sum of weights, weighted V sum) add directly; the last
-// slice to finish adds them in slice order and normalises.
+// One workgroup per row (b, j).  Thread i owns segments 2i and 2i+1 and reads
+// the first 64 bytes of both records in one go (count, max key and up to
+// seven survivors each); an exclusive scan of the counts places every
+// survivor in the row's list, which is built in LDS (survivors past the
+// seventh of a segment are read from the rest of its record).  Then every
+// group of D/8 lanes takes one survivor per round: weight exp(s - M) with M
+// the row maximum, 16-byte loads of its V row, fp32 accumulation.  Lists
+// longer than kAttendWin are processed in windows.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
-    constexpr int LPE = D / 8;        // lanes per survivor (16 B each)
-    constexpr int EPB = kThreads / LPE;  // survivors per block round
-    constexpr int UN = 4;
-    __shared__ int pre[kMaxSub + 1];
-    __shared__ int ired[kWaves];
-    __shared__ uint32_t kred[kWaves];
-    __shared__ float ored[kWaves][D];
-    __shared__ float lred[kWaves];
-    __shared__ int is_last;
+__global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
+    constexpr int LPE = D / 8;                  // lanes per survivor (16 B each)
+    constexpr int EPB = kAttendThreads / LPE;   // survivors per block round
+    constexpr int UN = 8;
+    constexpr int SPT = kSegPerThread;
+    __shared__ int lt[kAttendWin];
+    __shared__ float ls[kAttendWin];
+    __shared__ int ired[kAttendWaves];
+    __shared__ uint32_t kred[kAttendWaves];
+    __shared__ float ored[kAttendWaves][D];
+    __shared__ float lred[kAttendWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = blockIdx.x / a.pw, w = blockIdx.x % a.pw;
+    const int row = blockIdx.x;
     const int b = row / a.h_q, j = row % a.h_q;
     const int vh = (int)(((int64_t)j * a.h_v) / a.h_q);
 
-    // segment headers -> exclusive prefix (pre[]), total count, max key
-    const int per = (a.n_sub + kThreads - 1) / kThreads;
-    const int s0 = min(a.n_sub, tid * per), s1 = min(a.n_sub, s0 + per);
-    int csum = 0;
+    u32x4 rec[SPT][4];
+    int cnt[SPT];
     uint32_t mk = 0u;
-    const int64_t hbase = (int64_t)row * a.n_sub;
-    for (int s = s0; s < s1; ++s) {
-        csum += a.seg_count[hbase + s];
-        const uint32_t k = a.seg_maxkey[hbase + s];
-        mk = mk > k ? mk : k;
+    const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int s = tid * SPT + i;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            rec[i][q] = s < a.n_sub ? ld16(rb + s * a.seg_w + q * 4) : u32x4{0u, 0u, 0u, 0u};
     }
-    int total;
-    int run = block_excl_scan(csum, ired, &total);
-    for (int s = s0; s < s1; ++s) {
-        pre[s] = run;
-        run += a.seg_count[hbase + s];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        cnt[i] = (int)rec[i][0][0];
+        mk = cnt[i] > 0 && rec[i][0][1] > mk ? rec[i][0][1] : mk;
     }
-    if (tid == 0) pre[a.n_sub] = total;
     mk = wave_max_u32(mk);
     if (lane == 0) kred[wave] = mk;
-    __syncthreads();
+    int total;
+    int mine = 0;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) mk = mk > kred[q] ? mk : kred[q];
+    for (int i = 0; i < SPT; ++i) mine += cnt[i];
+    const int pre = block_excl_scan<kAttendWaves>(mine, ired, &total);  // barriers
+#pragma unroll
+    for (int q = 0; q < kAttendWaves; ++q) mk = mk > kred[q] ? mk : kred[q];
     const float M = fkey_inv(mk);
-    const int64_t n = total;
-    const int64_t lo = n * w / a.pw, hi = n * (w + 1) / a.pw;
 
     const int e_in = tid / LPE, cl = tid % LPE;
     const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.l_kv * D + cl * 8;
@@ -310,39 +331,69 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     float lsum = 0.f;
-    for (int64_t e0 = lo; e0 < hi; e0 += (int64_t)EPB * UN) {
-        int tt[UN];
-        float pp[UN];
+    for (int w0 = 0; w0 < total; w0 += kAttendWin) {
+        const int w1 = min(total, w0 + kAttendWin);
+        // place this thread's survivors that fall in [w0, w1)
+        int e = pre;
 #pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const int64_t e = e0 + u * EPB + e_in;
-            tt[u] = -1;
-            pp[u] = 0.f;
-            if (e < hi) {
-                int lo_s = 0, hi_s = a.n_sub;  // largest s with pre[s] <= e
-                while (hi_s - lo_s > 1) {
-                    const int mid = (lo_s + hi_s) >> 1;
-                    if (pre[mid] <= e) lo_s = mid; else hi_s = mid;
+        for (int i = 0; i < SPT; ++i) {
+            const int n_i = cnt[i];
+            if (e < w1 && e + n_i > w0) {
+#pragma unroll
+                for (int k = 0; k < kRecHead; ++k) {
+                    const int q = (2 + 2 * k) / 4, c = (2 + 2 * k) % 4;
+                    const int pos = e + k;
+                    if (k < n_i && pos >= w0 && pos < w1) {
+                        lt[pos - w0] = (int)rec[i][q][c];
+                        ls[pos - w0] = __uint_as_float(rec[i][q][c + 1]);
+                    }
                 }
-                const int64_t idx = (hbase + lo_s) * a.sub_cap + (e - pre[lo_s]);
-                tt[u] = a.seg_t[idx];
-                pp[u] = expf(a.seg_s[idx] - M);
+                if (n_i > kRecHead) {
+                    const int s = tid * SPT + i;
+                    const int2 *pr = (const int2 *)(rb + s * a.seg_w) + 1;
+                    const int k0 = max(kRecHead, w0 - e), k1 = min(n_i, w1 - e);
+                    for (int k = k0; k < k1; k += 4) {
+                        int2 v[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) v[u] = k + u < k1 ? pr[k + u] : int2{0, 0};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (k + u < k1) {
+                                lt[e + k + u - w0] = v[u].x;
+                                ls[e + k + u - w0] = __int_as_float(v[u].y);
+                            }
+                    }
+                }
+            }
+            e += n_i;
+        }
+        __syncthreads();
+        const int nw = w1 - w0;
+        for (int e0 = 0; e0 < nw; e0 += EPB * UN) {
+            int tt[UN];
+            float pp[UN];
+            u32x4 vv[UN];
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const int ei = e0 + u * EPB + e_in;
+                tt[u] = ei < nw ? lt[ei] : -1;
+                pp[u] = ei < nw ? ls[ei] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                vv[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < UN; ++u) {
+                const float p = tt[u] >= 0 ? expf(pp[u] - M) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += p * bf_lo(vv[u][i]);
+                    acc[2 * i + 1] += p * bf_hi(vv[u][i]);
+                }
+                lsum += (cl == 0) ? p : 0.f;
             }
         }
-        u32x4 vv[UN];
-#pragma unroll
-        for (int u = 0; u < UN; ++u)
-            vv[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int u = 0; u < UN; ++u) {
-            const float p = pp[u];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += p * bf_lo(vv[u][i]);
-                acc[2 * i + 1] += p * bf_hi(vv[u][i]);
-            }
-            lsum += (cl == 0) ? p : 0.f;
-        }
+        __syncthreads();
     }
     // reduce over the survivors handled by the lanes of a wave sharing cl
 #pragma unroll
@@ -355,41 +406,16 @@ __global__ __launch_bounds__(kThreads) void k_attend(AttendArgs a) {
         for (int i = 0; i < 8; ++i) ored[wave][lane * 8 + i] = acc[i];
     if (lane == 0) lred[wave] = lsum;
     __syncthreads();
-    float *part = a.partial + ((int64_t)row * a.pw + w) * (D + 4);
-    if (tid < D) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < kWaves; ++q) s += ored[q][tid];
-        __hip_atomic_store(part + 4 + tid, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == 0) {
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < kWaves; ++q) s += lred[q];
-        __hip_atomic_store(part, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = atomicAdd(a.ticket + row, 1u);
-        is_last = (old == (uint32_t)(a.pw - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
     if (tid < D) {
         float so = 0.f, sl = 0.f;
-        for (int q = 0; q < a.pw; ++q) {
-            const float *pq = a.partial + ((int64_t)row * a.pw + q) * (D + 4);
-            so += __hip_atomic_load(pq + 4 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sl += __hip_atomic_load(pq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < kAttendWaves; ++q) {
+            so += ored[q][tid];
+            sl += lred[q];
         }
         a.O[(int64_t)row * D + tid] = sl > 0.f ? so / sl : 0.f;
     }
-    if (tid == 0) {
-        if (a.counts) a.counts[row] = (int32_t)n;
-        atomicExch(a.ticket + row, 0u);
-    }
+    if (tid == 0 && a.counts) a.counts[row] = total;
 }
 
 // ------------------------------------------------------------------ refresh
@@ -430,7 +456,7 @@ __device__ void find_bin_desc(const uint32_t *bins, int nbins, uint32_t k, int *
     uint32_t c = 0;
     for (int i = 0; i < per; ++i) c += bins[top - i];
     int total;
-    const uint32_t before = (uint32_t)block_excl_scan((int)c, red, &total);
+    const uint32_t before = (uint32_t)block_excl_scan<kWaves>((int)c, red, &total);
     if (before < k && k <= before + c) {
         uint32_t cum = before;
         for (int i = 0; i < per; ++i) {
@@ -467,14 +493,18 @@ __global__ __launch_bounds__(kThreads) void k_select1(RadixArgs a) {
     }
 }
 
-// Gather the order keys of the bucket holding tau into cand[row].
+// Gather the order keys of the bucket holding tau into cand[row]: keys are
+// staged in LDS, then one global reservation per block.
 __global__ __launch_bounds__(kThreads) void k_collect(RadixArgs a) {
+    __shared__ uint32_t keys[kHistBlockMax];
+    __shared__ uint32_t nk, base;
     const int row = blockIdx.x / a.bpr, blk = blockIdx.x % a.bpr;
     const uint32_t prefix = a.state[(int64_t)row * 4 + 0];
     uint32_t *fill = a.state + (int64_t)row * 4 + 3;
     const int64_t t0 = (int64_t)blk * a.blk_len, t1 = min(a.l_kv, t0 + a.blk_len);
     const float *Ar = a.A + (int64_t)row * a.ld_a;
-    uint32_t *cr = a.cand + (int64_t)row * a.l_kv;
+    if (threadIdx.x == 0) nk = 0u;
+    __syncthreads();
     for (int64_t tb = t0; tb < t1; tb += kThreads) {
         const int64_t t = tb + threadIdx.x;
         uint32_t key = 0u;
@@ -485,12 +515,17 @@ __global__ __launch_bounds__(kThreads) void k_collect(RadixArgs a) {
         }
         const uint64_t m = ballot(p);
         if (m) {
-            uint32_t base = 0u;
-            if ((threadIdx.x & 63) == 0) base = atomicAdd(fill, (uint32_t)__popcll(m));
-            base = __shfl(base, 0);
-            if (p) cr[base + mbcnt_lt(m)] = key;
+            uint32_t wb = 0u;
+            if ((threadIdx.x & 63) == 0) wb = atomicAdd(&nk, (uint32_t)__popcll(m));
+            wb = __shfl(wb, 0);
+            if (p) keys[wb + mbcnt_lt(m)] = key;
         }
     }
+    __syncthreads();
+    if (threadIdx.x == 0) base = nk ? atomicAdd(fill, nk) : 0u;
+    __syncthreads();
+    uint32_t *cr = a.cand + (int64_t)row * a.l_kv + base;
+    for (uint32_t i = threadIdx.x; i < nk; i += kThreads) cr[i] = keys[i];
 }
 
 // Finish the select on the bucket's keys: digits 20..10 then 9..0.
@@ -527,19 +562,16 @@ __global__ __launch_bounds__(kThreads) void k_select_final(RadixArgs a) {
 }
 
 // Refresh step selection from the materialised scores: A >= tau into the
-// same (row, sub-chunk) segments k_select writes.  Wave w of the block for
+// same (row, segment) records k_select writes.  Wave w of the block for
 // (row, chunk) covers positions [chunk*chunk_len + w*sub_cap, ... + sub_cap).
 struct CompactArgs {
     const float *A;
     int64_t ld_a, l_kv, chunk_len;
     int n_chunk;
     const float *tau;
-    int32_t *seg_t;
-    float *seg_s;
-    int32_t *seg_count;
-    uint32_t *seg_maxkey;
+    int32_t *seg;
     int n_sub;
-    int64_t sub_cap;
+    int64_t sub_cap, seg_w;
 };
 
 __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
@@ -550,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     const int64_t t1 = min(a.l_kv, t0 + a.sub_cap);
     const float tau = a.tau[row];
     const float *Ar = a.A + (int64_t)row * a.ld_a;
-    const int64_t sbase = ((int64_t)row * a.n_sub + sub) * a.sub_cap;
+    int2 *rec = (int2 *)(a.seg + ((int64_t)row * a.n_sub + sub) * a.seg_w);
     int cnt = 0;
     uint32_t mk = 0u;
     for (int64_t tb = t0; tb < t1; tb += 64) {
@@ -563,19 +595,14 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
         }
         const uint64_t m = ballot(p);
         if (p) {
-            const int pos = cnt + mbcnt_lt(m);
-            a.seg_t[sbase + pos] = (int32_t)t;
-            a.seg_s[sbase + pos] = s;
+            rec[1 + cnt + mbcnt_lt(m)] = int2{(int)t, __float_as_int(s)};
             const uint32_t k = fkey(s);
             mk = mk > k ? mk : k;
         }
         cnt += __popcll(m);
     }
     mk = wave_max_u32(mk);
-    if (lane == 0) {
-        a.seg_count[(int64_t)row * a.n_sub + sub] = cnt;
-        a.seg_maxkey[(int64_t)row * a.n_sub + sub] = mk;
-    }
+    if (lane == 0) rec[0] = int2{cnt, (int)mk};
 }
 
 // ------------------------------------------------------------------ dense
@@ -816,10 +843,9 @@ __global__ void k_fill_u8(uint8_t *p, int64_t n, uint8_t v) {
 }
 
 struct MaskArgs {
-    const int32_t *seg_t;
-    const int32_t *seg_count;
+    const int32_t *seg;
     int n_sub;
-    int64_t sub_cap, l_kv;
+    int64_t sub_cap, seg_w, l_kv;
     uint8_t *mask;  // [rows][l_kv]
 };
 
@@ -827,11 +853,11 @@ struct MaskArgs {
 __global__ __launch_bounds__(kThreads) void k_mask(MaskArgs a) {
     const int64_t rs = blockIdx.x;  // row * n_sub + sub
     const int64_t row = rs / a.n_sub;
-    int64_t cnt = a.seg_count[rs];
+    const int2 *rec = (const int2 *)(a.seg + rs * a.seg_w);
+    int64_t cnt = rec[0].x;
     cnt = cnt < 0 ? 0 : (cnt > a.sub_cap ? a.sub_cap : cnt);  // never trust stale contents
-    const int32_t *st = a.seg_t + rs * a.sub_cap;
     for (int64_t i = threadIdx.x; i < cnt; i += kThreads) {
-        const int32_t t = st[i];
+        const int32_t t = rec[1 + i].x;
         if (t >= 0 && t < a.l_kv) a.mask[row * a.l_kv + t] = 1;
     }
 }

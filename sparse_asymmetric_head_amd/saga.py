@@ -41,10 +41,8 @@ class WsLayout(ctypes.Structure):
         ("bytes", ctypes.c_size_t),
         ("scores_off", ctypes.c_size_t),
         ("scores_ld", ctypes.c_int64),
-        ("seg_count_off", ctypes.c_size_t),
-        ("seg_maxkey_off", ctypes.c_size_t),
         ("seg_off", ctypes.c_size_t),
-        ("seg_score_off", ctypes.c_size_t),
+        ("seg_words", ctypes.c_int64),
         ("chunk_len", ctypes.c_int64),
         ("n_chunk", ctypes.c_int64),
         ("n_seg", ctypes.c_int64),

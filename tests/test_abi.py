@@ -76,13 +76,12 @@ def test_workspace_layout_consistent(L, shape):
     assert lay.bytes == nbytes
     assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
     assert lay.n_seg == 4 * lay.n_chunk and lay.seg_cap * 4 == lay.chunk_len
+    assert lay.n_seg <= 1024
     assert lay.scores_ld >= l_kv and lay.scores_ld % 4 == 0
+    assert lay.seg_words % 16 == 0 and lay.seg_words >= 2 + 2 * lay.seg_cap
     rows = B * h_q
     regions = sorted([
-        (lay.seg_count_off, rows * lay.n_seg * 4),
-        (lay.seg_maxkey_off, rows * lay.n_seg * 4),
-        (lay.seg_off, rows * lay.n_seg * lay.seg_cap * 4),
-        (lay.seg_score_off, rows * lay.n_seg * lay.seg_cap * 4),
+        (lay.seg_off, rows * lay.n_seg * lay.seg_words * 4),
         (lay.scores_off, rows * lay.scores_ld * 4),
     ])
     for (o1, n1), (o2, _) in zip(regions, regions[1:]):
