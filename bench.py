@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
-    ap.add_argument("--cpu-sample-layers", type=int, default=4)
+    ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--kernel-timing-steps", type=int, default=8)
     return ap.parse_args()
 
@@ -230,27 +230,29 @@ def main() -> int:
 
         lib = oracle.load()
         S = max(1, min(args.cpu_sample_layers, L))
-        t_ref = t_two = 0.0
+        steps = R + 1  # one refresh step and R non-refresh steps per layer
+        t_one = t_all = 0.0
         for l in range(S):
-            x = wl.make_layer(cfg, l, device=dev, cfg_index=ci, steps=2)
+            x = wl.make_layer(cfg, l, device=dev, cfg_index=ci, steps=steps)
             Qh, Kh, Vh = (oracle._u16(x[k]) for k in ("Q", "K", "V"))
             del x
             c0 = time.perf_counter()
             oracle.trajectory(Qh[:1], Kh, Vh, h_k, h_v, N, R, lib=lib)
             c1 = time.perf_counter()
-            oracle.trajectory(Qh[:2], Kh, Vh, h_k, h_v, N, R, lib=lib)
+            oracle.trajectory(Qh, Kh, Vh, h_k, h_v, N, R, lib=lib)
             c2 = time.perf_counter()
-            t_ref += c1 - c0
-            t_two += c2 - c1
-        t_ref /= S
-        t_norm = max(t_two / S - t_ref, 0.0)
+            t_one += c1 - c0
+            t_all += c2 - c1
+        t_ref = t_one / S
+        t_norm = max((t_all / S - t_ref) / (steps - 1), 0.0)
         cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
         cpu = {"value": round(cpu_us, 1), "unit": "us/step", "cores": oracle.num_threads(lib),
                "kind": "oracle",
-               "sample": (f"{S} of {L} layers x (1 refresh step + 1 non-refresh step) of "
-                          f"{cfg.name}, per-layer costs amortised over R={R} and scaled to "
-                          f"{L} layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s "
-                          f"per layer-step)")}
+               "sample": (f"{S} of {L} layers x {steps + 1} oracle layer-steps each (one refresh "
+                          f"step alone, then a refresh + {steps - 1} non-refresh steps) of "
+                          f"{cfg.name}; per-layer costs amortised over R={R} and scaled to {L} "
+                          f"layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
+                          f"layer-step, {t_one + t_all:.1f} s of oracle time)")}
         log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads")
 
     out = {

@@ -19,7 +19,7 @@ using namespace saga;
 #define SAGA_SELECT_BLOCKS 512
 #endif
 constexpr int kTargetSelectBlocks = SAGA_SELECT_BLOCKS;  // streaming blocks per launch
-constexpr int64_t kChunkUnit = 256;       // chunk_len granularity (positions)
+constexpr int64_t kChunkUnit = 64 * SAGA_SELECT_U;  // chunk_len granularity: one wave-iteration stride of all 4 waves
 constexpr int64_t kHistBlock = kHistBlockMax;  // positions per histogram/collect block
 constexpr size_t kAlign = 256;
 

@@ -65,18 +65,29 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
     return v;
 }
 
+// DPP controls (GFX9 encoding).
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS traffic).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr8, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xc, 0xf, false);
+    return x;
+}
+
 // Block-wide exclusive scan of v over the NW*64 threads of a block; returns
 // the prefix, *total receives the sum.  Uses red[NW] of LDS; contains two
 // barriers, so every thread of the block must call it.
 template <int NW>
 __device__ __forceinline__ int block_excl_scan(int v, int *red, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) red[wave] = x;
     __syncthreads();
     int before = 0, tot = 0;

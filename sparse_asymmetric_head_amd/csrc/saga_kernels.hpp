@@ -35,8 +35,11 @@
 
 namespace saga {
 
-#ifndef SAGA_PREFETCH
-#define SAGA_PREFETCH 1  // k_select: load the next tiles before scoring the current ones
+#ifndef SAGA_KMAP
+#define SAGA_KMAP 1  // k_select: 1 = each MFMA k-step loads contiguous 64-byte half rows
+#endif
+#ifndef SAGA_SELECT_U
+#define SAGA_SELECT_U 4  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
 #endif
 #ifndef SAGA_NT_LOADS
 #define SAGA_NT_LOADS 1  // k_select: non-temporal (streaming) loads of the key cache
@@ -91,8 +94,18 @@ struct SelectArgs {
 // segment record of that head.
 template <int D, int NT, bool MATERIALIZE>
 __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
+    // First d-index of the 8 elements lane quarter lq supplies at MFMA
+    // k-step s; the query operand uses the same map, so any permutation of
+    // the d axis gives the same dot products.
+    auto kcol = [](int lq, int s) {
+#if SAGA_KMAP
+        return s * 32 + lq * 8;          // a k-step reads 64 contiguous bytes of 16 rows
+#else
+        return lq * (D / 4) + s * 8;     // a lane reads D/2 contiguous bytes of its row
+#endif
+    };
     constexpr int KS = D / 32;             // MFMA k-steps per row
-    constexpr int U = (D == 64) ? 4 : 2;   // tiles per wave iteration (128 B per lane)
+    constexpr int U = SAGA_SELECT_U * 64 / D;  // tiles per wave iteration
     constexpr int QW = D / 4;              // elements of a row per lane quarter
     __shared__ int2 st[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
 
@@ -111,10 +124,10 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
         const int j = j_lo + nt * 16 + ln;
         const bool jv = j < j_hi;
-        const uint16_t *qp = a.Q + ((int64_t)b * a.h_q + (jv ? j : j_lo)) * D + lq * QW;
+        const uint16_t *qp = a.Q + ((int64_t)b * a.h_q + (jv ? j : j_lo)) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            u32x4 r = ld16(qp + s * 8);
+            u32x4 r = ld16(qp + kcol(lq, s));
             if (!jv) r = u32x4{0u, 0u, 0u, 0u};
             qop[nt][s] = as_bf16x8(r);
         }
@@ -144,27 +157,8 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
         }
     };
 
-    // K tiles of one wave iteration; the next iteration's tiles are loaded
-    // before the current ones are scored so that loads stay in flight.
-    auto load_tiles = [&](u32x4 (&kr)[U][KS], int64_t t0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = t0 + u * 16 + ln;
-            const uint16_t *kp = Kb + row * D + lq * QW;
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kr[u][s] = (row < t_end) ? ld_k(kp + s * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    constexpr int64_t kStride = kWaves * 16 * U;
-    u32x4 kr[U][KS];
-    int64_t t0 = t_begin + wave * 16 * U;
-    if (t0 < t_end) load_tiles(kr, t0);
-    for (; t0 < t_end; t0 += kStride) {
-#if SAGA_PREFETCH
-        u32x4 kn[U][KS];
-        if (t0 + kStride < t_end) load_tiles(kn, t0 + kStride);
-#endif
+    // Score, compare and stage one wave iteration (U tiles starting at t0).
+    auto process = [&](const u32x4 (&kr)[U][KS], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tr = t0 + u * 16 + lq * 4;  // position of acc[0]
@@ -226,14 +220,36 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                 }
             }
         }
-#if SAGA_PREFETCH
+    };
+    // K tiles of one wave iteration.  Rows past the end of the chunk are
+    // clamped to its last row (their scores are masked), so the loads need no
+    // branches and two buffers can be kept in flight.
+    const int64_t last = t_end - 1;
+    auto load_tiles = [&](u32x4 (&kr)[U][KS], int64_t t0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            int64_t row = t0 + u * 16 + ln;
+            row = row < last ? row : last;
+            const uint16_t *kp = Kb + row * D;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) kr[u][s] = kn[u][s];
-#else
-        if (t0 + kStride < t_end) load_tiles(kr, t0 + kStride);
-#endif
+            for (int s = 0; s < KS; ++s) kr[u][s] = ld_k(kp + kcol(lq, s));
+        }
+    };
+    constexpr int64_t kStride = kWaves * 16 * U;
+    int64_t t0 = t_begin + wave * 16 * U;
+    if (t0 < t_end) {
+        u32x4 ka[U][KS], kb[U][KS];
+        load_tiles(ka, t0);
+        for (;;) {
+            load_tiles(kb, t0 + kStride);   // next tiles (clamped past the end)
+            process(ka, t0);
+            t0 += kStride;
+            if (t0 >= t_end) break;
+            load_tiles(ka, t0 + kStride);
+            process(kb, t0);
+            t0 += kStride;
+            if (t0 >= t_end) break;
+        }
     }
     if constexpr (!MATERIALIZE) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
