@@ -23,6 +23,72 @@ import time
 
 METRIC = "µs per decode-attention step and achieved HBM GB/s at 128K ctx, 1 MI355X"
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_select_traffic_llama32-1b-128k-16L.json")
+DOMINANT = "saga::k_select<64, 1, false>"
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources, so counter figures taken for other code are not reused."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_asymmetric_head_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, out: str) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
+    `bench.py --calibrate-copy MIB` into HBM bytes per launch of the dominant kernel,
+    each counter scaled by what it reads for the calibration copy of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(path):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
+                float(r["Counter_Value"]))
+        return vals
+
+    known_kib = copy_mib * 1024.0
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        v = per_kernel(path)
+        copy = [x for (k, g), xs in v.items() if "copyBuffer" in k for x in xs
+                if x > 0.25 * known_kib]
+        dom = [x for (k, g), xs in v.items() if k.replace("void ", "", 1).startswith(DOMINANT)
+               for x in xs]
+        if not copy or not dom:
+            raise SystemExit(f"{path}: calibration copy or {DOMINANT} not found")
+        factor = known_kib / statistics.median(copy)
+        res[name] = {"counter_kib_per_launch": statistics.median(dom), "launches": len(dom),
+                     "copy_counter_kib": statistics.median(copy), "scale": round(factor, 4)}
+    traffic = sum(r["counter_kib_per_launch"] * r["scale"] for r in res.values()) * 1024.0
+    summary = {"kernel": DOMINANT, "workload": "llama32-1b-128k-16L",
+               "traffic_bytes_per_launch": round(traffic), "counters": res,
+               "calibration": f"__amd_rocclr_copyBuffer of {copy_mib} MiB (torch D2D copy)",
+               "kernel_source_sha256": kernel_source_hash()}
+    with open(out, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    return summary
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when the kernel sources changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def log(msg: str) -> None:
@@ -40,11 +106,20 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--kernel-timing-steps", type=int, default=8)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the dominant kernel's counter traffic summary and exit")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 4 plain device-to-device copies of MIB MiB (a reference "
+                         "kernel of known traffic for hardware counter runs)")
     return ap.parse_args()
 
 
 def main() -> int:
     args = parse()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                                       args.calibrate_copy or 256, TRAFFIC_FILE)))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the SAGA decode step here runs on a single "
@@ -69,6 +144,17 @@ def main() -> int:
                                               cfg.N, cfg.R, cfg.steps, cfg.layers)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 4 copies of {args.calibrate_copy} MiB "
+            f"({n} bytes read and {n} written per copy)")
+        del src, dst
     log(f"workload {cfg.name}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv} N={N} "
         f"R={R} layers={L}")
 
@@ -276,7 +362,8 @@ def main() -> int:
         "mean_survivors_per_row": round(mean_count, 1),
         "roofline": {"bound": "hbm", "kernel": "k_select (score + compare + compact)",
                      "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                     "traffic": measured_traffic(), "traffic_unit": "HBM bytes per launch",
                      "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg},
         "dense_gqa": dense,
         "cpu_baseline": cpu,

@@ -448,15 +448,40 @@ struct RadixArgs {
     float *tau;       // [rows]
 };
 
-// Digit 1: bits 31..21 of the order key, per-block LDS histogram.
+// Digit 1: bits 31..21 of the order key, per-block LDS histogram.  A block
+// covers blk_len positions of one row; each thread issues all its float4
+// loads before touching the histogram.
+constexpr int kRadixVec = kHistBlockMax / (4 * kThreads);  // float4 loads per thread (8)
+
+__device__ __forceinline__ void load_block_scores(const float *Ar, int64_t t0, int64_t t1,
+                                                  f32x4 (&v)[kRadixVec]) {
+#pragma unroll
+    for (int u = 0; u < kRadixVec; ++u) {
+        const int64_t t = t0 + ((int64_t)u * kThreads + threadIdx.x) * 4;
+        if (t + 3 < t1) {
+            v[u] = *(const f32x4 *)(Ar + t);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[u][c] = (t + c < t1) ? Ar[t + c] : NAN;
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void k_hist(RadixArgs a) {
     __shared__ uint32_t h[kHistBins];
     const int row = blockIdx.x / a.bpr, blk = blockIdx.x % a.bpr;
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
-    __syncthreads();
     const int64_t t0 = (int64_t)blk * a.blk_len, t1 = min(a.l_kv, t0 + a.blk_len);
-    const float *Ar = a.A + (int64_t)row * a.ld_a;
-    for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) atomicAdd(&h[fkey(Ar[t]) >> 21], 1u);
+    f32x4 v[kRadixVec];
+    load_block_scores(a.A + (int64_t)row * a.ld_a, t0, t1, v);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kRadixVec; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t t = t0 + ((int64_t)u * kThreads + threadIdx.x) * 4 + c;
+            if (t < t1) atomicAdd(&h[fkey(v[u][c]) >> 21], 1u);
+        }
     __syncthreads();
     uint32_t *hg = a.hist + (int64_t)row * kHistBins;
     for (int i = threadIdx.x; i < kHistBins; i += kThreads)
@@ -518,25 +543,25 @@ __global__ __launch_bounds__(kThreads) void k_collect(RadixArgs a) {
     const uint32_t prefix = a.state[(int64_t)row * 4 + 0];
     uint32_t *fill = a.state + (int64_t)row * 4 + 3;
     const int64_t t0 = (int64_t)blk * a.blk_len, t1 = min(a.l_kv, t0 + a.blk_len);
-    const float *Ar = a.A + (int64_t)row * a.ld_a;
     if (threadIdx.x == 0) nk = 0u;
+    f32x4 v[kRadixVec];
+    load_block_scores(a.A + (int64_t)row * a.ld_a, t0, t1, v);
     __syncthreads();
-    for (int64_t tb = t0; tb < t1; tb += kThreads) {
-        const int64_t t = tb + threadIdx.x;
-        uint32_t key = 0u;
-        bool p = false;
-        if (t < t1) {
-            key = fkey(Ar[t]);
-            p = (key >> 21) == prefix;
+#pragma unroll
+    for (int u = 0; u < kRadixVec; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t t = t0 + ((int64_t)u * kThreads + threadIdx.x) * 4 + c;
+            const uint32_t key = fkey(v[u][c]);
+            const bool p = t < t1 && (key >> 21) == prefix;
+            const uint64_t m = ballot(p);
+            if (m) {
+                uint32_t wb = 0u;
+                if ((threadIdx.x & 63) == 0) wb = atomicAdd(&nk, (uint32_t)__popcll(m));
+                wb = __shfl(wb, 0);
+                if (p) keys[wb + mbcnt_lt(m)] = key;
+            }
         }
-        const uint64_t m = ballot(p);
-        if (m) {
-            uint32_t wb = 0u;
-            if ((threadIdx.x & 63) == 0) wb = atomicAdd(&nk, (uint32_t)__popcll(m));
-            wb = __shfl(wb, 0);
-            if (p) keys[wb + mbcnt_lt(m)] = key;
-        }
-    }
     __syncthreads();
     if (threadIdx.x == 0) base = nk ? atomicAdd(fill, nk) : 0u;
     __syncthreads();
@@ -601,21 +626,34 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     int2 *rec = (int2 *)(a.seg + ((int64_t)row * a.n_sub + sub) * a.seg_w);
     int cnt = 0;
     uint32_t mk = 0u;
-    for (int64_t tb = t0; tb < t1; tb += 64) {
-        const int64_t t = tb + lane;
-        float s = 0.f;
-        bool p = false;
-        if (t < t1) {
-            s = Ar[t];
-            p = s >= tau;
+    // 256 positions per pass: lane l takes positions 4l..4l+3 (one float4);
+    // survivors are ranked in position order.
+    for (int64_t tb = t0; tb < t1; tb += 256) {
+        const int64_t t = tb + 4 * lane;
+        f32x4 v;
+        if (t + 3 < t1) {
+            v = *(const f32x4 *)(Ar + t);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = (t + c < t1) ? Ar[t + c] : -INFINITY;
         }
-        const uint64_t m = ballot(p);
-        if (p) {
-            rec[1 + cnt + mbcnt_lt(m)] = int2{(int)t, __float_as_int(s)};
-            const uint32_t k = fkey(s);
-            mk = mk > k ? mk : k;
+        bool p[4];
+        int mine = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            p[c] = (t + c < t1) && v[c] >= tau;
+            mine += p[c];
         }
-        cnt += __popcll(m);
+        const int incl = wave_incl_scan(mine);
+        int pos = cnt + incl - mine;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (p[c]) {
+                rec[1 + pos++] = int2{(int)(t + c), __float_as_int(v[c])};
+                const uint32_t k = fkey(v[c]);
+                mk = mk > k ? mk : k;
+            }
+        cnt += __shfl(incl, 63);
     }
     mk = wave_max_u32(mk);
     if (lane == 0) rec[0] = int2{cnt, (int)mk};
