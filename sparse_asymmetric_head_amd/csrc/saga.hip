@@ -16,9 +16,13 @@ namespace {
 using namespace saga;
 
 #ifndef SAGA_SELECT_BLOCKS
-#define SAGA_SELECT_BLOCKS 512
+#define SAGA_SELECT_BLOCKS 256
 #endif
 constexpr int kTargetSelectBlocks = SAGA_SELECT_BLOCKS;  // streaming blocks per launch
+#ifndef SAGA_DENSE_BLOCKS
+#define SAGA_DENSE_BLOCKS 512
+#endif
+constexpr int kTargetDenseBlocks = SAGA_DENSE_BLOCKS;  // dense baseline blocks per launch
 constexpr int64_t kChunkUnit = 64 * SAGA_SELECT_U;  // chunk_len granularity: one wave-iteration stride of all 4 waves
 constexpr int64_t kHistBlock = kHistBlockMax;  // positions per histogram/collect block
 constexpr size_t kAlign = 256;
@@ -109,7 +113,7 @@ int make_dense_plan(int B, int h_q, int h_kv, int d, int64_t l_kv, DensePlan *p)
     p->rows = B * h_q;
     p->gmax = (int)ceil_div(h_q, h_kv);
     const int64_t pairs = (int64_t)B * h_kv;
-    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), kChunkUnit) * kChunkUnit;
+    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetDenseBlocks), kChunkUnit) * kChunkUnit;
     const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kChunkUnit) * kChunkUnit;
     if (cl < cl_min) cl = cl_min;
     if (cl < kChunkUnit) cl = kChunkUnit;
@@ -194,9 +198,11 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.O = O;
     aa.counts = counts;
     if (p.d == 64)
-        hipLaunchKernelGGL(k_attend<64>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
+        hipLaunchKernelGGL(k_attend<64>, dim3(p.rows * kAttendSplit), dim3(kAttendThreads), 0, s,
+                           aa);
     else
-        hipLaunchKernelGGL(k_attend<128>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
+        hipLaunchKernelGGL(k_attend<128>, dim3(p.rows * kAttendSplit), dim3(kAttendThreads), 0,
+                           s, aa);
     return launch_status();
 }
 

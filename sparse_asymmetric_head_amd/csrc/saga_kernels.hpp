@@ -287,30 +287,42 @@ constexpr int kAttendWaves = 8;
 constexpr int kAttendThreads = kAttendWaves * kWave;
 constexpr int kAttendWin = 4096;  // survivors staged in LDS per window
 constexpr int kSegPerThread = kMaxSub / kAttendThreads;
+#ifndef SAGA_ATTEND_SPLIT
+#define SAGA_ATTEND_SPLIT 4  // blocks per row, each owning d/SPLIT output columns
+#endif
+constexpr int kAttendSplit = SAGA_ATTEND_SPLIT;
 
-// One workgroup per row (b, j).  Thread i owns segments 2i and 2i+1 and reads
-// the first 64 bytes of both records in one go (count, max key and up to
-// seven survivors each); an exclusive scan of the counts places every
-// survivor in the row's list, which is built in LDS (survivors past the
-// seventh of a segment are read from the rest of its record).  Then every
-// group of D/8 lanes takes one survivor per round: weight exp(s - M) with M
-// the row maximum, 16-byte loads of its V row, fp32 accumulation.  Lists
-// longer than kAttendWin are processed in windows.
+// kAttendSplit blocks per row (b, j), block c owning output columns
+// [c*D/S, (c+1)*D/S).  Every block reads the row's records the same way:
+// thread i owns segments 2i and 2i+1 and reads the first 64 bytes of both in
+// one go (count, max key and up to seven survivors each); an exclusive scan
+// of the counts places every survivor in the row's list, built in LDS
+// (survivors past the seventh of a segment come from the rest of the
+// record); M = the row maximum from the record headers.  Groups of
+// D/(8*S) lanes then take one survivor per round: weight exp(s - M), 16-byte
+// loads of the block's columns of its V row, fp32 accumulation.  All blocks
+// of a row see the same list in the same order, so the weight sums agree and
+// the result is deterministic.  Lists longer than kAttendWin go in windows.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
-    constexpr int LPE = D / 8;                  // lanes per survivor (16 B each)
+    constexpr int DC = D / kAttendSplit;        // columns of this block
+    constexpr int LPE = DC / 8;                 // lanes per survivor (16 B each)
+    constexpr int EPW = kWave / LPE;            // survivors per wave round
     constexpr int EPB = kAttendThreads / LPE;   // survivors per block round
-    constexpr int UN = 8;
+    constexpr int UN = 4;
     constexpr int SPT = kSegPerThread;
+    constexpr int NPART = kAttendThreads / DC;  // partial sums per column
+    static_assert(DC % 8 == 0 && LPE >= 1 && kWave % LPE == 0, "attend column split");
     __shared__ int lt[kAttendWin];
     __shared__ float ls[kAttendWin];
     __shared__ int ired[kAttendWaves];
     __shared__ uint32_t kred[kAttendWaves];
-    __shared__ float ored[kAttendWaves][D];
+    __shared__ float red[kAttendWaves * EPW][DC];
+    __shared__ float part[NPART][DC];
     __shared__ float lred[kAttendWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / kAttendSplit, csl = blockIdx.x % kAttendSplit;
     const int b = row / a.h_q, j = row % a.h_q;
     const int vh = (int)(((int64_t)j * a.h_v) / a.h_q);
 
@@ -325,24 +337,23 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         for (int q = 0; q < 4; ++q)
             rec[i][q] = s < a.n_sub ? ld16(rb + s * a.seg_w + q * 4) : u32x4{0u, 0u, 0u, 0u};
     }
+    int mine = 0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         cnt[i] = (int)rec[i][0][0];
         mk = cnt[i] > 0 && rec[i][0][1] > mk ? rec[i][0][1] : mk;
+        mine += cnt[i];
     }
     mk = wave_max_u32(mk);
     if (lane == 0) kred[wave] = mk;
     int total;
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) mine += cnt[i];
     const int pre = block_excl_scan<kAttendWaves>(mine, ired, &total);  // barriers
 #pragma unroll
     for (int q = 0; q < kAttendWaves; ++q) mk = mk > kred[q] ? mk : kred[q];
     const float M = fkey_inv(mk);
 
     const int e_in = tid / LPE, cl = tid % LPE;
-    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.l_kv * D + cl * 8;
+    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.l_kv * D + csl * DC + cl * 8;
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -411,27 +422,32 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         }
         __syncthreads();
     }
-    // reduce over the survivors handled by the lanes of a wave sharing cl
+    // sum over the block's survivor groups in a fixed order: every lane
+    // parks its 8 column sums, NPART threads per column add fixed subsets,
+    // then one thread per column adds the NPART partials.
 #pragma unroll
-    for (int o = LPE; o < 64; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o);
+    for (int i = 0; i < 8; ++i) red[e_in][cl * 8 + i] = acc[i];
     lsum = wave_sum(lsum);
-    if (lane < LPE)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ored[wave][lane * 8 + i] = acc[i];
     if (lane == 0) lred[wave] = lsum;
     __syncthreads();
-    if (tid < D) {
+    {
+        const int c = tid % DC, q = tid / DC;
+        constexpr int GPP = kAttendWaves * EPW / NPART;  // groups per partial
+        float sacc = 0.f;
+#pragma unroll
+        for (int g = 0; g < GPP; ++g) sacc += red[q * GPP + g][c];
+        part[q][c] = sacc;
+    }
+    __syncthreads();
+    if (tid < DC) {
         float so = 0.f, sl = 0.f;
 #pragma unroll
-        for (int q = 0; q < kAttendWaves; ++q) {
-            so += ored[q][tid];
-            sl += lred[q];
-        }
-        a.O[(int64_t)row * D + tid] = sl > 0.f ? so / sl : 0.f;
+        for (int q = 0; q < NPART; ++q) so += part[q][tid];
+#pragma unroll
+        for (int q = 0; q < kAttendWaves; ++q) sl += lred[q];
+        a.O[(int64_t)row * D + csl * DC + tid] = sl > 0.f ? so / sl : 0.f;
     }
-    if (tid == 0 && a.counts) a.counts[row] = total;
+    if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
 }
 
 // ------------------------------------------------------------------ refresh

@@ -267,3 +267,77 @@ def test_dense_gqa_full_size(ci):
     assert rel_err(O, ref) <= OUT_RTOL
     del x
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+def test_graph_capture_replays_match_eager():
+    """A captured decode step (refresh and non-refresh) replayed several times,
+    with eager work and synchronisations in between, matches the eager result
+    on every replay (no memset nodes; counters return to zero)."""
+    x = wl.make_random(2, 12, 3, 6, 64, 9000, seed=21, device="cuda", steps=3, planted=32)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    B, h_q, d = Q.shape[1:]
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    N = 77
+    dev = Q.device
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N), dev)
+    q = torch.empty_like(Q[0])
+    tau = torch.zeros(B, h_q, dtype=torch.float32, device=dev)
+    O = torch.empty(B, h_q, d, dtype=torch.float32, device=dev)
+    cnt = torch.empty(B, h_q, dtype=torch.int32, device=dev)
+    s = torch.cuda.Stream()
+    ref = {}
+    with torch.cuda.stream(s):
+        for refresh, t in ((True, 0), (False, 1)):
+            q.copy_(Q[t])
+            saga.saga_decode_step(q, K, V, N, tau, refresh, O, cnt, ws)
+            s.synchronize()
+            ref[refresh] = (O.clone(), cnt.clone(), tau.clone())
+        graphs = {}
+        for refresh in (True, False):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                saga.saga_decode_step(q, K, V, N, tau, refresh, O, cnt, ws)
+            graphs[refresh] = g
+        for rep in range(3):
+            for refresh, t in ((True, 0), (False, 1)):
+                q.copy_(Q[t])
+                O.fill_(float("nan"))
+                cnt.fill_(-1)
+                graphs[refresh].replay()
+                s.synchronize()
+                assert torch.equal(O, ref[refresh][0]), (rep, refresh)
+                assert torch.equal(cnt, ref[refresh][1]), (rep, refresh)
+                assert torch.equal(tau, ref[refresh][2]), (rep, refresh)
+                # eager work on the same workspace between replays
+                saga.saga_decode_step(q, K, V, N, tau, refresh, O, cnt, ws)
+                s.synchronize()
+
+
+def test_select_attend_halves_equal_decode_step():
+    """saga_select followed by saga_attend is exactly saga_decode_step."""
+    x = wl.make_random(1, 16, 2, 8, 128, 7000, seed=22, device="cuda", steps=2, planted=16)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    B, h_q, d = Q.shape[1:]
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    N = 100
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
+    outs = []
+    for split in (False, True):
+        tau = torch.zeros(B, h_q, dtype=torch.float32, device="cuda")
+        O = torch.empty(B, h_q, d, dtype=torch.float32, device="cuda")
+        cnt = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+        res = []
+        for t, refresh in ((0, True), (1, False)):
+            if split:
+                saga.saga_select(Q[t], K, h_v, N, tau, refresh, ws)
+                saga.saga_attend(V, B, h_q, h_k, N, O, cnt, ws)
+            else:
+                saga.saga_decode_step(Q[t], K, V, N, tau, refresh, O, cnt, ws)
+            torch.cuda.synchronize()
+            res.append((O.clone(), cnt.clone(), tau.clone()))
+        outs.append(res)
+    for a, b in zip(*outs):
+        for u, v in zip(a, b):
+            assert torch.equal(u, v)
