@@ -104,7 +104,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
-    ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--cpu-sample-layers", type=int, default=16)
     ap.add_argument("--kernel-timing-steps", type=int, default=8)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the dominant kernel's counter traffic summary and exit")
@@ -319,7 +319,7 @@ def main() -> int:
 
         lib = oracle.load()
         S = max(1, min(args.cpu_sample_layers, L))
-        steps = R + 1  # one refresh step and R non-refresh steps per layer
+        steps = 2 * R + 1  # refreshes at 0 and R, 2R - 1 non-refresh steps per layer
         t_one = t_all = 0.0
         for l in range(S):
             x = wl.make_layer(cfg, l, device=dev, cfg_index=ci, steps=steps)
@@ -333,12 +333,13 @@ def main() -> int:
             t_one += c1 - c0
             t_all += c2 - c1
         t_ref = t_one / S
-        t_norm = max((t_all / S - t_ref) / (steps - 1), 0.0)
+        # the full trajectory holds 2 refresh steps and steps - 2 non-refresh ones
+        t_norm = max((t_all / S - 2 * t_ref) / (steps - 2), 0.0)
         cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
         cpu = {"value": round(cpu_us, 1), "unit": "us/step", "cores": oracle.num_threads(lib),
                "kind": "oracle",
                "sample": (f"{S} of {L} layers x {steps + 1} oracle layer-steps each (one refresh "
-                          f"step alone, then a refresh + {steps - 1} non-refresh steps) of "
+                          f"step alone, then {steps} steps with refreshes at 0 and {R}) of "
                           f"{cfg.name}; per-layer costs amortised over R={R} and scaled to {L} "
                           f"layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
                           f"layer-step, {t_one + t_all:.1f} s of oracle time)")}

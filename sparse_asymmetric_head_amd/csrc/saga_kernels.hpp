@@ -692,11 +692,11 @@ struct DenseArgs {
 template <int D, int GMAX>
 __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     constexpr int KS = D / 32;
-    constexpr int U = (D == 64) ? 4 : 2;
-    constexpr int QW = D / 4;
+    constexpr int U = SAGA_SELECT_U * 64 / D;
     constexpr int LPR = D / 8;          // lanes per V row
     constexpr int RPI = 64 / LPR;       // V rows per wave load
     constexpr int RPL = 16 / RPI;       // V rows per lane per tile
+    constexpr bool kPingPong = GMAX <= 8;  // two tile buffers fit in registers
     __shared__ float p_lds[kWaves][U * 16][16];
     __shared__ float al_lds[kWaves][16];
     __shared__ float wm[kWaves][16], wl[kWaves][16];
@@ -711,15 +711,16 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     const int G = j_hi - j_lo;
     const int64_t t_begin = (int64_t)chunk * a.chunk_len;
     const int64_t t_end = min(a.l_kv, t_begin + a.chunk_len);
+    auto kcol = [](int lq, int s) { return s * 32 + lq * 8; };  // same d-axis map for Q and K
 
     bf16x8 qop[KS];
     {
         const int j = j_lo + ln;
         const bool jv = ln < G;
-        const uint16_t *qp = a.Q + ((int64_t)b * a.h_q + (jv ? j : j_lo)) * D + lq * QW;
+        const uint16_t *qp = a.Q + ((int64_t)b * a.h_q + (jv ? j : j_lo)) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            u32x4 r = ld16(qp + s * 8);
+            u32x4 r = ld16(qp + kcol(lq, s));
             if (!jv) r = u32x4{0u, 0u, 0u, 0u};
             qop[s] = as_bf16x8(r);
         }
@@ -734,24 +735,27 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     const uint16_t *Kb = a.K + (int64_t)bg * a.l_kv * D;
     const uint16_t *Vb = a.V + (int64_t)bg * a.l_kv * D;
     const int vr = lane / LPR, vc = (lane % LPR) * 8;
+    const int64_t last = t_end - 1;
 
-    for (int64_t t0 = t_begin + wave * 16 * U; t0 < t_end; t0 += kWaves * 16 * U) {
-        u32x4 kr[U][KS];
-        u32x4 vv[U][RPL];
+    // K and V tiles of one wave iteration; rows past the chunk are clamped to
+    // its last row (their scores are set to -inf, so they weigh nothing).
+    auto load_tiles = [&](u32x4 (&kr)[U][KS], u32x4 (&vv)[U][RPL], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t row = t0 + u * 16 + ln;
-            const uint16_t *kp = Kb + row * D + lq * QW;
+            int64_t row = t0 + u * 16 + ln;
+            row = row < last ? row : last;
+            const uint16_t *kp = Kb + row * D;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-                kr[u][s] = (row < t_end) ? ld16_stream(kp + s * 8) : u32x4{0u, 0u, 0u, 0u};
+            for (int s = 0; s < KS; ++s) kr[u][s] = ld_k(kp + kcol(lq, s));
 #pragma unroll
             for (int k = 0; k < RPL; ++k) {
-                const int64_t vrow = t0 + u * 16 + vr + k * RPI;
-                vv[u][k] = (vrow < t_end) ? ld16_stream(Vb + vrow * D + vc)
-                                          : u32x4{0u, 0u, 0u, 0u};
+                int64_t vrow = t0 + u * 16 + vr + k * RPI;
+                vrow = vrow < last ? vrow : last;
+                vv[u][k] = ld_k(Vb + vrow * D + vc);
             }
         }
+    };
+    auto process = [&](const u32x4 (&kr)[U][KS], const u32x4 (&vv)[U][RPL], int64_t t0) {
         float sc[U][4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -814,6 +818,33 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
             }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
+    };
+
+    constexpr int64_t kStride = kWaves * 16 * U;
+    int64_t t0 = t_begin + wave * 16 * U;
+    if (t0 < t_end) {
+        u32x4 ka[U][KS], va[U][RPL];
+        load_tiles(ka, va, t0);
+        if constexpr (kPingPong) {
+            u32x4 kb[U][KS], vb[U][RPL];
+            for (;;) {
+                load_tiles(kb, vb, t0 + kStride);
+                process(ka, va, t0);
+                t0 += kStride;
+                if (t0 >= t_end) break;
+                load_tiles(ka, va, t0 + kStride);
+                process(kb, vb, t0);
+                t0 += kStride;
+                if (t0 >= t_end) break;
+            }
+        } else {
+            for (;;) {
+                process(ka, va, t0);
+                t0 += kStride;
+                if (t0 >= t_end) break;
+                load_tiles(ka, va, t0);
+            }
+        }
     }
     // combine the lanes of a wave that hold the same columns
 #pragma unroll
