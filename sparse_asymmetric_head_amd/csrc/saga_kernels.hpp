@@ -159,9 +159,13 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 
     // Score, compare and stage one wave iteration (U tiles starting at t0).
     auto process = [&](const u32x4 (&kr)[U][KS], int64_t t0) {
+        // Whole iteration inside the chunk (every iteration but possibly the
+        // last): no per-element position checks.
+        const bool inside = t0 + 16 * U <= t_end;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tr = t0 + u * 16 + lq * 4;  // position of acc[0]
+            const int rem = inside ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - tr));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -176,12 +180,12 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                     const int j = j_lo + nt * 16 + ln;
                     if (j < j_hi) {
                         float *Ap = a.A + ((int64_t)b * a.h_q + j) * a.ld_a + tr;
-                        if (tr + 3 < t_end) {
+                        if (rem == 4) {
                             *(f32x4 *)Ap = f32x4{sc[0], sc[1], sc[2], sc[3]};
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                if (tr + r < t_end) Ap[r] = sc[r];
+                                if (r < rem) Ap[r] = sc[r];
                         }
                     }
                 } else {
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                     uint64_t m[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pr[r] = (tr + r < t_end) && (sc[r] >= tau_l[nt]);
+                        pr[r] = (r < rem) && (sc[r] >= tau_l[nt]);
                         m[r] = ballot(pr[r]);
                     }
                     if ((m[0] | m[1] | m[2] | m[3]) != 0ull) {

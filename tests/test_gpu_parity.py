@@ -341,3 +341,30 @@ def test_select_attend_halves_equal_decode_step():
     for a, b in zip(*outs):
         for u, v in zip(a, b):
             assert torch.equal(u, v)
+
+
+def test_attend_windows_and_long_records():
+    """More than 4096 survivors per row (the attend kernel's LDS window is
+    refilled) and segments far beyond the seven survivors a record's first 64
+    bytes hold: a stale tau of -inf selects every position."""
+    for (B, h_q, h_k, h_v, d, l_kv) in [(1, 8, 2, 4, 64, 10000), (2, 4, 1, 2, 128, 9001)]:
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=31 + d, device="cuda", planted=8)
+        Q, K, V = x["Q"][0], x["K"], x["V"]
+        tau = torch.full((B, h_q), float("-inf"), dtype=torch.float32, device="cuda")
+        O, cnt, ws = _step(Q, K, V, 16, tau, False)
+        assert (cnt == l_kv).all()
+        ref, _ = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v,
+                                   np.ones((B, h_q, l_kv), np.uint8))
+        assert rel_err(O.cpu().numpy().astype(np.float64), ref) <= OUT_RTOL
+        # a moderate stale threshold: about a third of each row survives
+        A = oracle.scores(bits(Q), bits(K), h_k)
+        t3 = np.quantile(A, 0.66, axis=-1).astype(np.float32)
+        tau = torch.from_numpy(t3).cuda()
+        O, cnt, ws = _step(Q, K, V, 16, tau, False)
+        m = read_mask(ws, (B, h_q, h_k, h_v, d, l_kv), 16)
+        for b in range(B):
+            for j in range(h_q):
+                check_selection(m[b, j], A[b, j], float(t3[b, j]), f"b={b} j={j}")
+        Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
+        assert np.array_equal(cg, cnt.cpu().numpy())
+        assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
