@@ -41,6 +41,9 @@ namespace saga {
 #ifndef SAGA_SELECT_U
 #define SAGA_SELECT_U 4  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
 #endif
+#ifndef SAGA_KT_LDS
+#define SAGA_KT_LDS 1  // k_select: contiguous key loads, moved into the MFMA layout through LDS
+#endif
 #ifndef SAGA_NT_LOADS
 #define SAGA_NT_LOADS 1  // k_select: non-temporal (streaming) loads of the key cache
 #endif
@@ -84,10 +87,14 @@ struct SelectArgs {
 // One workgroup = (batch b, key head g, chunk of cache positions).  Each wave
 // takes 16-row tiles of K, U tiles at a time, interleaved across the 4 waves.
 // MFMA 16x16x32 bf16: A operand = 16 K rows (M = position), B operand = the
-// group's query heads (N = head, padded to 16 per N-tile), K dim = d.  Lane
-// l loads d/2 contiguous bytes of row l%16 (bytes (l/16)*d/2 ...), and the
-// query operand uses the same permutation of the d axis, so each lane issues
-// 16-byte loads and the whole tile is a contiguous 16*d*2-byte block.
+// group's query heads (N = head, padded to 16 per N-tile), K dim = d.  At
+// k-step s lane l supplies row l%16, d-elements s*32 + (l/16)*8 .. +8, and
+// the query operand uses the same permutation of the d axis.  An operand
+// register thus holds 16 different rows in every 16-lane quarter, a load
+// pattern that costs about 10% of the read bandwidth, so the tiles are
+// loaded contiguously (lane l of a load takes 16 bytes at l*16 of a 1 KiB
+// run of rows) and moved into the operand layout through a wave-private,
+// XOR-swizzled LDS tile (conflict-free 16-byte writes and reads).
 // Output: lane l holds rows 4*(l/16)+r, r = 0..3, of query head l%16.
 // Survivors are ranked per (wave, head) with ballots (deterministic order:
 // tile, then row, then lane), staged in LDS and flushed to the wave's
@@ -107,7 +114,11 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     constexpr int KS = D / 32;             // MFMA k-steps per row
     constexpr int U = SAGA_SELECT_U * 64 / D;  // tiles per wave iteration
     constexpr int QW = D / 4;              // elements of a row per lane quarter
+    constexpr int CPR = D / 8;             // 16-byte columns per cache row
+    constexpr int RPL = 64 / CPR;          // rows per contiguous wave load
+    static_assert(KS * RPL == 16, "a tile is KS contiguous wave loads");
     __shared__ int2 st[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
+    __shared__ u32x4 kt[SAGA_KT_LDS ? kWaves : 1][SAGA_KT_LDS ? U * 16 * CPR : 1];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 15, lq = lane >> 4;
@@ -158,10 +169,34 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     };
 
     // Score, compare and stage one wave iteration (U tiles starting at t0).
-    auto process = [&](const u32x4 (&kr)[U][KS], int64_t t0) {
+    auto process = [&](const u32x4 (&kin)[U][KS], int64_t t0) {
         // Whole iteration inside the chunk (every iteration but possibly the
         // last): no per-element position checks.
         const bool inside = t0 + 16 * U <= t_end;
+#if SAGA_KT_LDS
+        // Row r, 16-byte column c of tile u sits at slot r*CPR + (c ^ (r & 7)):
+        // eight consecutive lanes of either access touch eight distinct bank
+        // groups.  The tile is private to the wave, whose LDS accesses run in
+        // order, so no barrier is needed.
+        u32x4 kr[U][KS];
+        u32x4 *w = kt[SAGA_KT_LDS ? wave : 0];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int r = s * RPL + lane / CPR, c = lane % CPR;
+                w[(u * 16 + r) * CPR + (c ^ (r & 7))] = kin[u][s];
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int c = kcol(lq, s) / 8;
+                kr[u][s] = w[(u * 16 + ln) * CPR + (c ^ (ln & 7))];
+            }
+#else
+        const u32x4 (&kr)[U][KS] = kin;
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tr = t0 + u * 16 + lq * 4;  // position of acc[0]
@@ -232,11 +267,20 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     auto load_tiles = [&](u32x4 (&kr)[U][KS], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+#if SAGA_KT_LDS
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {   // tile u is KS contiguous 1 KiB wave loads
+                int64_t row = t0 + u * 16 + s * RPL + lane / CPR;
+                row = row < last ? row : last;
+                kr[u][s] = ld_k(Kb + row * D + (lane % CPR) * 8);
+            }
+#else
             int64_t row = t0 + u * 16 + ln;
             row = row < last ? row : last;
             const uint16_t *kp = Kb + row * D;
 #pragma unroll
             for (int s = 0; s < KS; ++s) kr[u][s] = ld_k(kp + kcol(lq, s));
+#endif
         }
     };
     constexpr int64_t kStride = kWaves * 16 * U;
@@ -295,6 +339,16 @@ constexpr int kSegPerThread = kMaxSub / kAttendThreads;
 #define SAGA_ATTEND_SPLIT 4  // blocks per row, each owning d/SPLIT output columns
 #endif
 constexpr int kAttendSplit = SAGA_ATTEND_SPLIT;
+#ifndef SAGA_ATTEND_XCD
+#define SAGA_ATTEND_XCD 1  // the blocks of a row share an XCD (and its L2)
+#endif
+constexpr int kXcds = 8;  // workgroups are dealt round-robin over the 8 XCDs
+
+// Blocks launched for the attend kernel over `rows` rows.
+__host__ __device__ constexpr int64_t attend_grid(int64_t rows) {
+    return SAGA_ATTEND_XCD ? (rows + kXcds - 1) / kXcds * kXcds * kAttendSplit
+                           : rows * kAttendSplit;
+}
 
 // kAttendSplit blocks per row (b, j), block c owning output columns
 // [c*D/S, (c+1)*D/S).  Every block reads the row's records the same way:
@@ -326,7 +380,16 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     __shared__ float lred[kAttendWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#if SAGA_ATTEND_XCD
+    // Block x runs on XCD x % 8: the blocks of one row get ids that agree
+    // mod 8, so the row's records and V lines are fetched into one L2.
+    const int xk = blockIdx.x / kXcds;
+    const int csl = xk % kAttendSplit;
+    const int row = xk / kAttendSplit * kXcds + blockIdx.x % kXcds;
+    if (row >= a.B * a.h_q) return;  // whole block: padding of the last XCD round
+#else
     const int row = blockIdx.x / kAttendSplit, csl = blockIdx.x % kAttendSplit;
+#endif
     const int b = row / a.h_q, j = row % a.h_q;
     const int vh = (int)(((int64_t)j * a.h_v) / a.h_q);
 

@@ -368,3 +368,32 @@ def test_attend_windows_and_long_records():
         Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
         assert np.array_equal(cg, cnt.cpu().numpy())
         assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
+
+
+def test_attend_mixed_counts_and_many_segments():
+    """Rows of one launch with very different survivor counts (per-row stale
+    thresholds: a few to half of the row), and rows with more than 256
+    segments (one or two key heads over a long cache), match the oracle on
+    the GPU's selection."""
+    cases = [
+        # B, h_q, h_k, h_v, d, l_kv, per-row quantiles of the stale threshold
+        (2, 4, 1, 2, 64, 9001, [0.999, 0.66, 0.995, 0.5]),
+        (2, 6, 2, 3, 128, 20000, [0.9995, 0.7, 0.998]),
+        (1, 8, 1, 2, 64, 70001, [0.996]),
+    ]
+    for (B, h_q, h_k, h_v, d, l_kv, qs) in cases:
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=l_kv % 1009, device="cuda", planted=8)
+        Q, K, V = x["Q"][0], x["K"], x["V"]
+        A = oracle.scores(bits(Q), bits(K), h_k)
+        t = np.empty((B, h_q), np.float32)
+        for bb in range(B):
+            for j in range(h_q):
+                t[bb, j] = np.quantile(A[bb, j], qs[(bb * h_q + j) % len(qs)])
+        O, cnt, ws = _step(Q, K, V, 16, torch.from_numpy(t).cuda(), False)
+        m = read_mask(ws, (B, h_q, h_k, h_v, d, l_kv), 16)
+        for bb in range(B):
+            for j in range(h_q):
+                check_selection(m[bb, j], A[bb, j], float(t[bb, j]), f"b={bb} j={j}")
+        Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
+        assert np.array_equal(cg, cnt.cpu().numpy())
+        assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
