@@ -68,6 +68,52 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 // DPP controls (GFX9 encoding).
 constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+constexpr int kDppSwapPairs = 0xB1;  // quad_perm [1,0,3,2]: lane l reads lane l ^ 1
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]: lane l reads lane l ^ 2
+constexpr int kDppRowRor4 = 0x124, kDppRowRor8 = 0x128;  // rotations within 16-lane rows
+
+// v of the lane a DPP control names (every lane valid).
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(dppi<CTRL>(__float_as_int(v)));
+}
+
+// The 16-byte vector of lane l ^ 1.
+__device__ __forceinline__ u32x4 swap_pairs(u32x4 v) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)dppi<kDppSwapPairs>((int)v[i]);
+    return r;
+}
+
+// Maximum over the wave through DPP within 16-lane rows and four readlanes
+// (no LDS); the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+    auto mx = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+    v = mx(v, (uint32_t)dppi<kDppSwapPairs>((int)v));
+    v = mx(v, (uint32_t)dppi<kDppQuadXor2>((int)v));
+    v = mx(v, (uint32_t)dppi<kDppRowRor4>((int)v));
+    v = mx(v, (uint32_t)dppi<kDppRowRor8>((int)v));
+    const int x = (int)v;
+    return mx(mx((uint32_t)__builtin_amdgcn_readlane(x, 0), (uint32_t)__builtin_amdgcn_readlane(x, 16)),
+              mx((uint32_t)__builtin_amdgcn_readlane(x, 32), (uint32_t)__builtin_amdgcn_readlane(x, 48)));
+}
+
+// Sum of v over the lanes of its 16-lane row whose index agrees with its own
+// modulo P (P = 1, 2, 4 or 8); every lane receives its sum, in a fixed order.
+template <int P>
+__device__ __forceinline__ float row_sum_mod(float v) {
+    static_assert(P == 1 || P == 2 || P == 4 || P == 8, "row_sum_mod");
+    if constexpr (P == 1) v += dppf<kDppSwapPairs>(v);
+    if constexpr (P <= 2) v += dppf<kDppQuadXor2>(v);
+    if constexpr (P <= 4) v += dppf<kDppRowRor4>(v);
+    v += dppf<kDppRowRor8>(v);
+    return v;
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS traffic).

@@ -14,9 +14,10 @@
 //                        heads of the group, compare with tau, compact the
 //                        survivors through LDS into per-(row, segment)
 //                        records.                         [HBM-bound, hot]
-//   k_attend             per row: read the segment records, build the row's
-//                        survivor list in LDS, softmax weights, gather of the
-//                        survivors' V rows, fp32 accumulation, O.
+//   k_attend             per row (a few column blocks): read the segment
+//                        records, wave-local survivor lists in LDS, softmax
+//                        weights, gather of the survivors' V rows, fp32
+//                        accumulation, O.
 // Refresh (every R steps) instead runs:
 //   k_select<.., true>   same score pass, writes fp32 A
 //   k_hist / k_select1 / k_collect / k_select_final   exact radix select
@@ -27,8 +28,8 @@
 // wave's share of a block's cache positions -- are stored as int32 words
 //   [0] count, [1] order key of their largest score, [2+2i] position t_i,
 //   [3+2i] bits of score s_i,
-// padded to a multiple of 16 words, so that the first 64 bytes hold the
-// count and the first seven survivors.
+// padded to a multiple of 16 words (at least 32), so that the first 128
+// bytes hold the count, the key and the first fifteen survivors.
 #pragma once
 
 #include "saga_device.hpp"
@@ -54,10 +55,12 @@ constexpr int kCapW = 32;     // LDS staging slots per (wave, query head)
 constexpr int kMaxSub = 1024; // max segments per row
 constexpr int kHistBins = 2048;
 constexpr int kHistBlockMax = 8192;  // positions per histogram/collect block
-constexpr int kRecHead = 7;   // survivors held in a record's first 64 bytes
+constexpr int kRecHead = 15;  // survivors held in a record's first 128 bytes
 
 // Words per segment record for a segment capacity of cap survivors.
-__host__ __device__ constexpr int64_t seg_words(int64_t cap) { return (2 + 2 * cap + 15) / 16 * 16; }
+__host__ __device__ constexpr int64_t seg_words(int64_t cap) {
+    return (2 + 2 * cap + 15) / 16 * 16 < 32 ? 32 : (2 + 2 * cap + 15) / 16 * 16;
+}
 
 // ------------------------------------------------------------------ select
 
@@ -333,8 +336,6 @@ struct AttendArgs {
 
 constexpr int kAttendWaves = 8;
 constexpr int kAttendThreads = kAttendWaves * kWave;
-constexpr int kAttendWin = 4096;  // survivors staged in LDS per window
-constexpr int kSegPerThread = kMaxSub / kAttendThreads;
 #ifndef SAGA_ATTEND_SPLIT
 #define SAGA_ATTEND_SPLIT 4  // blocks per row, each owning d/SPLIT output columns
 #endif
@@ -350,39 +351,41 @@ __host__ __device__ constexpr int64_t attend_grid(int64_t rows) {
                            : rows * kAttendSplit;
 }
 
+constexpr int kWaveWin = 256;  // survivors staged per wave and window
+
 // kAttendSplit blocks per row (b, j), block c owning output columns
-// [c*D/S, (c+1)*D/S).  Every block reads the row's records the same way:
-// thread i owns segments 2i and 2i+1 and reads the first 64 bytes of both in
-// one go (count, max key and up to seven survivors each); an exclusive scan
-// of the counts places every survivor in the row's list, built in LDS
-// (survivors past the seventh of a segment come from the rest of the
-// record); M = the row maximum from the record headers.  Groups of
-// D/(8*S) lanes then take one survivor per round: weight exp(s - M), 16-byte
-// loads of the block's columns of its V row, fp32 accumulation.  All blocks
-// of a row see the same list in the same order, so the weight sums agree and
-// the result is deterministic.  Lists longer than kAttendWin go in windows.
+// [c*D/S, (c+1)*D/S); every block of a row reads the row's records the same
+// way and gathers the same survivors in the same order, so the blocks agree
+// on the weight sum and the result is deterministic.
+// The two lanes of pair i of a wave own segment i of the pass
+// (256 segments per pass over the block): each loads one half of the
+// record's first 128 bytes and they swap halves with DPP, so both hold the
+// count, the max key and the first fifteen survivors.  A DPP scan of the
+// counts places the wave's survivors in a wave-private LDS list (entries past
+// the fifteenth of a segment are loaded by the whole wave, 64 per round);
+// groups of d/32 lanes then gather one survivor each per round, so the
+// loads stay dense.  Weights use the wave's running maximum (rescaled when a
+// later pass raises it); sums over lanes run through DPP; the one block
+// barrier comes at the end, where a thread per column rescales the eight
+// waves' partials to the row maximum and adds them in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     constexpr int DC = D / kAttendSplit;        // columns of this block
     constexpr int LPE = DC / 8;                 // lanes per survivor (16 B each)
-    constexpr int EPW = kWave / LPE;            // survivors per wave round
-    constexpr int EPB = kAttendThreads / LPE;   // survivors per block round
+    constexpr int EPI = kWave / LPE;            // survivors per wave round
     constexpr int UN = 4;
-    constexpr int SPT = kSegPerThread;
-    constexpr int NPART = kAttendThreads / DC;  // partial sums per column
-    static_assert(DC % 8 == 0 && LPE >= 1 && kWave % LPE == 0, "attend column split");
-    __shared__ int lt[kAttendWin];
-    __shared__ float ls[kAttendWin];
-    __shared__ int ired[kAttendWaves];
-    __shared__ uint32_t kred[kAttendWaves];
-    __shared__ float red[kAttendWaves * EPW][DC];
-    __shared__ float part[NPART][DC];
-    __shared__ float lred[kAttendWaves];
+    constexpr int SEGP = kAttendThreads / 2;    // segments per pass
+    static_assert(LPE >= 1 && LPE <= 8 && DC % 8 == 0, "attend column split");
+    static_assert(seg_words(1) >= 32, "128-byte record heads");
+    __shared__ int wlt[kAttendWaves][kWaveWin];
+    __shared__ float wls[kAttendWaves][kWaveWin];
+    __shared__ float wpart[kAttendWaves * 4][DC];
+    __shared__ float wlp[kAttendWaves * 4];
+    __shared__ float wmx[kAttendWaves];
+    __shared__ int wcnt[kAttendWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #if SAGA_ATTEND_XCD
-    // Block x runs on XCD x % 8: the blocks of one row get ids that agree
-    // mod 8, so the row's records and V lines are fetched into one L2.
     const int xk = blockIdx.x / kXcds;
     const int csl = xk % kAttendSplit;
     const int row = xk / kAttendSplit * kXcds + blockIdx.x % kXcds;
@@ -392,129 +395,136 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
 #endif
     const int b = row / a.h_q, j = row % a.h_q;
     const int vh = (int)(((int64_t)j * a.h_v) / a.h_q);
-
-    u32x4 rec[SPT][4];
-    int cnt[SPT];
-    uint32_t mk = 0u;
     const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-        const int s = tid * SPT + i;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            rec[i][q] = s < a.n_sub ? ld16(rb + s * a.seg_w + q * 4) : u32x4{0u, 0u, 0u, 0u};
-    }
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-        cnt[i] = (int)rec[i][0][0];
-        mk = cnt[i] > 0 && rec[i][0][1] > mk ? rec[i][0][1] : mk;
-        mine += cnt[i];
-    }
-    mk = wave_max_u32(mk);
-    if (lane == 0) kred[wave] = mk;
-    int total;
-    const int pre = block_excl_scan<kAttendWaves>(mine, ired, &total);  // barriers
-#pragma unroll
-    for (int q = 0; q < kAttendWaves; ++q) mk = mk > kred[q] ? mk : kred[q];
-    const float M = fkey_inv(mk);
-
-    const int e_in = tid / LPE, cl = tid % LPE;
+    const int h = lane & 1;
+    const int e_in = lane / LPE, cl = lane % LPE;
     const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.l_kv * D + csl * DC + cl * 8;
+    int *lt = wlt[wave];
+    float *ls = wls[wave];
+
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    float lsum = 0.f;
-    for (int w0 = 0; w0 < total; w0 += kAttendWin) {
-        const int w1 = min(total, w0 + kAttendWin);
-        // place this thread's survivors that fall in [w0, w1)
-        int e = pre;
+    float l = 0.f, m_run = -INFINITY;
+    int cnt_w = 0;
+    for (int p0 = 0; p0 < a.n_sub; p0 += SEGP) {
+        const int sg = p0 + (tid >> 1);
+        const bool has = sg < a.n_sub;
+        const int32_t *rs = rb + (int64_t)sg * a.seg_w;
+        u32x4 own[4], hd[8];
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) {
-            const int n_i = cnt[i];
-            if (e < w1 && e + n_i > w0) {
+        for (int q = 0; q < 4; ++q) own[q] = has ? ld16(rs + h * 16 + q * 4) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int k = 0; k < kRecHead; ++k) {
-                    const int q = (2 + 2 * k) / 4, c = (2 + 2 * k) % 4;
-                    const int pos = e + k;
-                    if (k < n_i && pos >= w0 && pos < w1) {
-                        lt[pos - w0] = (int)rec[i][q][c];
-                        ls[pos - w0] = __uint_as_float(rec[i][q][c + 1]);
-                    }
-                }
-                if (n_i > kRecHead) {
-                    const int s = tid * SPT + i;
-                    const int2 *pr = (const int2 *)(rb + s * a.seg_w) + 1;
-                    const int k0 = max(kRecHead, w0 - e), k1 = min(n_i, w1 - e);
-                    for (int k = k0; k < k1; k += 4) {
-                        int2 v[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) v[u] = k + u < k1 ? pr[k + u] : int2{0, 0};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (k + u < k1) {
-                                lt[e + k + u - w0] = v[u].x;
-                                ls[e + k + u - w0] = __int_as_float(v[u].y);
-                            }
-                    }
-                }
-            }
-            e += n_i;
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 oth = swap_pairs(own[q]);
+            hd[q] = h ? oth : own[q];
+            hd[4 + q] = h ? own[q] : oth;
         }
-        __syncthreads();
-        const int nw = w1 - w0;
-        for (int e0 = 0; e0 < nw; e0 += EPB * UN) {
-            int tt[UN];
-            float pp[UN];
-            u32x4 vv[UN];
+        const int n = (int)hd[0][0];
+        const uint32_t mk = wave_max_u32_dpp(n > 0 ? hd[0][1] : 0u);
+        const int incl = wave_incl_scan(h == 0 ? n : 0);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        if (tot == 0) continue;  // wave-uniform
+        cnt_w += tot;
+        const int ex = incl - n;  // the pair's first slot in the wave's sequence
+        const float m_new = fmaxf(m_run, fkey_inv(mk));
+        const float sc = expf(m_run - m_new);  // 0 while m_run is -inf
 #pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const int ei = e0 + u * EPB + e_in;
-                tt[u] = ei < nw ? lt[ei] : -1;
-                pp[u] = ei < nw ? ls[ei] : 0.f;
-            }
+        for (int i = 0; i < 8; ++i) acc[i] *= sc;
+        l *= sc;
+        m_run = m_new;
+        const uint64_t big = ballot(h == 0 && n > kRecHead);
+        for (int w0 = 0; w0 < tot; w0 += kWaveWin) {
+            const int w1 = min(tot, w0 + kWaveWin);
+            // survivors k < fifteen from the registers: lane h takes k = h mod 2
 #pragma unroll
-            for (int u = 0; u < UN; ++u)
-                vv[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int u = 0; u < UN; ++u) {
-                const float p = tt[u] >= 0 ? expf(pp[u] - M) : 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += p * bf_lo(vv[u][i]);
-                    acc[2 * i + 1] += p * bf_hi(vv[u][i]);
+            for (int k = 0; k < kRecHead; ++k) {
+                const int e = ex + k;
+                if ((k & 1) == h && k < n && e >= w0 && e < w1) {
+                    lt[e - w0] = (int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4];
+                    ls[e - w0] = __uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]);
                 }
-                lsum += (cl == 0) ? p : 0.f;
             }
+            // the rest of long segments, 64 entries per wave round
+            for (uint64_t bm = big; bm != 0ull; bm &= bm - 1ull) {
+                const int src = __ffsll((unsigned long long)bm) - 1;
+                const int sn = __builtin_amdgcn_readlane(n, src);
+                const int sx = __builtin_amdgcn_readlane(ex, src);
+                const int ssg = __builtin_amdgcn_readlane(sg, src);
+                const int2 *pr = (const int2 *)(rb + (int64_t)ssg * a.seg_w) + 1;
+                const int k0 = max(kRecHead, w0 - sx), k1 = min(sn, w1 - sx);
+                for (int k = k0 + lane; k < k1; k += kWave) {
+                    const int2 v = pr[k];
+                    lt[sx + k - w0] = v.x;
+                    ls[sx + k - w0] = __int_as_float(v.y);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const int W = w1 - w0;
+            for (int e0 = 0; e0 < W; e0 += EPI * UN) {
+                int tt[UN];
+                float pp[UN];
+                u32x4 vv[UN];
+#pragma unroll
+                for (int u = 0; u < UN; ++u) {
+                    const int ei = e0 + u * EPI + e_in;
+                    tt[u] = ei < W ? lt[ei] : -1;
+                    pp[u] = ei < W ? ls[ei] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < UN; ++u)
+                    vv[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int u = 0; u < UN; ++u) {
+                    const float p = tt[u] >= 0 ? expf(pp[u] - m_run) : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] += p * bf_lo(vv[u][i]);
+                        acc[2 * i + 1] += p * bf_hi(vv[u][i]);
+                    }
+                    l += (cl == 0) ? p : 0.f;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // list reused by the next window
         }
-        __syncthreads();
     }
-    // sum over the block's survivor groups in a fixed order: every lane
-    // parks its 8 column sums, NPART threads per column add fixed subsets,
-    // then one thread per column adds the NPART partials.
+    // lanes of one column group: sum within each 16-lane row, then the
+    // (wave, row) partials go to LDS
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red[e_in][cl * 8 + i] = acc[i];
-    lsum = wave_sum(lsum);
-    if (lane == 0) lred[wave] = lsum;
-    __syncthreads();
-    {
-        const int c = tid % DC, q = tid / DC;
-        constexpr int GPP = kAttendWaves * EPW / NPART;  // groups per partial
-        float sacc = 0.f;
+    for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<LPE>(acc[i]);
+    l = row_sum_mod<LPE>(l);
+    const int wr = wave * 4 + (lane >> 4);
+    if ((lane & 15) < LPE) {
 #pragma unroll
-        for (int g = 0; g < GPP; ++g) sacc += red[q * GPP + g][c];
-        part[q][c] = sacc;
+        for (int i = 0; i < 8; ++i) wpart[wr][cl * 8 + i] = acc[i];
+        if (cl == 0) wlp[wr] = l;
+    }
+    if (lane == 0) {
+        wmx[wave] = m_run;
+        wcnt[wave] = cnt_w;
     }
     __syncthreads();
     if (tid < DC) {
+        float M = -INFINITY;
+        int total = 0;
+#pragma unroll
+        for (int q = 0; q < kAttendWaves; ++q) {
+            M = fmaxf(M, wmx[q]);
+            total += wcnt[q];
+        }
         float so = 0.f, sl = 0.f;
 #pragma unroll
-        for (int q = 0; q < NPART; ++q) so += part[q][tid];
+        for (int q = 0; q < kAttendWaves; ++q) {
+            const float f = wcnt[q] > 0 ? expf(wmx[q] - M) : 0.f;
 #pragma unroll
-        for (int q = 0; q < kAttendWaves; ++q) sl += lred[q];
+            for (int r = 0; r < 4; ++r) {
+                so += f * wpart[q * 4 + r][tid];
+                sl += f * wlp[q * 4 + r];
+            }
+        }
         a.O[(int64_t)row * D + csl * DC + tid] = sl > 0.f ? so / sl : 0.f;
+        if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
     }
-    if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
 }
 
 // ------------------------------------------------------------------ refresh
