@@ -345,8 +345,9 @@ def test_select_attend_halves_equal_decode_step():
 
 def test_attend_windows_and_long_records():
     """Far more than 256 survivors per wave (the attend kernel's wave-local
-    LDS window of 256 entries is refilled many times) and segments far beyond the fifteen survivors a record's first
-    128 bytes hold: a stale tau of -inf selects every position."""
+    LDS window of 256 entries is refilled many times) and segments far
+    beyond the fifteen survivors a record's first 128 bytes hold: a stale
+    tau of -inf selects every position."""
     for (B, h_q, h_k, h_v, d, l_kv) in [(1, 8, 2, 4, 64, 10000), (2, 4, 1, 2, 128, 9001)]:
         x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=31 + d, device="cuda", planted=8)
         Q, K, V = x["Q"][0], x["K"], x["V"]
