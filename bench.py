@@ -7,7 +7,11 @@ the score/compare/compact pass over the key cache (with the exact threshold
 refresh on every R-th step) and the sparse softmax + gather-PV.  Inputs are
 seeded synthetic tensors already resident in HBM.  The dense full-attention
 GQA kernel runs on its own cache in the same process, and the fp64 CPU oracle
-is timed on a bounded sample on the host cores.
+is timed on a bounded sample on the host cores.  Besides the mean over the
+timed steps (`value`), per-step p10/p50/p90 and the medians of refresh and
+non-refresh steps are reported (`per_step_us`), and the dominant kernel's rate
+is given against both the 8 TB/s spec and the library's plain streaming-read
+probe over the same caches (`roofline.probe_read_gbps`, `frac_of_probe`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
@@ -217,10 +221,33 @@ def main() -> int:
         gpu_ms = ev0.elapsed_time(ev1)
         wall_ms = (t_wall1 - t_wall0) * 1e3
         sel_counts.append(cnts.float().mean().item())
+        # A second pass over the same steps with one event between consecutive
+        # steps gives the per-step distribution (refresh and non-refresh steps
+        # apart); the events cost a little, so `value` comes from the pass above.
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record(stream)
+        for i, t in enumerate(range(args.warmup, args.warmup + args.steps)):
+            step(t)
+            evs[i + 1].record(stream)
+        stream.synchronize()
+        step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
     ms_per_step = max(gpu_ms, wall_ms) / args.steps
     us_per_step = ms_per_step * 1e3
+    ref_us = [u for i, u in enumerate(step_us) if (args.warmup + i) % R == 0]
+    non_us = [u for i, u in enumerate(step_us) if (args.warmup + i) % R != 0]
+
+    def pct(xs, q):
+        xs = sorted(xs)
+        return xs[min(len(xs) - 1, max(0, round(q * (len(xs) - 1))))] if xs else None
+
+    per_step = {"p10": pct(step_us, 0.1), "p50": pct(step_us, 0.5), "p90": pct(step_us, 0.9),
+                "non_refresh_p50": pct(non_us, 0.5),
+                "refresh_p50": pct(ref_us, 0.5), "refresh_steps": len(ref_us)}
+    per_step = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in per_step.items()}
     log(f"timed {args.steps} steps: {us_per_step:.1f} us/step (events {gpu_ms:.3f} ms, "
-        f"wall {wall_ms:.3f} ms)")
+        f"wall {wall_ms:.3f} ms); per step p10/p50/p90 {per_step['p10']}/{per_step['p50']}/"
+        f"{per_step['p90']} us, non-refresh p50 {per_step['non_refresh_p50']}, refresh p50 "
+        f"{per_step['refresh_p50']}")
 
     # ------------------------------------------------------------ kernel timing pass
     # The dominant kernel (the streaming score/compare/compact pass) timed
@@ -258,6 +285,36 @@ def main() -> int:
         stream.synchronize()
     sel_us = k0.elapsed_time(k1) * 1e3 / (reps * L * inner)
     mean_count = sum(sel_counts) / len(sel_counts)
+
+    # ------------------------------------------------------------ achievable read
+    # The library's plain streaming-read probe over the same key caches, same
+    # protocol: the achievable-read reference for the streaming kernel.
+    sink = torch.zeros(saga.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+
+        def probe_pass():
+            for _ in range(inner):
+                for l in range(L):
+                    saga.saga_read_probe(Ks[l], sink, stream)
+
+        probe_pass()
+        stream.synchronize()
+        pg = None
+        if not args.no_graph:
+            pg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(pg, stream=stream):
+                probe_pass()
+        run_probe = pg.replay if pg is not None else probe_pass
+        run_probe()
+        stream.synchronize()
+        k0.record(stream)
+        for _ in range(reps):
+            run_probe()
+        k1.record(stream)
+        stream.synchronize()
+    probe_us = k0.elapsed_time(k1) * 1e3 / (reps * L * inner)
+    probe_gbps = B * h_k * l_kv * d * 2 / (probe_us * 1e-6) / 1e9
+    log(f"read probe over the same caches: {probe_us:.2f} us/launch -> {probe_gbps:.0f} GB/s")
 
     k_bytes = B * h_k * l_kv * d * 2
     q_bytes = B * h_q * d * 2
@@ -368,7 +425,10 @@ def main() -> int:
                      "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                      "traffic": measured_traffic(), "traffic_unit": "HBM bytes per launch",
-                     "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg},
+                     "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg,
+                     "probe_read_gbps": round(probe_gbps, 1),
+                     "frac_of_probe": round(achieved / 1e9 / probe_gbps, 4)},
+        "per_step_us": per_step,
         "dense_gqa": dense,
         "cpu_baseline": cpu,
     }

@@ -155,6 +155,19 @@ int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv,
 int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k, int h_v, int d,
                         int64_t l_kv, int64_t N, uint8_t *mask, void *hip_stream);
 
+/*
+ * Measurement utility, not part of the method: read the `bytes` bytes at buf
+ * once with the streaming kernels' launch shape (256 workgroups of 4 waves,
+ * 16-byte non-temporal loads, eight in flight per lane) and store, for each
+ * workgroup i, the XOR of the 32-bit words it read in sink[i].  Its rate is
+ * the achievable-read reference the streaming kernels are compared with.
+ * buf: device pointer, 16-byte aligned, bytes a positive multiple of 16;
+ * sink: device array of SAGA_PROBE_SINK_WORDS words (entries past the
+ * workgroups used are left untouched).  Enqueued on hip_stream.
+ */
+#define SAGA_PROBE_SINK_WORDS 256
+int saga_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -407,4 +407,16 @@ int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k
     return launch_status();
 }
 
+int saga_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *hip_stream) {
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes <= 0 || bytes % 16 != 0)
+        return SAGA_ERR_INVALID_ARG;
+    const int64_t n16 = bytes / 16;
+    static_assert(kTargetSelectBlocks <= SAGA_PROBE_SINK_WORDS, "probe sink");
+    const int64_t per = ceil_div(n16, kTargetSelectBlocks);
+    const int blocks = (int)ceil_div(n16, per);
+    hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(kThreads), 0, (hipStream_t)hip_stream,
+                       (const u32x4 *)buf, n16, per, sink);
+    return launch_status();
+}
+
 }  // extern "C"

@@ -752,6 +752,41 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     if (lane == 0) rec[0] = int2{cnt, (int)mk};
 }
 
+// ------------------------------------------------------------------ read probe
+
+// Plain streaming read (the reference rate for the streaming kernels): block
+// i reads a contiguous range, each lane eight 16-byte loads per round that
+// are kThreads * 16 bytes apart, and folds the words it read with XOR.
+// Positions past the range are clamped to its last item and masked, so the
+// loads carry no branches.
+__global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4 *p, int64_t n16, int64_t per,
+                                                          uint32_t *sink) {
+    __shared__ uint32_t red[kWaves];
+    const int64_t beg = (int64_t)blockIdx.x * per;
+    const int64_t end = min(n16, beg + per);
+    uint32_t acc = 0u;
+    for (int64_t i = beg + threadIdx.x; i < end; i += kThreads * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t k = i + (int64_t)u * kThreads;
+            v[u] = ld16_stream(p + (k < end ? k : end - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (i + (int64_t)u * kThreads < end) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0u;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) r ^= red[w];
+        sink[blockIdx.x] = r;
+    }
+}
+
 // ------------------------------------------------------------------ dense
 
 struct DenseArgs {

@@ -26,8 +26,9 @@ EXPORTS = (
     "saga_status_string", "saga_version", "saga_workspace_bytes", "saga_dense_workspace_bytes",
     "saga_workspace_init", "saga_refresh_threshold", "saga_decode_step",
     "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
-    "saga_attend",
+    "saga_attend", "saga_read_probe",
 )
+PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
 
 class SagaError(RuntimeError):
@@ -89,6 +90,8 @@ def lib(path: str | None = None):
     L.saga_workspace_layout.restype = i32
     L.saga_selection_mask.argtypes = [vp, sz, i32, i32, i32, i32, i32, i64, i64, vp, vp]
     L.saga_selection_mask.restype = i32
+    L.saga_read_probe.argtypes = [vp, i64, vp, vp]
+    L.saga_read_probe.restype = i32
     if path is None:
         _lib = L
     return L
@@ -213,6 +216,14 @@ def saga_selection_mask(ws, B, h_q, h_k, h_v, d, l_kv, N, mask, stream=None) -> 
     _check(lib().saga_selection_mask(_ptr(ws), ws.numel(), B, h_q, h_k, h_v, d, l_kv, int(N),
                                      _ptr(mask), _stream(stream)),
            "saga_selection_mask")
+
+
+def saga_read_probe(buf, sink, stream=None) -> None:
+    """Measurement utility: stream-read buf once (the achievable-read reference);
+    sink (uint32/int32, PROBE_SINK_WORDS entries) receives per-workgroup XOR folds."""
+    assert sink.numel() >= PROBE_SINK_WORDS and sink.element_size() == 4
+    _check(lib().saga_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                 _stream(stream)), "saga_read_probe")
 
 
 # ----------------------------------------------------------------- conveniences

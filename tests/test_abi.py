@@ -143,6 +143,12 @@ def test_entry_points_validate_before_launch(L):
         saga.SAGA_ERR_INVALID_ARG
     assert L.saga_selection_mask(fake, need, B, h_q, h_k, h_v, d, l_kv, N, None, None) == \
         saga.SAGA_ERR_INVALID_ARG
+    rp = L.saga_read_probe
+    assert rp(None, 1024, fake, None) == saga.SAGA_ERR_INVALID_ARG
+    assert rp(fake, 1024, None, None) == saga.SAGA_ERR_INVALID_ARG
+    assert rp(mis, 1024, fake, None) == saga.SAGA_ERR_INVALID_ARG
+    assert rp(fake, 1000, fake, None) == saga.SAGA_ERR_INVALID_ARG   # not a multiple of 16
+    assert rp(fake, 0, fake, None) == saga.SAGA_ERR_INVALID_ARG
 
 
 def test_binding_refuses_without_library(tmp_path):

@@ -398,3 +398,19 @@ def test_attend_mixed_counts_and_many_segments():
         Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
         assert np.array_equal(cg, cnt.cpu().numpy())
         assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
+
+
+def test_read_probe_checksum():
+    """The measurement probe reads every 16-byte item of its buffer exactly
+    once: the XOR of its per-workgroup folds equals the XOR of all words."""
+    g = torch.Generator().manual_seed(5)
+    for nbytes in (16, 4096 + 48, (64 << 20) + 16 * 7):
+        words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g, dtype=torch.int64)
+        host = words.to(torch.int32)
+        buf = host.cuda()
+        sink = torch.zeros(saga.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        saga.saga_read_probe(buf, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+        assert got == want, nbytes
