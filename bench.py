@@ -4,7 +4,8 @@ HBM bandwidth at 128K context on one MI355X.
 
 A step is one decode token through all layers of the workload: for each layer,
 the score/compare/compact pass over the key cache (with the exact threshold
-refresh on every R-th step) and the sparse softmax + gather-PV.  Inputs are
+refresh on every R-th step, found from the previous refresh's survivors as a
+pivot) and the sparse softmax + gather-PV.  Inputs are
 seeded synthetic tensors already resident in HBM.  The dense full-attention
 GQA kernel runs on its own cache in the same process, and the fp64 CPU oracle
 is timed on a bounded sample on the host cores.  Besides the mean over the
@@ -172,27 +173,31 @@ def main() -> int:
 
     ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N), dev)
     taus = torch.zeros(L, B, h_q, dtype=torch.float32, device=dev)
+    pivots = torch.full((L, B, h_q, N), -1, dtype=torch.int32, device=dev)
     Os = torch.empty(L, B, h_q, d, dtype=torch.float32, device=dev)
     cnts = torch.empty(L, B, h_q, dtype=torch.int32, device=dev)
     qbuf = torch.empty(L, B, h_q, d, dtype=torch.bfloat16, device=dev)
 
-    def layer_pass(refresh: bool):
+    # refresh modes of saga_decode_step_pivot: 0 compare with tau, 1 full
+    # exact refresh (records the pivot), 2 exact refresh from the pivot
+    def layer_pass(mode: int):
         for l in range(L):
-            saga.saga_decode_step(qbuf[l], Ks[l], Vs[l], N, taus[l], refresh, Os[l], cnts[l], ws)
+            saga.saga_decode_step_pivot(qbuf[l], Ks[l], Vs[l], N, taus[l], pivots[l], mode,
+                                        Os[l], cnts[l], ws)
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         qbuf.copy_(Qall[0])
-        layer_pass(True)  # eager first call: loads the kernels
-        layer_pass(False)
+        layer_pass(1)  # eager first call: loads the kernels; first refresh of every layer
+        layer_pass(0)
     stream.synchronize()
     graphs = {}
     if not args.no_graph:
         for refresh in (True, False):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                layer_pass(refresh)
+                layer_pass(2 if refresh else 0)
             graphs[refresh] = g
         log("graphs captured")
 
@@ -202,7 +207,7 @@ def main() -> int:
         if graphs:
             graphs[refresh].replay()
         else:
-            layer_pass(refresh)
+            layer_pass(2 if refresh else 0)
 
     sel_counts = []
     with torch.cuda.stream(stream):

@@ -118,6 +118,29 @@ int saga_attend(const void *V, int B, int h_q, int h_k, int h_v, int d, int64_t 
                 float *O, int32_t *counts, void *ws, size_t ws_bytes, void *hip_stream);
 
 /*
+ * saga_decode_step with a cheaper exact refresh.  pivot: caller-owned int32
+ * device array [B*h_q][N], the per-row state of this refresh scheme (like
+ * tau, one per layer / sequence), written by every refresh.
+ *   refresh 0: compare with tau, as saga_decode_step; pivot is not touched.
+ *   refresh 1: exact refresh as saga_decode_step, then N positions of each
+ *              row's survivors are recorded in pivot (increasing).
+ *   refresh 2: exact refresh from pivot: the least current score over the
+ *              row's N recorded positions, less a rounding margin, is a lower
+ *              bound on the new N-th largest score; one compare pass lists
+ *              every score at or above it and the exact N-th largest is
+ *              selected among those (same tau as refresh 1, bit for bit);
+ *              the new survivors' positions are recorded again.  A pivot row
+ *              that is not N strictly increasing positions inside the cache
+ *              gives the bound -inf: still exact, but it lists every score.
+ * The threshold refresh is defined in Methodology > Atop-N Attention (items
+ * 1-2, eq. 6) of the pages; this entry point only changes how it is found.
+ */
+int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                           int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
+                           int refresh, float *O, int32_t *counts, void *ws, size_t ws_bytes,
+                           void *hip_stream);
+
+/*
  * Dense full-attention GQA decode, the in-run baseline (eqs. 2-4):
  *   O[b][j] := softmax(q K_g^T / sqrt(d)) V_g,  g = floor(j*h_kv/h_q),
  * with K, V both [B][h_kv][l_kv][d] bf16; fp32 output.
@@ -134,13 +157,15 @@ typedef struct saga_ws_layout {
     int64_t scores_ld;     /* row stride of the scores, in elements (>= l_kv) */
     size_t seg_off;        /* int32 [B*h_q][n_seg][seg_words]: survivor records, each
                               { count, order key of the max score, then (t, score bits)
-                              pairs }; segment k of a row covers cache positions
-                              [c*chunk_len + w*seg_cap, ... + seg_cap), c = k/4, w = k%4 */
+                              pairs }; segment k = 4c + w of a row lists positions of
+                              chunk c from the groups of seg_group rows w, w+4, w+8, ...
+                              of that chunk (seg_cap positions in all) */
     int64_t seg_words;     /* int32 words per record (multiple of 16) */
     int64_t chunk_len;     /* cache positions per streaming block */
     int64_t n_chunk;       /* blocks per key-head row: ceil(l_kv / chunk_len) */
     int64_t n_seg;         /* segments per row (n_chunk * 4) */
     int64_t seg_cap;       /* positions covered by one segment (chunk_len / 4) */
+    int64_t seg_group;     /* rows per group of a segment (16 * 4 * 64 / d) */
 } saga_ws_layout;
 
 /* Fill *out for this shape.  Returns SAGA_OK or a negative status. */
@@ -148,9 +173,10 @@ int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv,
                           saga_ws_layout *out);
 
 /*
- * Expand the survivor segments of the last saga_decode_step on this
- * workspace into a byte mask: mask[b][j][t] = 1 if t was in S[b][j], else 0.
- * mask is a device pointer of B*h_q*l_kv bytes.  Enqueued on hip_stream.
+ * Expand the survivor segments of the last saga_decode_step (or
+ * saga_decode_step_pivot) on this workspace into a byte mask: mask[b][j][t]
+ * = 1 if t was in S[b][j], else 0.  mask is a device pointer of B*h_q*l_kv
+ * bytes.  Enqueued on hip_stream.
  */
 int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k, int h_v, int d,
                         int64_t l_kv, int64_t N, uint8_t *mask, void *hip_stream);

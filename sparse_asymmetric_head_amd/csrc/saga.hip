@@ -40,7 +40,8 @@ struct Plan {
     int64_t ld_a;
     int hist_bpr;
     // byte offsets into the workspace
-    size_t off_hist, off_state, counters_end;
+    size_t off_hist, off_state, off_pi, counters_end;
+    int64_t grp;  // rows per k_select wave iteration (16 * U): the record order's groups
     int64_t seg_w;
     size_t off_seg, off_scores, off_cand;
     size_t total;
@@ -76,6 +77,7 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->n_sub = p->n_chunk * kWaves;
     p->sub_cap = cl / kWaves;
+    p->grp = 1024 * SAGA_SELECT_U / d;
     p->ld_a = ceil_div(l_kv, 64) * 64;
     p->hist_bpr = (int)ceil_div(l_kv, kHistBlock);
 
@@ -85,6 +87,8 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     o = align_up(o + rows * kHistBins * sizeof(uint32_t));
     p->off_state = o;
     o = align_up(o + rows * 4 * sizeof(uint32_t));
+    p->off_pi = o;   // fp32 [rows]: lower bounds of a refresh from a pivot
+    o = align_up(o + rows * sizeof(float));
     p->counters_end = o;
     p->seg_w = seg_words(p->sub_cap);
     p->off_seg = o;
@@ -215,7 +219,7 @@ int run_select(const Plan &p, const void *Q, const void *K, float *tau, int refr
         if (st != SAGA_OK) return st;
         CompactArgs ca;
         ca.A = (const float *)(w + p.off_scores);
-        ca.ld_a = p.ld_a, ca.l_kv = p.l_kv, ca.chunk_len = p.chunk_len;
+        ca.ld_a = p.ld_a, ca.l_kv = p.l_kv, ca.chunk_len = p.chunk_len, ca.grp = p.grp;
         ca.n_chunk = p.n_chunk;
         ca.tau = tau;
         ca.seg = (int32_t *)(w + p.off_seg);
@@ -227,6 +231,39 @@ int run_select(const Plan &p, const void *Q, const void *K, float *tau, int refr
         SelectArgs sa = select_args(p, Q, K, tau, w);
         launch_select<false>(p, sa, s);
     }
+    return launch_status();
+}
+
+// k_refine over the current records: the exact N-th largest listed score
+// -> tau (and the records' threshold); N positions of the survivors -> pivot.
+void launch_refine(const Plan &p, float *tau, int32_t *pivot, char *w, hipStream_t s) {
+    RefineArgs r;
+    r.seg = (int32_t *)(w + p.off_seg);
+    r.n_sub = p.n_sub;
+    r.seg_w = p.seg_w, r.sub_cap = p.sub_cap, r.N = p.N;
+    r.tau = tau;
+    r.pivot = pivot;
+    hipLaunchKernelGGL(k_refine, dim3(p.rows), dim3(kThreads), 0, s, r);
+}
+
+// Exact refresh from the pivot positions: lower bound per row, a compare
+// pass that lists every score at or above it, then k_refine.
+int run_pivot_refresh(const Plan &p, const void *Q, const void *K, float *tau, int32_t *pivot,
+                      char *w, hipStream_t s) {
+    PivotArgs pa;
+    pa.Q = (const uint16_t *)Q, pa.K = (const uint16_t *)K;
+    pa.B = p.B, pa.h_q = p.h_q, pa.h_k = p.h_k;
+    pa.l_kv = p.l_kv, pa.N = p.N, pa.chunk_len = p.chunk_len, pa.grp = p.grp;
+    pa.scale = (float)(1.0 / sqrt((double)p.d));
+    pa.pivot = pivot;
+    pa.pi = (float *)(w + p.off_pi);
+    if (p.d == 64)
+        hipLaunchKernelGGL(k_pivot<64>, dim3(p.rows), dim3(kAttendThreads), 0, s, pa);
+    else
+        hipLaunchKernelGGL(k_pivot<128>, dim3(p.rows), dim3(kAttendThreads), 0, s, pa);
+    SelectArgs sa = select_args(p, Q, K, (const float *)(w + p.off_pi), w);
+    launch_select<false>(p, sa, s);
+    launch_refine(p, tau, pivot, w, s);
     return launch_status();
 }
 
@@ -278,6 +315,7 @@ int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv,
     out->n_chunk = p.n_chunk;
     out->n_seg = p.n_sub;
     out->seg_cap = p.sub_cap;
+    out->seg_group = p.grp;
     return SAGA_OK;
 }
 
@@ -338,6 +376,34 @@ int saga_decode_step(const void *Q, const void *K, const void *V, int B, int h_q
     char *w = (char *)ws;
     hipStream_t s = (hipStream_t)hip_stream;
     if ((st = run_select(p, Q, K, tau, refresh, w, s)) != SAGA_OK) return st;
+    return run_attend(p, V, O, counts, w, s);
+}
+
+int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                           int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
+                           int refresh, float *O, int32_t *counts, void *ws, size_t ws_bytes,
+                           void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !V || !tau || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(tau, 4) || !aligned(O, 4) || (counts && !aligned(counts, 4)))
+        return SAGA_ERR_INVALID_ARG;
+    if (refresh < 0 || refresh > 2) return SAGA_ERR_INVALID_ARG;
+    if (refresh && (!pivot || !aligned(pivot, 4))) return SAGA_ERR_INVALID_ARG;
+    if ((st = check_ws(p, ws, ws_bytes)) != SAGA_OK) return st;
+    char *w = (char *)ws;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (refresh == 2) {
+        st = run_pivot_refresh(p, Q, K, tau, pivot, w, s);
+    } else {
+        st = run_select(p, Q, K, tau, refresh, w, s);
+        if (st == SAGA_OK && refresh == 1) {
+            launch_refine(p, tau, pivot, w, s);  // same tau again; records the pivot
+            st = launch_status();
+        }
+    }
+    if (st != SAGA_OK) return st;
     return run_attend(p, V, O, counts, w, s);
 }
 

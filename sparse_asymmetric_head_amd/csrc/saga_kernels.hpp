@@ -57,6 +57,19 @@ constexpr int kHistBins = 2048;
 constexpr int kHistBlockMax = 8192;  // positions per histogram/collect block
 constexpr int kRecHead = 15;  // survivors held in a record's first 128 bytes
 
+// Rank of cache position t in the order the survivor records list positions
+// (a bijection on the positions): chunk; wave w of the chunk's block (the
+// segment); the wave's groups of grp = 16*U rows (wave w takes groups w,
+// w+4, ...); the 16-row tile within the group; inside a tile, output
+// register r = row % 4 first, then lane quarter row / 4 (the ballot order).
+__host__ __device__ inline int64_t record_order_key(int64_t t, int64_t chunk_len, int64_t grp) {
+    const int64_t c = t / chunk_len, o = t % chunk_len;
+    const int64_t gi = o / grp, i = o % grp;
+    const int64_t w = gi % kWaves, k = gi / kWaves;
+    const int64_t q = i % 16;
+    return c * chunk_len + w * (chunk_len / kWaves) + k * grp + (i - q) + (q % 4) * 4 + q / 4;
+}
+
 // Words per segment record for a segment capacity of cap survivors.
 __host__ __device__ constexpr int64_t seg_words(int64_t cap) {
     return (2 + 2 * cap + 15) / 16 * 16 < 32 ? 32 : (2 + 2 * cap + 15) / 16 * 16;
@@ -101,7 +114,8 @@ struct SelectArgs {
 // Output: lane l holds rows 4*(l/16)+r, r = 0..3, of query head l%16.
 // Survivors are ranked per (wave, head) with ballots (deterministic order:
 // tile, then row, then lane), staged in LDS and flushed to the wave's
-// segment record of that head.
+// segment record of that head.  The record order of the positions is the
+// bijection record_order_key below.
 template <int D, int NT, bool MATERIALIZE>
 __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     // First d-index of the 8 elements lane quarter lq supplies at MFMA
@@ -696,11 +710,12 @@ __global__ __launch_bounds__(kThreads) void k_select_final(RadixArgs a) {
 }
 
 // Refresh step selection from the materialised scores: A >= tau into the
-// same (row, segment) records k_select writes.  Wave w of the block for
-// (row, chunk) covers positions [chunk*chunk_len + w*sub_cap, ... + sub_cap).
+// same (row, segment) records k_select writes, in the same record order:
+// wave w of the block for (row, chunk) lists, for its record indices j =
+// 0, 1, ..., the position whose record_order_key within the segment is j.
 struct CompactArgs {
     const float *A;
-    int64_t ld_a, l_kv, chunk_len;
+    int64_t ld_a, l_kv, chunk_len, grp;
     int n_chunk;
     const float *tau;
     int32_t *seg;
@@ -712,44 +727,358 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = blockIdx.x / a.n_chunk, chunk = blockIdx.x % a.n_chunk;
     const int sub = chunk * kWaves + wave;
-    const int64_t t0 = (int64_t)chunk * a.chunk_len + (int64_t)wave * a.sub_cap;
-    const int64_t t1 = min(a.l_kv, t0 + a.sub_cap);
+    const int64_t c0 = (int64_t)chunk * a.chunk_len;
+    const int64_t t_end = min(a.l_kv, c0 + a.chunk_len);
     const float tau = a.tau[row];
     const float *Ar = a.A + (int64_t)row * a.ld_a;
     int2 *rec = (int2 *)(a.seg + ((int64_t)row * a.n_sub + sub) * a.seg_w);
+    const int64_t tiles_per_grp = a.grp / 16;
+    // 16 tiles of the segment per round, in record order; lane l takes tile
+    // l / 4, rows 4 * (l % 4) .. +3 (one float4, output registers r = 0..3)
+    const int tt = lane >> 2, lq = lane & 3;
+    const uint64_t tile_lanes = 0xFull << (4 * tt), below = (1ull << (4 * tt)) - 1ull;
+    const uint64_t lt = (1ull << lane) - 1ull;
     int cnt = 0;
     uint32_t mk = 0u;
-    // 256 positions per pass: lane l takes positions 4l..4l+3 (one float4);
-    // survivors are ranked in position order.
-    for (int64_t tb = t0; tb < t1; tb += 256) {
-        const int64_t t = tb + 4 * lane;
+    const int64_t n_tiles = a.sub_cap / 16;
+    for (int64_t T0 = 0; T0 < n_tiles; T0 += 16) {
+        const int64_t T = T0 + tt;  // tile of the segment, in record order
+        const int64_t k = T / tiles_per_grp, u = T % tiles_per_grp;
+        const int64_t t = c0 + (k * kWaves + wave) * a.grp + u * 16 + lq * 4;
         f32x4 v;
-        if (t + 3 < t1) {
+        if (T < n_tiles && t + 3 < t_end) {
             v = *(const f32x4 *)(Ar + t);
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = (t + c < t1) ? Ar[t + c] : -INFINITY;
+            for (int r = 0; r < 4; ++r) v[r] = (T < n_tiles && t + r < t_end) ? Ar[t + r] : -INFINITY;
         }
         bool p[4];
-        int mine = 0;
+        uint64_t m[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            p[c] = (t + c < t1) && v[c] >= tau;
-            mine += p[c];
+        for (int r = 0; r < 4; ++r) {
+            p[r] = T < n_tiles && t + r < t_end && v[r] >= tau;
+            m[r] = ballot(p[r]);
         }
-        const int incl = wave_incl_scan(mine);
-        int pos = cnt + incl - mine;
+        // rank: survivors of earlier tiles, then of this tile's earlier
+        // registers, then of this register's lower lanes
+        int rank = cnt;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (p[c]) {
-                rec[1 + pos++] = int2{(int)(t + c), __float_as_int(v[c])};
-                const uint32_t k = fkey(v[c]);
-                mk = mk > k ? mk : k;
+        for (int r = 0; r < 4; ++r) rank += __popcll(m[r] & below);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (p[r]) {
+                rec[1 + rank + __popcll(m[r] & tile_lanes & lt)] =
+                    int2{(int)(t + r), __float_as_int(v[r])};
+                const uint32_t kv = fkey(v[r]);
+                mk = mk > kv ? mk : kv;
             }
-        cnt += __shfl(incl, 63);
+            rank += __popcll(m[r] & tile_lanes);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cnt += __popcll(m[r]);
     }
     mk = wave_max_u32(mk);
     if (lane == 0) rec[0] = int2{cnt, (int)mk};
+}
+
+// ------------------------------------------------------------------ refresh from a pivot
+
+// The exact refresh without materialising the scores.  Any N distinct
+// positions P give a lower bound on the row's N-th largest score: the least
+// of their scores (P is taken as distinct when its record_order_keys
+// increase, the order k_refine writes it in).  k_pivot computes it (less a margin that covers the
+// difference between its own fp32 sums and the MFMA's), k_select then lists
+// every position scoring at least that bound, and k_refine finds the exact
+// N-th largest among the listed scores -- they include the N largest -- and
+// records N positions of the new survivors as the next refresh's P.
+
+struct PivotArgs {
+    const uint16_t *Q, *K;
+    int B, h_q, h_k;
+    int64_t l_kv, N, chunk_len, grp;
+    float scale;
+    const int32_t *pivot;  // [rows][N]: positions with increasing record_order_key, else unusable
+    float *pi;             // [rows] out: the lower bound (-inf when P is unusable)
+};
+
+// Relative margin on |q|.|k| sums: the two fp32 sums of d exact products
+// differ by at most 2 (d - 1) 2^-24 of the sum of absolute products, far
+// below 2^-12 for d <= 128.
+constexpr float kPivotMargin = 1.0f / 4096.0f;
+
+// One block (512 threads) per row; thread i takes pivot positions i, i + 512,
+// ...: the position loads, then the key-row loads, all in flight together.
+template <int D>
+__global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
+    constexpr int NW = kAttendThreads / kWave;
+    __shared__ float wmin[NW];
+    __shared__ int wbad[NW];
+    const int row = blockIdx.x, b = row / a.h_q, j = row % a.h_q;
+    const int g = (int)(((int64_t)j * a.h_k) / a.h_q);
+    float qf[D];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const u32x4 v = ld16(a.Q + (int64_t)row * D + c * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qf[c * 8 + 2 * i] = bf_lo(v[i]);
+            qf[c * 8 + 2 * i + 1] = bf_hi(v[i]);
+        }
+    }
+    const uint16_t *Kg = a.K + ((int64_t)b * a.h_k + g) * a.l_kv * D;
+    const int32_t *P = a.pivot + (int64_t)row * a.N;
+    float mn = INFINITY;
+    int bad = 0;
+    for (int64_t i0 = 0; i0 < a.N; i0 += kAttendThreads) {
+        const int64_t i = i0 + threadIdx.x;
+        const int64_t ii = i < a.N ? i : a.N - 1;
+        const int p = P[ii];
+        const int prev = ii > 0 ? P[ii - 1] : -1;
+        const bool in = p >= 0 && p < a.l_kv;
+        const int64_t kp = in ? record_order_key(p, a.chunk_len, a.grp) : -1;
+        const int64_t kq = ii == 0 ? -1
+                         : (prev >= 0 && prev < a.l_kv ? record_order_key(prev, a.chunk_len, a.grp)
+                                                        : INT64_MAX);
+        const bool ok = in && kp > kq;  // inside the cache, distinct (increasing keys)
+        if (i < a.N) bad |= !ok;
+        const uint16_t *kr = Kg + (int64_t)(ok ? p : 0) * D;
+        u32x4 kv[D / 8];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) kv[c] = ld16(kr + c * 8);
+        float s = 0.f, e = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) {
+                const float p0 = qf[c * 8 + 2 * i2] * bf_lo(kv[c][i2]);
+                const float p1 = qf[c * 8 + 2 * i2 + 1] * bf_hi(kv[c][i2]);
+                s += p0 + p1;
+                e += fabsf(p0) + fabsf(p1);
+            }
+        const float sc = s * a.scale - (e * a.scale * kPivotMargin + 1e-30f);
+        if (i < a.N) mn = fminf(mn, sc);
+    }
+    mn = -wave_max(-mn);
+    bad = wave_sum_i32(bad);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        wmin[wave] = mn;
+        wbad[wave] = bad;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = INFINITY;
+        int bd = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            m = fminf(m, wmin[w]);
+            bd += wbad[w];
+        }
+        a.pi[row] = bd ? -INFINITY : m;
+    }
+}
+
+struct RefineArgs {
+    int32_t *seg;        // [rows][n_sub][seg_w] records of every score >= pi; rewritten to S
+    int n_sub;
+    int64_t seg_w, sub_cap, N;
+    float *tau;          // [rows] out: the exact N-th largest score
+    int32_t *pivot;      // [rows][N] out: positions of N survivors, in record order
+};
+
+constexpr int kRefineCap = 8192;  // listed scores staged in LDS
+
+// One block per row.  The listed scores (up to kRefineCap staged in LDS with
+// their positions and segments, else read from the records on every pass)
+// go through three radix digits (11, 11 and 10 bits of the order key, from
+// the top) to the exact key of rank N.  The survivors (score >= tau) are
+// then walked in record order: the first N positions go to pivot, and every
+// record is rewritten in place to its survivors (same order; the max key
+// stays right, since a record that keeps any survivor keeps its largest).
+__global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
+    constexpr int SPT = kMaxSub / kThreads;  // segments per thread (4)
+    constexpr int SU = 8;                    // staging loads in flight per thread
+    __shared__ uint32_t ekey[kRefineCap];
+    __shared__ int epos[kRefineCap];
+    __shared__ uint16_t eseg[kRefineCap];
+    __shared__ uint32_t h[kHistBins];
+    __shared__ int soff[kMaxSub + 1];
+    __shared__ int pcnt[kMaxSub], pbase[kMaxSub];
+    __shared__ int red[kWaves];
+    __shared__ int sel_bin;
+    __shared__ uint32_t above;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
+
+    // segment counts -> offsets of the flattened list
+    int c[SPT], mine = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int sgi = tid * SPT + i;
+        int n = sgi < a.n_sub ? rb[(int64_t)sgi * a.seg_w] : 0;
+        n = n < 0 ? 0 : (n > a.sub_cap ? (int)a.sub_cap : n);
+        c[i] = n;
+        mine += n;
+    }
+    int total;
+    int pre = block_excl_scan<kWaves>(mine, red, &total);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int sgi = tid * SPT + i;
+        if (sgi < a.n_sub) {
+            soff[sgi] = pre;
+            pcnt[sgi] = 0;
+        }
+        pre += c[i];
+    }
+    if (tid == 0) {
+        soff[a.n_sub] = total;
+        sel_bin = 0;
+        above = 0u;
+    }
+    __syncthreads();
+    if (total == 0) return;  // block-uniform; no survivors listed (cannot happen for N >= 1)
+    // segment of flattened entry i (soff is non-decreasing)
+    auto seg_of = [&](int i) {
+        int lo = 0, hi = a.n_sub - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (soff[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    auto entry_ptr = [&](int sgi, int i) {
+        return (const int2 *)(rb + (int64_t)sgi * a.seg_w) + 1 + (i - soff[sgi]);
+    };
+    const bool staged = total <= kRefineCap;
+    if (staged) {
+        for (int base = 0; base < total; base += kThreads * SU) {
+            int sgs[SU];
+            int2 v[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = min(total - 1, base + u * kThreads + tid);
+                sgs[u] = seg_of(i);
+                v[u] = *entry_ptr(sgs[u], i);
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = base + u * kThreads + tid;
+                if (i < total) {
+                    epos[i] = v[u].x;
+                    ekey[i] = fkey(__int_as_float(v[u].y));
+                    eseg[i] = (uint16_t)sgs[u];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    auto key_at = [&](int i) {
+        return staged ? ekey[i] : fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
+    };
+
+    // digit 1: bits 31..21
+    for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < total; i += kThreads) atomicAdd(&h[key_at(i) >> 21], 1u);
+    __syncthreads();
+    find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
+    const uint32_t d0 = (uint32_t)sel_bin, k0 = (uint32_t)a.N - above;
+    // digit 2: bits 20..10 among keys with digit 1 = d0
+    for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < total; i += kThreads) {
+        const uint32_t k = key_at(i);
+        if ((k >> 21) == d0) atomicAdd(&h[(k >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    find_bin_desc(h, kHistBins, k0, &sel_bin, &above, red);
+    const uint32_t d1 = (uint32_t)sel_bin, k1 = k0 - above;
+    // digit 3: bits 9..0
+    for (int i = tid; i < 1024; i += kThreads) h[i] = 0u;
+    __syncthreads();
+    const uint32_t pfx = (d0 << 11) | d1;
+    for (int i = tid; i < total; i += kThreads) {
+        const uint32_t k = key_at(i);
+        if ((k >> 10) == pfx) atomicAdd(&h[k & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin_desc(h, 1024, k1, &sel_bin, &above, red);
+    const uint32_t tkey = (pfx << 10) | (uint32_t)sel_bin;
+    if (tid == 0) a.tau[row] = fkey_inv(tkey);
+
+    // survivors per segment, their record-order ranks, the first N -> pivot
+    const int per = (total + kThreads - 1) / kThreads;
+    const int i0 = min(total, tid * per), i1 = min(total, i0 + per);
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) {
+        if (key_at(i) >= tkey) {
+            ++cnt;
+            if (staged) atomicAdd(&pcnt[eseg[i]], 1);
+        }
+    }
+    int tot_pass;
+    int r = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+    int32_t *P = a.pivot + (int64_t)row * a.N;
+    for (int i = i0; i < i1 && r < a.N; ++i) {
+        if (key_at(i) >= tkey) {
+            P[r] = staged ? epos[i] : entry_ptr(seg_of(i), i)->x;
+            ++r;
+        }
+    }
+    if (staged) {
+        // survivors before each segment -> in-place rewrite from the LDS copy
+        int pm = 0, pc[SPT];
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int sgi = tid * SPT + i;
+            pc[i] = sgi < a.n_sub ? pcnt[sgi] : 0;
+            pm += pc[i];
+        }
+        int ptot;
+        int pb = block_excl_scan<kWaves>(pm, red, &ptot);
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int sgi = tid * SPT + i;
+            if (sgi < a.n_sub) {
+                pbase[sgi] = pb;
+                rb[(int64_t)sgi * a.seg_w] = pc[i];  // new count; the key word stays
+            }
+            pb += pc[i];
+        }
+        __syncthreads();
+        int rr = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t k = ekey[i];
+            if (k >= tkey) {
+                const int sgi = eseg[i];
+                int2 *dst = (int2 *)(rb + (int64_t)sgi * a.seg_w) + 1 + (rr - pbase[sgi]);
+                *dst = int2{epos[i], __float_as_int(fkey_inv(k))};
+                ++rr;
+            }
+        }
+    } else {
+        // in place, one segment per wave at a time, 64 entries per round: a
+        // round reads its entries before writing survivors to lower indices
+        __syncthreads();  // every read of the walk above is done
+        for (int sgi = wave; sgi < a.n_sub; sgi += kWaves) {
+            const int n = soff[sgi + 1] - soff[sgi];
+            int2 *e = (int2 *)(rb + (int64_t)sgi * a.seg_w) + 1;
+            int kept = 0;
+            for (int k0 = 0; k0 < n; k0 += kWave) {
+                const int k = k0 + lane;
+                const int2 v = k < n ? e[k] : int2{0, 0};
+                const bool ps = k < n && fkey(__int_as_float(v.y)) >= tkey;
+                const uint64_t m = ballot(ps);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                if (ps) e[kept + mbcnt_lt(m)] = v;
+                kept += __popcll(m);
+            }
+            if (lane == 0) rb[(int64_t)sgi * a.seg_w] = kept;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ read probe

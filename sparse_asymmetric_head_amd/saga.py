@@ -26,7 +26,7 @@ EXPORTS = (
     "saga_status_string", "saga_version", "saga_workspace_bytes", "saga_dense_workspace_bytes",
     "saga_workspace_init", "saga_refresh_threshold", "saga_decode_step",
     "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
-    "saga_attend", "saga_read_probe",
+    "saga_attend", "saga_read_probe", "saga_decode_step_pivot",
 )
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
@@ -48,6 +48,7 @@ class WsLayout(ctypes.Structure):
         ("n_chunk", ctypes.c_int64),
         ("n_seg", ctypes.c_int64),
         ("seg_cap", ctypes.c_int64),
+        ("seg_group", ctypes.c_int64),
     ]
 
 
@@ -79,6 +80,9 @@ def lib(path: str | None = None):
     L.saga_decode_step.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, vp, i32, vp,
                                    vp, vp, sz, vp]
     L.saga_decode_step.restype = i32
+    L.saga_decode_step_pivot.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, vp, vp,
+                                         i32, vp, vp, vp, sz, vp]
+    L.saga_decode_step_pivot.restype = i32
     L.saga_select.argtypes = [vp, vp, i32, i32, i32, i32, i32, i64, i64, vp, i32, vp, sz, vp]
     L.saga_select.restype = i32
     L.saga_attend.argtypes = [vp, i32, i32, i32, i32, i32, i64, i64, vp, vp, vp, sz, vp]
@@ -185,6 +189,20 @@ def saga_decode_step(Q, K, V, N: int, tau, refresh: bool, O, counts=None, ws=Non
                                   _ptr(tau), 1 if refresh else 0, _ptr(O), _ptr(counts),
                                   _ptr(ws), ws.numel(), _stream(stream)),
            "saga_decode_step")
+
+
+def saga_decode_step_pivot(Q, K, V, N: int, tau, pivot, refresh: int, O, counts=None, ws=None,
+                           stream=None) -> None:
+    """refresh: 0 compare with tau, 1 exact refresh (records the pivot), 2 exact
+    refresh from the pivot; pivot is an int32 [B][h_q][N] tensor."""
+    B, h_q, d = _dims(Q, K, V)
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    if ws is None:
+        raise ValueError("a workspace is required (alloc_workspace)")
+    _check(lib().saga_decode_step_pivot(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
+                                        int(N), _ptr(tau), _ptr(pivot), int(refresh), _ptr(O),
+                                        _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_decode_step_pivot")
 
 
 def saga_select(Q, K, h_v: int, N: int, tau, refresh: bool, ws, stream=None) -> None:

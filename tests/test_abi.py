@@ -76,6 +76,7 @@ def test_workspace_layout_consistent(L, shape):
     assert lay.bytes == nbytes
     assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
     assert lay.n_seg == 4 * lay.n_chunk and lay.seg_cap * 4 == lay.chunk_len
+    assert lay.seg_group == 64 * 64 // d and lay.chunk_len % (4 * lay.seg_group) == 0
     assert lay.n_seg <= 1024
     assert lay.scores_ld >= l_kv and lay.scores_ld % 4 == 0
     assert lay.seg_words % 16 == 0 and lay.seg_words >= 2 + 2 * lay.seg_cap
@@ -143,6 +144,15 @@ def test_entry_points_validate_before_launch(L):
         saga.SAGA_ERR_INVALID_ARG
     assert L.saga_selection_mask(fake, need, B, h_q, h_k, h_v, d, l_kv, N, None, None) == \
         saga.SAGA_ERR_INVALID_ARG
+    dp = L.saga_decode_step_pivot
+    pargs = [fake, fake, fake, B, h_q, h_k, h_v, d, l_kv, N, fake, fake, 2, fake, None, fake, need,
+             None]
+    bad = list(pargs); bad[11] = None          # refresh without a pivot array
+    assert dp(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(pargs); bad[12] = 3             # unknown refresh mode
+    assert dp(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(pargs); bad[16] = need - 256
+    assert dp(*bad) == saga.SAGA_ERR_WORKSPACE
     rp = L.saga_read_probe
     assert rp(None, 1024, fake, None) == saga.SAGA_ERR_INVALID_ARG
     assert rp(fake, 1024, None, None) == saga.SAGA_ERR_INVALID_ARG

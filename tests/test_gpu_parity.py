@@ -390,7 +390,8 @@ def test_attend_mixed_counts_and_many_segments():
         for bb in range(B):
             for j in range(h_q):
                 t[bb, j] = np.quantile(A[bb, j], qs[(bb * h_q + j) % len(qs)])
-        O, cnt, ws = _step(Q, K, V, 16, torch.from_numpy(t).cuda(), False)
+        tg = torch.from_numpy(t).cuda()
+        O, cnt, ws = _step(Q, K, V, 16, tg, False)
         m = read_mask(ws, (B, h_q, h_k, h_v, d, l_kv), 16)
         for bb in range(B):
             for j in range(h_q):
@@ -414,3 +415,93 @@ def test_read_probe_checksum():
         got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
         want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
         assert got == want, nbytes
+
+
+def ws_layout(B, h_q, h_k, h_v, d, l_kv, N):
+    return saga.saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, N)
+
+
+def record_order_keys(t, lay):
+    """Rank of each position in the order the survivor records list them:
+    chunk, segment (wave w takes the chunk's row groups w, w+4, ...), group,
+    16-row tile, then row % 4 before row / 4 inside the tile."""
+    t = np.asarray(t, np.int64)
+    c, o = t // lay.chunk_len, t % lay.chunk_len
+    gi, i = o // lay.seg_group, o % lay.seg_group
+    w, k = gi % 4, gi // 4
+    q = i % 16
+    return c * lay.chunk_len + w * lay.seg_cap + k * lay.seg_group + (i - q) + (q % 4) * 4 + q // 4
+
+
+def _pivot_trajectory(Q, K, V, N, R, invalid_first=False):
+    """Run the same steps with saga_decode_step (full refreshes) and with
+    saga_decode_step_pivot (refresh 1 first, then refreshes from the pivot);
+    return per-step (tau, O, counts, pivot-or-None, mask) of both."""
+    T, B, h_q, d = Q.shape
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    shape = (B, h_q, h_k, h_v, d, l_kv)
+    nb = saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N)
+    ws_a, ws_b = saga.alloc_workspace(nb), saga.alloc_workspace(nb)
+    tau_a = torch.zeros(B, h_q, device="cuda")
+    tau_b = torch.zeros(B, h_q, device="cuda")
+    piv = torch.full((B, h_q, N), -1, dtype=torch.int32, device="cuda")
+    out_a, out_b = [], []
+    for t in range(T):
+        ref = t % R == 0
+        O_a = torch.empty(B, h_q, d, device="cuda"); c_a = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+        O_b = torch.empty_like(O_a); c_b = torch.empty_like(c_a)
+        saga.saga_decode_step(Q[t], K, V, N, tau_a, ref, O_a, c_a, ws_a)
+        mode = 0 if not ref else (2 if (t > 0 or invalid_first) else 1)
+        saga.saga_decode_step_pivot(Q[t], K, V, N, tau_b, piv, mode, O_b, c_b, ws_b)
+        torch.cuda.synchronize()
+        out_a.append((tau_a.clone(), O_a, c_a, None, read_mask(ws_a, shape, N)))
+        out_b.append((tau_b.clone(), O_b, c_b, piv.clone() if ref else None,
+                      read_mask(ws_b, shape, N)))
+    return out_a, out_b
+
+
+PIVOT_CASES = [
+    # B, h_q, h_k, h_v, d, l_kv, N, R, T, planted, drift
+    (1, 32, 4, 16, 64, 32768, 256, 4, 9, 64, 0.05),
+    (2, 12, 1, 4, 128, 20000, 100, 3, 7, 32, 0.05),
+    (2, 6, 4, 5, 64, 3001, 37, 2, 5, 8, 0.05),
+    (1, 8, 2, 4, 64, 30000, 64, 2, 5, 0, 3.0),   # the query changes a lot between refreshes
+]
+
+
+@pytest.mark.parametrize("case", PIVOT_CASES, ids=[str(c) for c in PIVOT_CASES])
+def test_pivot_refresh_matches_full_refresh(case):
+    """The refresh from a pivot gives the same tau bit for bit as the full
+    refresh, hence the same selections, outputs (bitwise: same survivors in
+    the same order) and counts; the recorded pivot rows are N increasing
+    positions of the selection."""
+    B, h_q, h_k, h_v, d, l_kv, N, R, T, P, drift = case
+    x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=l_kv % 997, device="cuda", steps=T,
+                       planted=P, drift=drift)
+    out_a, out_b = _pivot_trajectory(x["Q"], x["K"], x["V"], N, R)
+    for t, ((ta, Oa, ca, _, ma), (tb, Ob, cb, pv, mb)) in enumerate(zip(out_a, out_b)):
+        assert torch.equal(ta.view(torch.int32), tb.view(torch.int32)), f"tau differs at step {t}"
+        assert np.array_equal(ma, mb), f"selection differs at step {t}"
+        assert torch.equal(ca, cb), f"counts differ at step {t}"
+        assert torch.equal(Oa, Ob), f"outputs differ at step {t}"
+        if pv is not None:
+            p = pv.cpu().numpy()
+            assert (p >= 0).all() and (p < l_kv).all()
+            keys = record_order_keys(p, ws_layout(B, h_q, h_k, h_v, d, l_kv, N))
+            assert (np.diff(keys, axis=-1) > 0).all(), "pivot not in record order"
+            rows = np.take_along_axis(mb.reshape(B * h_q, l_kv), p.reshape(B * h_q, N), axis=1)
+            assert (rows == 1).all(), f"pivot outside the selection at step {t}"
+
+
+def test_pivot_refresh_with_unusable_pivot_is_exact():
+    """A pivot row that is not N increasing positions (here all -1) gives the
+    bound -inf: every score is listed (more than the refine kernel stages in
+    LDS at l_kv = 20000) and tau is still exact."""
+    for (B, h_q, h_k, h_v, d, l_kv, N) in [(1, 8, 2, 4, 64, 20000, 50), (1, 4, 1, 2, 128, 5000, 5000)]:
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=77, device="cuda", steps=2, planted=8)
+        out_a, out_b = _pivot_trajectory(x["Q"], x["K"], x["V"], N, 1, invalid_first=True)
+        for (ta, Oa, ca, _, ma), (tb, Ob, cb, pv, mb) in zip(out_a, out_b):
+            assert torch.equal(ta.view(torch.int32), tb.view(torch.int32))
+            assert np.array_equal(ma, mb) and torch.equal(ca, cb) and torch.equal(Oa, Ob)
+            keys = record_order_keys(pv.cpu().numpy(), ws_layout(B, h_q, h_k, h_v, d, l_kv, N))
+            assert (np.diff(keys, axis=-1) > 0).all()
