@@ -331,6 +331,49 @@ def main() -> int:
     achieved = select_alg / (sel_us * 1e-6)
     log(f"select kernel {sel_us:.2f} us/launch -> {achieved / 1e9:.0f} GB/s")
 
+    # ------------------------------------------------------------ SAGA full attention
+    # The decoupled heads without the sparsity (every position), on the same
+    # caches: K read once per key head, V once per value head.
+    full = None
+    if not args.no_dense:
+        fws = torch.empty(saga.saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv),
+                          dtype=torch.uint8, device=dev)
+        fO = torch.empty(L, B, h_q, d, dtype=torch.float32, device=dev)
+
+        def full_pass():
+            for l in range(L):
+                saga.saga_full_attention(qbuf[l], Ks[l], Vs[l], fO[l], fws)
+
+        with torch.cuda.stream(stream):
+            full_pass()
+            stream.synchronize()
+            fg = None
+            if not args.no_graph:
+                fg = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(fg, stream=stream):
+                    full_pass()
+            run_full = fg.replay if fg is not None else full_pass
+            for _ in range(args.warmup):
+                run_full()
+            stream.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(args.steps):
+                run_full()
+            e1.record(stream)
+            stream.synchronize()
+            w1 = time.perf_counter()
+        full_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3
+        full_bytes = L * (B * (h_k + h_v) * l_kv * d * 2 + q_bytes + o_bytes)
+        full = {"us_per_step": round(full_us, 2),
+                "hbm_gbps": round(full_bytes / (full_us * 1e-6) / 1e9, 1),
+                "speedup_saga_sparse_vs_full": round(full_us / us_per_step, 3)}
+        log(f"SAGA full attention (h_k={h_k}, h_v={h_v}): {full_us:.1f} us/step, "
+            f"{full['hbm_gbps']:.0f} GB/s")
+        del fws, fO
+
     # ------------------------------------------------------------ dense baseline
     dense = None
     if cfg.dense_h_kv and not args.no_dense:
@@ -371,6 +414,8 @@ def main() -> int:
         dense = {"h_kv": hk, "us_per_step": round(dense_us, 2),
                  "hbm_gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
                  "speedup_saga_vs_dense": round(dense_us / us_per_step, 3)}
+        if full is not None:
+            full["speedup_vs_dense_gqa"] = round(dense_us / full["us_per_step"], 3)
         log(f"dense GQA h_kv={hk}: {dense_us:.1f} us/step, speedup {dense_us / us_per_step:.2f}x")
         del dl
 
@@ -435,6 +480,7 @@ def main() -> int:
                      "frac_of_probe": round(achieved / 1e9 / probe_gbps, 4)},
         "per_step_us": per_step,
         "dense_gqa": dense,
+        "saga_full_attention": full,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

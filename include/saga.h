@@ -149,6 +149,23 @@ int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, 
                             int h_kv, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
                             void *hip_stream);
 
+/*
+ * SAGA full attention: the decoupled heads without the sparsity, softmax
+ * over every cache position (SAGA Architecture; eqs. 2-4 with key head
+ * floor(j*h_k/h_q) and value head floor(j*h_v/h_q)):
+ *   O[b][j] := softmax(q_j K_{kh(j)}^T / sqrt(d)) V_{vh(j)},
+ * K bf16 [B][h_k][l_kv][d], V bf16 [B][h_v][l_kv][d], 1 <= h_k <= h_v <= h_q,
+ * d in {64, 128}; fp32 output [B][h_q][d].  Each key row is read once per
+ * key head (once per subset of four value heads when a key head serves more
+ * than four), each value row once.  ws: saga_full_attention_workspace_bytes
+ * bytes, 256-byte aligned.  h_k = h_v is saga_dense_gqa_baseline.  Returns
+ * SAGA_ERR_UNSUPPORTED when a block would serve more than 16 query heads.
+ */
+size_t saga_full_attention_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv);
+int saga_full_attention(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                        int h_v, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
+                        void *hip_stream);
+
 /* Where the last call left its intermediate results inside the workspace
  * (byte offsets from ws), for inspection and testing. */
 typedef struct saga_ws_layout {

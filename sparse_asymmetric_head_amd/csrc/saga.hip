@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -102,21 +104,67 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
 }
 
 struct DensePlan {
-    int rows, gmax;
+    int rows, gmax, nv, n_vsub;
     int64_t chunk_len;
     int n_chunk;
     size_t total;
 };
 
-int make_dense_plan(int B, int h_q, int h_kv, int d, int64_t l_kv, DensePlan *p) {
-    if (B < 1 || h_q < 1 || h_kv < 1 || h_kv > h_q || l_kv < 1) return SAGA_ERR_INVALID_ARG;
+int64_t host_group_lo(int64_t g, int64_t h_q, int64_t h_k) { return (g * h_q + h_k - 1) / h_k; }
+
+// Dense decode plan for key heads h_k and value heads h_v (h_k = h_v: GQA).
+// A block serves one key head's chunk and the query heads of up to nv of
+// its group's value heads; groups with more value heads (or with more than
+// 8 query heads over nv value heads) are split into n_vsub subsets, each
+// reading the key rows again.
+int make_dense_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, DensePlan *p) {
+    if (B < 1 || h_q < 1 || h_k < 1 || h_v < 1 || l_kv < 1) return SAGA_ERR_INVALID_ARG;
+    if (h_k > h_v || h_v > h_q) return SAGA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
-    if (ceil_div(h_q, h_kv) > 16) return SAGA_ERR_UNSUPPORTED;
     if (l_kv * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)B * h_q >= (int64_t(1) << 20)) return SAGA_ERR_UNSUPPORTED;
+    auto vh = [&](int64_t j) { return j * h_v / h_q; };
+    int64_t maxv = 1;
+    for (int g = 0; g < h_k; ++g) {
+        const int64_t jl = host_group_lo(g, h_q, h_k), jh = host_group_lo(g + 1, h_q, h_k);
+        if (jh > jl) maxv = std::max(maxv, vh(jh - 1) - vh(jl) + 1);
+    }
+    // query heads per block for subsets of nv value heads
+    auto block_heads = [&](int nv, int n_vsub) {
+        int64_t gm = 0;
+        for (int g = 0; g < h_k; ++g) {
+            const int64_t jl = host_group_lo(g, h_q, h_k), jh = host_group_lo(g + 1, h_q, h_k);
+            for (int vs = 0; vs < n_vsub; ++vs) {
+                int64_t a = jl, bq = jh;
+                if (nv > 1 || n_vsub > 1) {
+                    const int64_t v_lo = vh(jl) + vs * nv;
+                    a = std::max(jl, host_group_lo(v_lo, h_q, h_v));
+                    bq = std::min(jh, host_group_lo(v_lo + nv, h_q, h_v));
+                }
+                gm = std::max(gm, bq - a);
+            }
+        }
+        return gm;
+    };
+    // the largest subset (fewest key re-reads) whose blocks keep at most 8
+    // query heads, the size that leaves registers for two tile buffers;
+    // else the subset with the fewest query heads per block
+    const int first = maxv == 1 ? 1 : (maxv == 2 ? 2 : 4);
+    int64_t gmax = -1;
+    for (int nv = first; nv >= 1; nv /= 2) {
+        const int nvs = (int)ceil_div(maxv, nv);
+        const int64_t gm = block_heads(nv, nvs);
+        if (gmax < 0 || gm < gmax) {
+            gmax = gm;
+            p->nv = nv;
+            p->n_vsub = nvs;
+        }
+        if (gm <= 8) break;
+    }
+    if (gmax > 16) return SAGA_ERR_UNSUPPORTED;
     p->rows = B * h_q;
-    p->gmax = (int)ceil_div(h_q, h_kv);
-    const int64_t pairs = (int64_t)B * h_kv;
+    p->gmax = (int)gmax;
+    const int64_t pairs = (int64_t)B * h_k * p->n_vsub;
     int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetDenseBlocks), kChunkUnit) * kChunkUnit;
     const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kChunkUnit) * kChunkUnit;
     if (cl < cl_min) cl = cl_min;
@@ -267,6 +315,60 @@ int run_pivot_refresh(const Plan &p, const void *Q, const void *K, float *tau, i
     return launch_status();
 }
 
+template <int D, int GMAX, int NV>
+void launch_dense_t(const DenseArgs &a, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((k_dense<D, GMAX, NV>), dim3(blocks), dim3(kThreads), 0, s, a);
+}
+
+template <int D, int NV>
+void launch_dense_g(const DensePlan &p, const DenseArgs &a, int blocks, hipStream_t s) {
+    if (p.gmax <= 4) launch_dense_t<D, 4, NV>(a, blocks, s);
+    else if (p.gmax <= 8) launch_dense_t<D, 8, NV>(a, blocks, s);
+    else launch_dense_t<D, 16, NV>(a, blocks, s);
+}
+
+// Dense split-KV decode (key heads h_k, value heads h_v) and the merge of
+// the chunk partials.
+int run_dense(const void *Q, const void *K, const void *V, int B, int h_q, int h_k, int h_v,
+              int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes, void *hip_stream) {
+    DensePlan p;
+    int st = make_dense_plan(B, h_q, h_k, h_v, d, l_kv, &p);
+    if (st != SAGA_OK) return st;
+    if (!Q || !K || !V || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(O, 4))
+        return SAGA_ERR_INVALID_ARG;
+    if (!ws || !aligned(ws, kAlign)) return SAGA_ERR_INVALID_ARG;
+    if (ws_bytes < p.total) return SAGA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)hip_stream;
+    DenseArgs a;
+    a.Q = (const uint16_t *)Q, a.K = (const uint16_t *)K, a.V = (const uint16_t *)V;
+    a.B = B, a.h_q = h_q, a.h_k = h_k, a.h_v = h_v;
+    a.n_chunk = p.n_chunk;
+    a.n_vsub = p.n_vsub;
+    a.l_kv = l_kv, a.chunk_len = p.chunk_len;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    a.partial = (float *)ws;
+    const int blocks = B * h_k * p.n_vsub * p.n_chunk;
+    if (d == 64) {
+        if (p.nv == 1) launch_dense_g<64, 1>(p, a, blocks, s);
+        else if (p.nv == 2) launch_dense_g<64, 2>(p, a, blocks, s);
+        else launch_dense_g<64, 4>(p, a, blocks, s);
+    } else {
+        if (p.nv == 1) launch_dense_g<128, 1>(p, a, blocks, s);
+        else if (p.nv == 2) launch_dense_g<128, 2>(p, a, blocks, s);
+        else launch_dense_g<128, 4>(p, a, blocks, s);
+    }
+    DenseMergeArgs m;
+    m.partial = (const float *)ws;
+    m.n_chunk = p.n_chunk;
+    m.O = O;
+    if (d == 64)
+        hipLaunchKernelGGL(k_dense_merge<64>, dim3(p.rows), dim3(kThreads), 0, s, m);
+    else
+        hipLaunchKernelGGL(k_dense_merge<128>, dim3(p.rows), dim3(kThreads), 0, s, m);
+    return launch_status();
+}
+
 int check_ws(const Plan &p, const void *ws, size_t ws_bytes) {
     if (!ws || !aligned(ws, kAlign)) return SAGA_ERR_INVALID_ARG;
     if (ws_bytes < p.total) return SAGA_ERR_WORKSPACE;
@@ -297,7 +399,13 @@ size_t saga_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t l_k
 
 size_t saga_dense_workspace_bytes(int B, int h_q, int h_kv, int d, int64_t l_kv) {
     DensePlan p;
-    return make_dense_plan(B, h_q, h_kv, d, l_kv, &p) == SAGA_OK ? p.total : 0;
+    return make_dense_plan(B, h_q, h_kv, h_kv, d, l_kv, &p) == SAGA_OK ? p.total : 0;
+}
+
+size_t saga_full_attention_workspace_bytes(int B, int h_q, int h_k, int h_v, int d,
+                                           int64_t l_kv) {
+    DensePlan p;
+    return make_dense_plan(B, h_q, h_k, h_v, d, l_kv, &p) == SAGA_OK ? p.total : 0;
 }
 
 int saga_workspace_layout(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N,
@@ -410,44 +518,13 @@ int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, i
 int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, int h_q,
                             int h_kv, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
                             void *hip_stream) {
-    DensePlan p;
-    int st = make_dense_plan(B, h_q, h_kv, d, l_kv, &p);
-    if (st != SAGA_OK) return st;
-    if (!Q || !K || !V || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
-        !aligned(O, 4))
-        return SAGA_ERR_INVALID_ARG;
-    if (!ws || !aligned(ws, kAlign)) return SAGA_ERR_INVALID_ARG;
-    if (ws_bytes < p.total) return SAGA_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)hip_stream;
-    DenseArgs a;
-    a.Q = (const uint16_t *)Q, a.K = (const uint16_t *)K, a.V = (const uint16_t *)V;
-    a.B = B, a.h_q = h_q, a.h_kv = h_kv;
-    a.n_chunk = p.n_chunk;
-    a.l_kv = l_kv, a.chunk_len = p.chunk_len;
-    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
-    a.partial = (float *)ws;
-    const int blocks = B * h_kv * p.n_chunk;
-#define SAGA_DENSE(DD, GG) \
-    hipLaunchKernelGGL((k_dense<DD, GG>), dim3(blocks), dim3(kThreads), 0, s, a)
-    if (d == 64) {
-        if (p.gmax <= 4) SAGA_DENSE(64, 4);
-        else if (p.gmax <= 8) SAGA_DENSE(64, 8);
-        else SAGA_DENSE(64, 16);
-    } else {
-        if (p.gmax <= 4) SAGA_DENSE(128, 4);
-        else if (p.gmax <= 8) SAGA_DENSE(128, 8);
-        else SAGA_DENSE(128, 16);
-    }
-#undef SAGA_DENSE
-    DenseMergeArgs m;
-    m.partial = (const float *)ws;
-    m.n_chunk = p.n_chunk;
-    m.O = O;
-    if (d == 64)
-        hipLaunchKernelGGL(k_dense_merge<64>, dim3(p.rows), dim3(kThreads), 0, s, m);
-    else
-        hipLaunchKernelGGL(k_dense_merge<128>, dim3(p.rows), dim3(kThreads), 0, s, m);
-    return launch_status();
+    return run_dense(Q, K, V, B, h_q, h_kv, h_kv, d, l_kv, O, ws, ws_bytes, hip_stream);
+}
+
+int saga_full_attention(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                        int h_v, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
+                        void *hip_stream) {
+    return run_dense(Q, K, V, B, h_q, h_k, h_v, d, l_kv, O, ws, ws_bytes, hip_stream);
 }
 
 int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k, int h_v, int d,

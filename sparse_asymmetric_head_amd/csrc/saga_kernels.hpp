@@ -1120,20 +1120,24 @@ __global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4 *p, int64_t
 
 struct DenseArgs {
     const uint16_t *Q, *K, *V;
-    int B, h_q, h_kv;
+    int B, h_q, h_k, h_v;  // K [B][h_k][l_kv][D], V [B][h_v][l_kv][D]
     int n_chunk;
+    int n_vsub;            // value-head subsets (of NV heads) per key head
     int64_t l_kv, chunk_len;
-    float scale_log2;  // log2(e) / sqrt(d)
-    float *partial;    // [rows][n_chunk][D + 4]: m (log2 units), l, -, -, o[D]
+    float scale_log2;      // log2(e) / sqrt(d)
+    float *partial;        // [rows][n_chunk][D + 4]: m (log2 units), l, -, -, o[D]
 };
 
-// Dense GQA split-KV decode: one workgroup per (b, kv head, chunk).  Scores
-// by MFMA as in k_select; online softmax in base 2 per wave; P*V on the VALU
-// (each lane owns 8 columns of a few rows of every tile).
-template <int D, int GMAX>
+// Dense split-KV decode with key head floor(j*h_k/h_q) and value head
+// floor(j*h_v/h_q): one workgroup per (b, key head, value-head subset,
+// chunk).  Scores by MFMA as in k_select; online softmax in base 2 per wave;
+// P*V on the VALU (each lane owns 8 columns of a few rows of every tile, of
+// each of the subset's NV value heads; a query head adds the rows of its own
+// value head, a wave-uniform choice).  NV = 1 is dense GQA (h_k = h_v).
+template <int D, int GMAX, int NV>
 __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     constexpr int KS = D / 32;
-    constexpr int U = SAGA_SELECT_U * 64 / D;
+    constexpr int U = NV == 1 ? SAGA_SELECT_U * 64 / D : 1;
     constexpr int LPR = D / 8;          // lanes per V row
     constexpr int RPI = 64 / LPR;       // V rows per wave load
     constexpr int RPL = 16 / RPI;       // V rows per lane per tile
@@ -1146,10 +1150,18 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 15, lq = lane >> 4;
     const int chunk = blockIdx.x % a.n_chunk;
-    const int bg = blockIdx.x / a.n_chunk;
-    const int b = bg / a.h_kv, g = bg % a.h_kv;
-    const int j_lo = group_lo(g, a.h_q, a.h_kv), j_hi = group_lo(g + 1, a.h_q, a.h_kv);
+    const int vsub = (blockIdx.x / a.n_chunk) % a.n_vsub;
+    const int bg = blockIdx.x / a.n_chunk / a.n_vsub;
+    const int b = bg / a.h_k, g = bg % a.h_k;
+    int j_lo = group_lo(g, a.h_q, a.h_k), j_hi = group_lo(g + 1, a.h_q, a.h_k);
+    // this block's value heads [v_lo, v_lo + NV) and their query heads
+    const int v_lo = (int)(((int64_t)j_lo * a.h_v) / a.h_q) + vsub * NV;
+    if (NV > 1 || a.n_vsub > 1) {
+        j_lo = max(j_lo, group_lo(v_lo, a.h_q, a.h_v));
+        j_hi = min(j_hi, group_lo(v_lo + NV, a.h_q, a.h_v));
+    }
     const int G = j_hi - j_lo;
+    if (G <= 0) return;  // whole block: a subset past the group's value heads
     const int64_t t_begin = (int64_t)chunk * a.chunk_len;
     const int64_t t_end = min(a.l_kv, t_begin + a.chunk_len);
     auto kcol = [](int lq, int s) { return s * 32 + lq * 8; };  // same d-axis map for Q and K
@@ -1174,13 +1186,22 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
         for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
 
     const uint16_t *Kb = a.K + (int64_t)bg * a.l_kv * D;
-    const uint16_t *Vb = a.V + (int64_t)bg * a.l_kv * D;
+    const uint16_t *Vb[NV];
+    int vix[GMAX];  // value head of each query head, within the subset
+#pragma unroll
+    for (int vi = 0; vi < NV; ++vi)
+        Vb[vi] = a.V + ((int64_t)b * a.h_v + min(v_lo + vi, a.h_v - 1)) * a.l_kv * D;
+    if constexpr (NV > 1) {
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+            vix[h] = (int)(((int64_t)(j_lo + h) * a.h_v) / a.h_q) - v_lo;
+    }
     const int vr = lane / LPR, vc = (lane % LPR) * 8;
     const int64_t last = t_end - 1;
 
     // K and V tiles of one wave iteration; rows past the chunk are clamped to
     // its last row (their scores are set to -inf, so they weigh nothing).
-    auto load_tiles = [&](u32x4 (&kr)[U][KS], u32x4 (&vv)[U][RPL], int64_t t0) {
+    auto load_tiles = [&](u32x4 (&kr)[U][KS], u32x4 (&vv)[U][RPL][NV], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int64_t row = t0 + u * 16 + ln;
@@ -1192,11 +1213,12 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
             for (int k = 0; k < RPL; ++k) {
                 int64_t vrow = t0 + u * 16 + vr + k * RPI;
                 vrow = vrow < last ? vrow : last;
-                vv[u][k] = ld_k(Vb + vrow * D + vc);
+#pragma unroll
+                for (int vi = 0; vi < NV; ++vi) vv[u][k][vi] = ld_k(Vb[vi] + vrow * D + vc);
             }
         }
     };
-    auto process = [&](const u32x4 (&kr)[U][KS], const u32x4 (&vv)[U][RPL], int64_t t0) {
+    auto process = [&](const u32x4 (&kr)[U][KS], const u32x4 (&vv)[U][RPL][NV], int64_t t0) {
         float sc[U][4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -1242,21 +1264,24 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int k = 0; k < RPL; ++k) {
-                float vf[8];
+            for (int k = 0; k < RPL; ++k)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    vf[2 * i] = bf_lo(vv[u][k][i]);
-                    vf[2 * i + 1] = bf_hi(vv[u][k][i]);
+                for (int vi = 0; vi < NV; ++vi) {
+                    float vf[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        vf[2 * i] = bf_lo(vv[u][k][vi][i]);
+                        vf[2 * i + 1] = bf_hi(vv[u][k][vi][i]);
+                    }
+                    const int rr = u * 16 + vr + k * RPI;
+#pragma unroll
+                    for (int h = 0; h < GMAX; ++h) {
+                        if (NV > 1 && vix[h] != vi) continue;  // uniform: another value head
+                        const float p = p_lds[wave][rr][h];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];
+                    }
                 }
-                const int rr = u * 16 + vr + k * RPI;
-#pragma unroll
-                for (int h = 0; h < GMAX; ++h) {
-                    const float p = p_lds[wave][rr][h];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];
-                }
-            }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
     };
@@ -1264,10 +1289,10 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     constexpr int64_t kStride = kWaves * 16 * U;
     int64_t t0 = t_begin + wave * 16 * U;
     if (t0 < t_end) {
-        u32x4 ka[U][KS], va[U][RPL];
+        u32x4 ka[U][KS], va[U][RPL][NV];
         load_tiles(ka, va, t0);
         if constexpr (kPingPong) {
-            u32x4 kb[U][KS], vb[U][RPL];
+            u32x4 kb[U][KS], vb[U][RPL][NV];
             for (;;) {
                 load_tiles(kb, vb, t0 + kStride);
                 process(ka, va, t0);

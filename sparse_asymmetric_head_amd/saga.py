@@ -26,7 +26,8 @@ EXPORTS = (
     "saga_status_string", "saga_version", "saga_workspace_bytes", "saga_dense_workspace_bytes",
     "saga_workspace_init", "saga_refresh_threshold", "saga_decode_step",
     "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
-    "saga_attend", "saga_read_probe", "saga_decode_step_pivot",
+    "saga_attend", "saga_read_probe", "saga_decode_step_pivot", "saga_full_attention",
+    "saga_full_attention_workspace_bytes",
 )
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
@@ -94,6 +95,10 @@ def lib(path: str | None = None):
     L.saga_workspace_layout.restype = i32
     L.saga_selection_mask.argtypes = [vp, sz, i32, i32, i32, i32, i32, i64, i64, vp, vp]
     L.saga_selection_mask.restype = i32
+    L.saga_full_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i64]
+    L.saga_full_attention_workspace_bytes.restype = sz
+    L.saga_full_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, sz, vp]
+    L.saga_full_attention.restype = i32
     L.saga_read_probe.argtypes = [vp, i64, vp, vp]
     L.saga_read_probe.restype = i32
     if path is None:
@@ -234,6 +239,20 @@ def saga_selection_mask(ws, B, h_q, h_k, h_v, d, l_kv, N, mask, stream=None) -> 
     _check(lib().saga_selection_mask(_ptr(ws), ws.numel(), B, h_q, h_k, h_v, d, l_kv, int(N),
                                      _ptr(mask), _stream(stream)),
            "saga_selection_mask")
+
+
+def saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv) -> int:
+    return int(lib().saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv))
+
+
+def saga_full_attention(Q, K, V, O, ws, stream=None) -> None:
+    """Dense attention with decoupled heads: key head floor(j*h_k/h_q), value
+    head floor(j*h_v/h_q); Q [B][h_q][d], K [B][h_k][l_kv][d], V [B][h_v][l_kv][d]."""
+    B, h_q, d = _dims(Q, K, V)
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    _check(lib().saga_full_attention(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
+                                     _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
+           "saga_full_attention")
 
 
 def saga_read_probe(buf, sink, stream=None) -> None:

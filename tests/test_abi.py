@@ -105,6 +105,12 @@ def test_invalid_shapes_rejected(L):
     assert f(1, 4, 1, 2, 128, 1 << 23, 64) == 0   # cache rows beyond 2^31 bytes
     assert L.saga_dense_workspace_bytes(1, 32, 8, 64, 4096) > 0
     assert L.saga_dense_workspace_bytes(1, 32, 1, 64, 4096) == 0  # group of 32 > 16
+    fw = L.saga_full_attention_workspace_bytes
+    assert fw(1, 32, 4, 16, 64, 4096) > 0
+    assert fw(1, 32, 2, 32, 128, 4096) > 0       # sixteen value heads per key head
+    assert fw(1, 32, 8, 4, 64, 4096) == 0        # h_k > h_v
+    assert fw(1, 64, 1, 1, 64, 4096) == 0        # 64 query heads in one block
+    assert fw(1, 32, 4, 16, 96, 4096) == 0       # d unsupported
 
 
 def test_entry_points_validate_before_launch(L):
@@ -153,6 +159,12 @@ def test_entry_points_validate_before_launch(L):
     assert dp(*bad) == saga.SAGA_ERR_INVALID_ARG
     bad = list(pargs); bad[16] = need - 256
     assert dp(*bad) == saga.SAGA_ERR_WORKSPACE
+    fa = L.saga_full_attention
+    fneed = L.saga_full_attention_workspace_bytes(1, 32, 4, 16, 64, 4096)
+    assert fa(fake, fake, None, 1, 32, 4, 16, 64, 4096, fake, fake, fneed, None) == \
+        saga.SAGA_ERR_INVALID_ARG
+    assert fa(fake, fake, fake, 1, 32, 4, 16, 64, 4096, fake, fake, fneed - 256, None) == \
+        saga.SAGA_ERR_WORKSPACE
     rp = L.saga_read_probe
     assert rp(None, 1024, fake, None) == saga.SAGA_ERR_INVALID_ARG
     assert rp(fake, 1024, None, None) == saga.SAGA_ERR_INVALID_ARG

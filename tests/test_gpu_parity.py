@@ -257,6 +257,49 @@ def test_dense_gqa_small(case):
     assert rel_err(O, ref) <= OUT_RTOL
 
 
+FULL = [
+    # B, h_q, h_k, h_v, d, l_kv
+    (1, 32, 4, 16, 64, 3000),    # Llama-like: four value heads per key head
+    (2, 12, 1, 4, 128, 2500),    # Qwen-like
+    (1, 32, 2, 32, 128, 1500),   # sixteen value heads per key head: four subsets
+    (2, 6, 4, 5, 64, 1001),      # non-integer head ratios, ragged tail
+    (1, 8, 2, 2, 64, 700),       # h_k = h_v: dense GQA
+    (1, 8, 2, 4, 64, 1234),      # two value heads per key head
+]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[str(c) for c in FULL])
+def test_full_attention_small(case):
+    """SAGA full attention (decoupled heads, no sparsity) against the oracle
+    with every position selected."""
+    B, h_q, h_k, h_v, d, l_kv = case
+    x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=hash(case) % 7919, device="cuda",
+                       planted=8)
+    ws = torch.empty(saga.saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty(B, h_q, d, dtype=torch.float32, device="cuda")
+    saga.saga_full_attention(x["Q"][0], x["K"], x["V"], O, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.given_mask(bits(x["Q"][0]), bits(x["K"]), bits(x["V"]), h_k, h_v,
+                               np.ones((B, h_q, l_kv), np.uint8))
+    assert rel_err(O.cpu().numpy().astype(np.float64), ref) <= OUT_RTOL
+
+
+def test_full_attention_llama_128k():
+    """SAGA full attention at the 128K Llama shape against the oracle."""
+    cfg = wl.CONFIGS[2]
+    x = wl.make_layer(cfg, 0, device="cuda", steps=1)
+    B, h_q, h_k, h_v, d, l_kv = cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv
+    ws = torch.empty(saga.saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty(B, h_q, d, dtype=torch.float32, device="cuda")
+    saga.saga_full_attention(x["Q"][0], x["K"], x["V"], O, ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.given_mask(bits(x["Q"][0]), bits(x["K"]), bits(x["V"]), h_k, h_v,
+                               np.ones((B, h_q, l_kv), np.uint8))
+    assert rel_err(O.cpu().numpy().astype(np.float64), ref) <= OUT_RTOL
+
+
 @pytest.mark.parametrize("ci", [1, 2, 3])
 def test_dense_gqa_full_size(ci):
     cfg = wl.CONFIGS[ci]
