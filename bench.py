@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama32-1b-128k-16L")
+    ap.add_argument("--l-kv", type=int, default=0, help="override the workload's context length")
+    ap.add_argument("--R", type=int, default=0, help="override the workload's refresh period")
+    ap.add_argument("--N", type=int, default=0, help="override the workload's N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
@@ -145,6 +148,9 @@ def main() -> int:
         print(f"unknown config {args.config}", file=sys.stderr)
         return 2
     ci = wl.config_index(cfg)
+    over = {k: v for k, v in (("l_kv", args.l_kv), ("R", args.R), ("N", args.N)) if v > 0}
+    if over:  # the same seeded recipe at another size or refresh period (a sweep point)
+        cfg = cfg.with_(**over)
     B, h_q, h_k, h_v, d, l_kv, N, R, T, L = (cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv,
                                               cfg.N, cfg.R, cfg.steps, cfg.layers)
     dev = torch.device("cuda:0")
@@ -465,7 +471,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "h_q": h_q, "h_k": h_k, "h_v": h_v, "d": d,
+        "config": {"workload": cfg.name + "".join(f" {k}={v}" for k, v in over.items()),
+                   "B": B, "h_q": h_q, "h_k": h_k, "h_v": h_v, "d": d,
                    "l_kv": l_kv, "N": N, "R": R, "layers": L, "global_batch": B,
                    "seq_len": l_kv, "parallelism": "single-gpu"},
         "hbm_gbps": round(step_alg / (us_per_step * 1e-6) / 1e9, 1),
