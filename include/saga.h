@@ -150,6 +150,31 @@ int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, 
                             void *hip_stream);
 
 /*
+ * A growing context: caches with room for cap rows per head, K bf16
+ * [B][h_k][cap][d] and V bf16 [B][h_v][cap][d], of which the first len rows
+ * hold the context (the decode step just before the method's: each new
+ * token's key and value rows are appended, and the new key is compared with
+ * the stale tau like every other position; Methodology > Atop-N Attention,
+ * item 2).
+ *
+ * saga_append_kv: K[b][g][pos] := k_new[b][g], V[b][v][pos] := v_new[b][v]
+ *   (k_new bf16 [B][h_k][d], v_new bf16 [B][h_v][d]); 0 <= pos < cap.
+ * saga_decode_step_cache: saga_decode_step_pivot over the first len rows
+ *   (N <= len <= cap).  ws: saga_cache_workspace_bytes(.., cap, N) bytes,
+ *   valid for every len <= cap.  The pivot rows are positions in the record
+ *   order of the chunking for len; when growth changes the chunking (about
+ *   every 64 * 256 / (B * h_k) rows) the next refresh from the pivot lists
+ *   every position: exact, slower.
+ */
+size_t saga_cache_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t cap, int64_t N);
+int saga_append_kv(void *K, void *V, const void *k_new, const void *v_new, int B, int h_k,
+                   int h_v, int d, int64_t cap, int64_t pos, void *hip_stream);
+int saga_decode_step_cache(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                           int h_v, int d, int64_t cap, int64_t len, int64_t N, float *tau,
+                           int32_t *pivot, int refresh, float *O, int32_t *counts, void *ws,
+                           size_t ws_bytes, void *hip_stream);
+
+/*
  * SAGA full attention: the decoupled heads without the sparsity, softmax
  * over every cache position (SAGA Architecture; eqs. 2-4 with key head
  * floor(j*h_k/h_q) and value head floor(j*h_v/h_q)):

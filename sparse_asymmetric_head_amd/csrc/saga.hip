@@ -40,6 +40,7 @@ struct Plan {
     int n_chunk, n_sub;
     int64_t sub_cap;
     int64_t ld_a;
+    int64_t ld_kv;  // rows per head in the K and V caches (>= l_kv)
     int hist_bpr;
     // byte offsets into the workspace
     size_t off_hist, off_state, off_pi, counters_end;
@@ -60,21 +61,33 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
     return SAGA_OK;
 }
 
-int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, Plan *p) {
-    int st = check_shape(B, h_q, h_k, h_v, d, l_kv, N);
-    if (st != SAGA_OK) return st;
-    memset(p, 0, sizeof *p);
-    p->B = B, p->h_q = h_q, p->h_k = h_k, p->h_v = h_v, p->d = d, p->l_kv = l_kv, p->N = N;
-    p->rows = B * h_q;
-    p->gmax = (int)ceil_div(h_q, h_k);
-    p->nt = p->gmax <= 16 ? 1 : (p->gmax <= 32 ? 2 : 4);
-    // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
-    // pairs, and at most kMaxSub/kWaves chunks per row.
-    const int64_t pairs = (int64_t)B * h_k;
+// Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
+// pairs, and at most kMaxSub/kWaves chunks per row (non-decreasing in l_kv).
+int64_t chunk_len_for(int64_t pairs, int64_t l_kv) {
     int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), kChunkUnit) * kChunkUnit;
     const int64_t cl_min = ceil_div(ceil_div(l_kv, kMaxSub / kWaves), kChunkUnit) * kChunkUnit;
     if (cl < cl_min) cl = cl_min;
     if (cl < kChunkUnit) cl = kChunkUnit;
+    return cl;
+}
+
+// cap > 0: a cache with room for cap rows per head, of which l_kv are in use;
+// the workspace regions are then sized for any length up to cap (records:
+// n_chunk * chunk_len < l_kv + chunk_len <= cap + chunk_len(cap)), so one
+// workspace serves the whole growth.
+int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, Plan *p,
+              int64_t cap = 0) {
+    int st = check_shape(B, h_q, h_k, h_v, d, cap > 0 ? cap : l_kv, N);
+    if (st != SAGA_OK) return st;
+    if (cap > 0 && (l_kv < 1 || l_kv > cap || N > l_kv)) return SAGA_ERR_INVALID_ARG;
+    memset(p, 0, sizeof *p);
+    p->B = B, p->h_q = h_q, p->h_k = h_k, p->h_v = h_v, p->d = d, p->l_kv = l_kv, p->N = N;
+    p->ld_kv = cap > 0 ? cap : l_kv;
+    p->rows = B * h_q;
+    p->gmax = (int)ceil_div(h_q, h_k);
+    p->nt = p->gmax <= 16 ? 1 : (p->gmax <= 32 ? 2 : 4);
+    const int64_t pairs = (int64_t)B * h_k;
+    const int64_t cl = chunk_len_for(pairs, l_kv);
     p->chunk_len = cl;
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->n_sub = p->n_chunk * kWaves;
@@ -94,11 +107,19 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     p->counters_end = o;
     p->seg_w = seg_words(p->sub_cap);
     p->off_seg = o;
-    o = align_up(o + rows * (size_t)p->n_sub * (size_t)p->seg_w * sizeof(int32_t));
+    size_t seg_bytes = rows * (size_t)p->n_sub * (size_t)p->seg_w * sizeof(int32_t);
+    int64_t ld_a_max = p->ld_a, cand_len = l_kv;
+    if (cap > 0) {
+        const int64_t ccap = chunk_len_for(pairs, cap);
+        seg_bytes = rows * (size_t)(2 * (cap + ccap) + 17 * (int64_t)kMaxSub) * sizeof(int32_t);
+        ld_a_max = ceil_div(cap, 64) * 64;
+        cand_len = cap;
+    }
+    o = align_up(o + seg_bytes);
     p->off_scores = o;
-    o = align_up(o + rows * (size_t)p->ld_a * sizeof(float));
+    o = align_up(o + rows * (size_t)ld_a_max * sizeof(float));
     p->off_cand = o;
-    o = align_up(o + rows * (size_t)l_kv * sizeof(uint32_t));
+    o = align_up(o + rows * (size_t)cand_len * sizeof(uint32_t));
     p->total = o;
     return SAGA_OK;
 }
@@ -205,6 +226,7 @@ SelectArgs select_args(const Plan &p, const void *Q, const void *K, const float 
     a.tau = tau;
     a.A = (float *)(ws + p.off_scores);
     a.ld_a = p.ld_a;
+    a.ld_kv = p.ld_kv;
     a.B = p.B, a.h_q = p.h_q, a.h_k = p.h_k;
     a.n_chunk = p.n_chunk;
     a.l_kv = p.l_kv, a.chunk_len = p.chunk_len;
@@ -247,6 +269,7 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.V = (const uint16_t *)V;
     aa.B = p.B, aa.h_q = p.h_q, aa.h_v = p.h_v;
     aa.l_kv = p.l_kv;
+    aa.ld_kv = p.ld_kv;
     aa.O = O;
     aa.counts = counts;
     if (p.d == 64)
@@ -301,7 +324,7 @@ int run_pivot_refresh(const Plan &p, const void *Q, const void *K, float *tau, i
     PivotArgs pa;
     pa.Q = (const uint16_t *)Q, pa.K = (const uint16_t *)K;
     pa.B = p.B, pa.h_q = p.h_q, pa.h_k = p.h_k;
-    pa.l_kv = p.l_kv, pa.N = p.N, pa.chunk_len = p.chunk_len, pa.grp = p.grp;
+    pa.l_kv = p.l_kv, pa.ld_kv = p.ld_kv, pa.N = p.N, pa.chunk_len = p.chunk_len, pa.grp = p.grp;
     pa.scale = (float)(1.0 / sqrt((double)p.d));
     pa.pivot = pivot;
     pa.pi = (float *)(w + p.off_pi);
@@ -487,13 +510,15 @@ int saga_decode_step(const void *Q, const void *K, const void *V, int B, int h_q
     return run_attend(p, V, O, counts, w, s);
 }
 
-int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
-                           int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
-                           int refresh, float *O, int32_t *counts, void *ws, size_t ws_bytes,
-                           void *hip_stream) {
-    Plan p;
-    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
-    if (st != SAGA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// saga_decode_step_pivot / saga_decode_step_cache on a plan.
+int decode_pivot(const Plan &p, const void *Q, const void *K, const void *V, float *tau,
+                 int32_t *pivot, int refresh, float *O, int32_t *counts, void *ws,
+                 size_t ws_bytes, void *hip_stream) {
+    int st;
     if (!Q || !K || !V || !tau || !O || !aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) ||
         !aligned(tau, 4) || !aligned(O, 4) || (counts && !aligned(counts, 4)))
         return SAGA_ERR_INVALID_ARG;
@@ -513,6 +538,56 @@ int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, i
     }
     if (st != SAGA_OK) return st;
     return run_attend(p, V, O, counts, w, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int saga_decode_step_pivot(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                           int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
+                           int refresh, float *O, int32_t *counts, void *ws, size_t ws_bytes,
+                           void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    return decode_pivot(p, Q, K, V, tau, pivot, refresh, O, counts, ws, ws_bytes, hip_stream);
+}
+
+size_t saga_cache_workspace_bytes(int B, int h_q, int h_k, int h_v, int d, int64_t cap,
+                                  int64_t N) {
+    Plan p;
+    return make_plan(B, h_q, h_k, h_v, d, cap, N, &p, cap) == SAGA_OK ? p.total : 0;
+}
+
+int saga_decode_step_cache(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                           int h_v, int d, int64_t cap, int64_t len, int64_t N, float *tau,
+                           int32_t *pivot, int refresh, float *O, int32_t *counts, void *ws,
+                           size_t ws_bytes, void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, len, N, &p, cap);
+    if (st != SAGA_OK) return st;
+    return decode_pivot(p, Q, K, V, tau, pivot, refresh, O, counts, ws, ws_bytes, hip_stream);
+}
+
+int saga_append_kv(void *K, void *V, const void *k_new, const void *v_new, int B, int h_k,
+                   int h_v, int d, int64_t cap, int64_t pos, void *hip_stream) {
+    if (B < 1 || h_k < 1 || h_v < h_k || cap < 1 || pos < 0 || pos >= cap)
+        return SAGA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
+    if (cap * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
+    if (!K || !V || !k_new || !v_new || !aligned(K, 16) || !aligned(V, 16) ||
+        !aligned(k_new, 16) || !aligned(v_new, 16))
+        return SAGA_ERR_INVALID_ARG;
+    AppendArgs a;
+    a.K = (uint16_t *)K, a.V = (uint16_t *)V;
+    a.k_new = (const uint16_t *)k_new, a.v_new = (const uint16_t *)v_new;
+    a.B = B, a.h_k = h_k, a.h_v = h_v, a.d = d;
+    a.ld_kv = cap, a.pos = pos;
+    const int64_t pieces = (int64_t)B * (h_k + h_v) * (d / 8);
+    const int blocks = (int)std::min<int64_t>(ceil_div(pieces, kThreads), 1024);
+    hipLaunchKernelGGL(k_append, dim3(blocks), dim3(kThreads), 0, (hipStream_t)hip_stream, a);
+    return launch_status();
 }
 
 int saga_dense_gqa_baseline(const void *Q, const void *K, const void *V, int B, int h_q,

@@ -91,6 +91,7 @@ struct SelectArgs {
     const float *tau;    // [B*h_q]            (compare mode)
     float *A;            // [B*h_q][ld_a]      (materialize mode)
     int64_t ld_a;
+    int64_t ld_kv;       // rows per key head in K (>= l_kv: a cache with room to grow)
     int B, h_q, h_k;
     int n_chunk;
     int64_t l_kv, chunk_len;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     const int sub = chunk * kWaves + wave;
     const uint64_t head_mask = 0x0001000100010001ull << ln;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
-    const uint16_t *Kb = a.K + (int64_t)bg * a.l_kv * D;
+    const uint16_t *Kb = a.K + (int64_t)bg * a.ld_kv * D;
 
     auto flush = [&]() {
 #pragma unroll
@@ -341,9 +342,9 @@ struct AttendArgs {
     const int32_t *seg;  // [rows][n_sub][seg_w] records
     int n_sub;
     int64_t seg_w;
-    const uint16_t *V;   // bf16 [B][h_v][l_kv][D]
+    const uint16_t *V;   // bf16 [B][h_v][ld_kv][D], rows < l_kv valid
     int B, h_q, h_v;
-    int64_t l_kv;
+    int64_t l_kv, ld_kv;
     float *O;            // [rows][D]
     int32_t *counts;     // [rows] or null
 };
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
     const int h = lane & 1;
     const int e_in = lane / LPE, cl = lane % LPE;
-    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.l_kv * D + csl * DC + cl * 8;
+    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + csl * DC + cl * 8;
     int *lt = wlt[wave];
     float *ls = wls[wave];
 
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
 struct PivotArgs {
     const uint16_t *Q, *K;
     int B, h_q, h_k;
-    int64_t l_kv, N, chunk_len, grp;
+    int64_t l_kv, ld_kv, N, chunk_len, grp;
     float scale;
     const int32_t *pivot;  // [rows][N]: positions with increasing record_order_key, else unusable
     float *pi;             // [rows] out: the lower bound (-inf when P is unusable)
@@ -825,7 +826,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
             qf[c * 8 + 2 * i + 1] = bf_hi(v[i]);
         }
     }
-    const uint16_t *Kg = a.K + ((int64_t)b * a.h_k + g) * a.l_kv * D;
+    const uint16_t *Kg = a.K + ((int64_t)b * a.h_k + g) * a.ld_kv * D;
     const int32_t *P = a.pivot + (int64_t)row * a.N;
     float mn = INFINITY;
     int bad = 0;
@@ -1078,6 +1079,31 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
             }
             if (lane == 0) rb[(int64_t)sgi * a.seg_w] = kept;
         }
+    }
+}
+
+// ------------------------------------------------------------------ cache append
+
+struct AppendArgs {
+    uint16_t *K, *V;               // [B][h_k][ld_kv][D], [B][h_v][ld_kv][D]
+    const uint16_t *k_new, *v_new; // [B][h_k][D], [B][h_v][D]
+    int B, h_k, h_v, d;
+    int64_t ld_kv, pos;
+};
+
+// Write the new token's key and value rows at cache position pos: one lane
+// per 16 bytes.
+__global__ __launch_bounds__(kThreads) void k_append(AppendArgs a) {
+    const int per = a.d / 8;  // 16-byte pieces per row
+    const int64_t nk = (int64_t)a.B * a.h_k * per, nv = (int64_t)a.B * a.h_v * per;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nk + nv;
+         i += (int64_t)gridDim.x * kThreads) {
+        const bool isk = i < nk;
+        const int64_t x = isk ? i : i - nk;
+        const int64_t head = x / per, c = x % per;  // head = b * h + g
+        const uint16_t *src = (isk ? a.k_new : a.v_new) + head * a.d + c * 8;
+        uint16_t *dst = (isk ? a.K : a.V) + (head * a.ld_kv + a.pos) * a.d + c * 8;
+        *(u32x4 *)dst = ld16(src);
     }
 }
 

@@ -27,7 +27,8 @@ EXPORTS = (
     "saga_workspace_init", "saga_refresh_threshold", "saga_decode_step",
     "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
     "saga_attend", "saga_read_probe", "saga_decode_step_pivot", "saga_full_attention",
-    "saga_full_attention_workspace_bytes",
+    "saga_full_attention_workspace_bytes", "saga_cache_workspace_bytes", "saga_append_kv",
+    "saga_decode_step_cache",
 )
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
@@ -99,6 +100,13 @@ def lib(path: str | None = None):
     L.saga_full_attention_workspace_bytes.restype = sz
     L.saga_full_attention.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, sz, vp]
     L.saga_full_attention.restype = i32
+    L.saga_cache_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i64, i64]
+    L.saga_cache_workspace_bytes.restype = sz
+    L.saga_append_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, vp]
+    L.saga_append_kv.restype = i32
+    L.saga_decode_step_cache.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, i64, vp,
+                                         vp, i32, vp, vp, vp, sz, vp]
+    L.saga_decode_step_cache.restype = i32
     L.saga_read_probe.argtypes = [vp, i64, vp, vp]
     L.saga_read_probe.restype = i32
     if path is None:
@@ -253,6 +261,35 @@ def saga_full_attention(Q, K, V, O, ws, stream=None) -> None:
     _check(lib().saga_full_attention(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
                                      _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_full_attention")
+
+
+def saga_cache_workspace_bytes(B, h_q, h_k, h_v, d, cap, N) -> int:
+    return int(lib().saga_cache_workspace_bytes(B, h_q, h_k, h_v, d, cap, int(N)))
+
+
+def saga_append_kv(K, V, k_new, v_new, pos: int, stream=None) -> None:
+    """K [B][h_k][cap][d], V [B][h_v][cap][d]; k_new [B][h_k][d], v_new [B][h_v][d] (bf16)."""
+    B, h_k, cap, d = K.shape
+    h_v = V.shape[1]
+    for t in (K, V, k_new, v_new):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError("caches and new rows must be contiguous bfloat16")
+    _check(lib().saga_append_kv(_ptr(K), _ptr(V), _ptr(k_new), _ptr(v_new), B, h_k, h_v, d, cap,
+                                int(pos), _stream(stream)), "saga_append_kv")
+
+
+def saga_decode_step_cache(Q, K, V, length: int, N: int, tau, pivot, refresh: int, O,
+                           counts=None, ws=None, stream=None) -> None:
+    """saga_decode_step_pivot over the first `length` rows of caches with room for
+    K.shape[2] rows per head."""
+    B, h_q, d = _dims(Q, K, V)
+    h_k, cap, h_v = K.shape[1], K.shape[2], V.shape[1]
+    if ws is None:
+        raise ValueError("a workspace is required (alloc_workspace)")
+    _check(lib().saga_decode_step_cache(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, cap,
+                                        int(length), int(N), _ptr(tau), _ptr(pivot), int(refresh),
+                                        _ptr(O), _ptr(counts), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "saga_decode_step_cache")
 
 
 def saga_read_probe(buf, sink, stream=None) -> None:

@@ -66,6 +66,18 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("shape", SHAPES)
+def test_cache_workspace_covers_every_length(L, shape):
+    """One cache workspace serves every length up to the capacity: no
+    length's own layout needs more (checked on a grid of lengths)."""
+    B, h_q, h_k, h_v, d, l_kv, N = shape
+    cap = l_kv
+    have = L.saga_cache_workspace_bytes(B, h_q, h_k, h_v, d, cap, N)
+    assert have > 0
+    for ln in sorted(set([N, cap] + [max(N, cap * i // 37) for i in range(1, 37)])):
+        assert L.saga_workspace_bytes(B, h_q, h_k, h_v, d, ln, N) <= have, ln
+
+
+@pytest.mark.parametrize("shape", SHAPES)
 def test_workspace_layout_consistent(L, shape):
     from sparse_asymmetric_head_amd import saga
 
@@ -165,6 +177,22 @@ def test_entry_points_validate_before_launch(L):
         saga.SAGA_ERR_INVALID_ARG
     assert fa(fake, fake, fake, 1, 32, 4, 16, 64, 4096, fake, fake, fneed - 256, None) == \
         saga.SAGA_ERR_WORKSPACE
+    cw = L.saga_cache_workspace_bytes
+    assert cw(1, 32, 4, 16, 64, 8192, 256) >= L.saga_workspace_bytes(1, 32, 4, 16, 64, 8192, 256)
+    cneed = cw(1, 32, 4, 16, 64, 8192, 256)
+    dc = L.saga_decode_step_cache
+    cargs = [fake, fake, fake, 1, 32, 4, 16, 64, 8192, 4000, 256, fake, fake, 0, fake, None, fake,
+             cneed, None]
+    bad = list(cargs); bad[9] = 8193              # len > cap
+    assert dc(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(cargs); bad[10] = 4001             # N > len
+    assert dc(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(cargs); bad[17] = cneed - 256
+    assert dc(*bad) == saga.SAGA_ERR_WORKSPACE
+    ap = L.saga_append_kv
+    assert ap(fake, fake, fake, fake, 1, 4, 16, 64, 8192, 8192, None) == saga.SAGA_ERR_INVALID_ARG
+    assert ap(fake, fake, fake, mis, 1, 4, 16, 64, 8192, 10, None) == saga.SAGA_ERR_INVALID_ARG
+    assert ap(fake, fake, fake, fake, 1, 4, 16, 80, 8192, 10, None) == saga.SAGA_ERR_UNSUPPORTED
     rp = L.saga_read_probe
     assert rp(None, 1024, fake, None) == saga.SAGA_ERR_INVALID_ARG
     assert rp(fake, 1024, None, None) == saga.SAGA_ERR_INVALID_ARG

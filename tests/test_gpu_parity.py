@@ -548,3 +548,52 @@ def test_pivot_refresh_with_unusable_pivot_is_exact():
             assert np.array_equal(ma, mb) and torch.equal(ca, cb) and torch.equal(Oa, Ob)
             keys = record_order_keys(pv.cpu().numpy(), ws_layout(B, h_q, h_k, h_v, d, l_kv, N))
             assert (np.diff(keys, axis=-1) > 0).all()
+
+
+CACHE_CASES = [
+    # B, h_q, h_k, h_v, d, l0, T, N, R
+    (1, 8, 2, 4, 64, 5000, 12, 64, 4),
+    (1, 8, 2, 4, 64, 32760, 12, 128, 3),   # the chunking changes at 32768 positions
+    (2, 12, 1, 4, 128, 3001, 9, 50, 4),
+]
+
+
+@pytest.mark.parametrize("case", CACHE_CASES, ids=[str(c) for c in CACHE_CASES])
+def test_growing_context_matches_contiguous(case):
+    """KV append + decode over a growing prefix of caches with spare room: each
+    step equals the contiguous path on a copy of the prefix (tau, counts and O
+    bit for bit; the cache path refreshes from the pivot), so the new key is
+    compared with the stale tau like every other position."""
+    B, h_q, h_k, h_v, d, l0, T, N, R = case
+    cap = l0 + T
+    x = wl.make_random(B, h_q, h_k, h_v, d, cap, seed=cap % 1013, device="cuda", steps=T,
+                       planted=16)
+    Kf, Vf, Q = x["K"], x["V"], x["Q"]
+    K = torch.zeros_like(Kf)
+    V = torch.zeros_like(Vf)
+    K[:, :, :l0] = Kf[:, :, :l0]
+    V[:, :, :l0] = Vf[:, :, :l0]
+    ws_c = saga.alloc_workspace(saga.saga_cache_workspace_bytes(B, h_q, h_k, h_v, d, cap, N))
+    tau_c = torch.zeros(B, h_q, device="cuda")
+    tau_r = torch.zeros(B, h_q, device="cuda")
+    piv = torch.full((B, h_q, N), -1, dtype=torch.int32, device="cuda")
+    for t in range(T):
+        pos = l0 + t
+        saga.saga_append_kv(K, V, Kf[:, :, pos].contiguous(), Vf[:, :, pos].contiguous(), pos)
+        length = pos + 1
+        ref = t % R == 0
+        mode = 0 if not ref else (1 if t == 0 else 2)
+        O_c = torch.empty(B, h_q, d, device="cuda")
+        c_c = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+        saga.saga_decode_step_cache(Q[t], K, V, length, N, tau_c, piv, mode, O_c, c_c, ws_c)
+        Kp, Vp = Kf[:, :, :length].contiguous(), Vf[:, :, :length].contiguous()
+        O_r, c_r, ws_r = _step(Q[t], Kp, Vp, N, tau_r, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(tau_c.view(torch.int32), tau_r.view(torch.int32)), f"tau at step {t}"
+        assert torch.equal(c_c, c_r), f"counts at step {t}"
+        assert torch.equal(O_c, O_r), f"outputs at step {t}"
+    assert torch.equal(K, Kf) and torch.equal(V, Vf)
+    m = read_mask(ws_r, (B, h_q, h_k, h_v, d, cap), N)
+    Og, cg = oracle.given_mask(bits(Q[T - 1]), bits(Kf), bits(Vf), h_k, h_v, m)
+    assert np.array_equal(cg, c_c.cpu().numpy())
+    assert rel_err(O_c.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
