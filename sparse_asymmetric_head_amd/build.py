@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "saga.hip")
+SRCS = [os.path.join(HERE, "csrc", "saga.hip"), os.path.join(HERE, "csrc", "merge.hip")]
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libsaga.so")
 ARCH = "gfx950"
@@ -39,7 +39,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra or []) + [SRC, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra or []) + SRCS + ["-o", tmp]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,230 @@
+// merge.hip -- host side of the GQA -> SAGA key-head merge (C ABI in include/saga_merge.h).
+//
+// Launch sequence on one stream:
+//   k_kproj          K = X W_K^T                                  (n/128 x h_kt*d/128 blocks)
+//   k_gram<D>        per-chunk second moments: S_r (h_kt items) and G_p of K_a - K_b (pairs)
+//   k_gram_reduce    fixed-order fp64 sum over chunks
+//   k_pair_eig<D>    eigenpairs of S_a + S_b                      (one block per pair)
+//   k_pair_loss<D>   S^+, P_a, P_b and the eq. 13 cost            (one block per pair)
+//   k_match          minimum-weight perfect matching              (one block)
+//   k_merged_weight  eq. 15 in the weight layout                  (h_kt/2 x d_model/256 blocks)
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/saga_merge.h"
+#include "merge_kernels.hpp"
+
+namespace {
+
+using namespace saga::merge;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kTargetGramBlocks = 1024;   // about four blocks per compute unit
+constexpr int64_t kMinChunkTokens = 64;
+
+struct MergePlan {
+    int64_t n;
+    int h_q, h_kt, d, dm, P, items, n_chunk;
+    int64_t chunk_tokens;
+    size_t off_K, off_part, off_SG, off_V, off_lam, off_Sp, off_Pm, off_dp, off_choice, bytes;
+};
+
+int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan *p) {
+    if (n < 1 || h_q < 1 || h_kt < 1 || d < 1 || d_model < 1) return SAGA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
+    if (h_kt % 2 || h_kt < 2 || h_kt > kMaxHeads) return SAGA_ERR_UNSUPPORTED;
+    if (h_q < h_kt || h_q > 1024) return SAGA_ERR_UNSUPPORTED;
+    if (d_model % 64 || d_model < 64 || d_model > 32768) return SAGA_ERR_UNSUPPORTED;
+    if (n > ((int64_t)1 << 26)) return SAGA_ERR_UNSUPPORTED;
+    p->n = n;
+    p->h_q = h_q;
+    p->h_kt = h_kt;
+    p->d = d;
+    p->dm = d_model;
+    p->P = h_kt * (h_kt - 1) / 2;
+    p->items = h_kt + p->P;
+    int64_t nc = ceil_div(kTargetGramBlocks, p->items);
+    const int64_t max_nc = ceil_div(n, kMinChunkTokens);
+    nc = nc < max_nc ? nc : max_nc;
+    nc = nc < 1 ? 1 : nc;
+    p->chunk_tokens = ceil_div(n, nc);
+    p->n_chunk = (int)ceil_div(n, p->chunk_tokens);
+    const size_t dd = (size_t)d * d * sizeof(float);
+    size_t o = 0;
+    p->off_K = o;      o = align_up(o + (size_t)n * h_kt * d * sizeof(float));
+    p->off_part = o;   o = align_up(o + (size_t)p->items * p->n_chunk * dd);
+    p->off_SG = o;     o = align_up(o + (size_t)p->items * dd);
+    p->off_V = o;      o = align_up(o + (size_t)p->P * dd);
+    p->off_lam = o;    o = align_up(o + (size_t)p->P * d * sizeof(float));
+    p->off_Sp = o;     o = align_up(o + (size_t)p->P * dd);
+    p->off_Pm = o;     o = align_up(o + (size_t)p->P * 2 * dd);
+    p->off_dp = o;     o = align_up(o + ((size_t)1 << h_kt) * sizeof(double));
+    p->off_choice = o; o = align_up(o + ((size_t)1 << h_kt));
+    p->bytes = o;
+    return SAGA_OK;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+void pair_table(int h_kt, uint8_t *pa, uint8_t *pb) {
+    int p = 0;
+    for (int a = 0; a < h_kt; ++a)
+        for (int b = a + 1; b < h_kt; ++b, ++p) {
+            pa[p] = (uint8_t)a;
+            pb[p] = (uint8_t)b;
+        }
+}
+
+size_t eig_lds_bytes(int d) {
+    return (size_t)2 * d * (d + 1) * sizeof(float) + (size_t)(d / 2) * 16 + 4 + 16;
+}
+size_t weight_lds_bytes(int d) { return (size_t)2 * d * d * sizeof(float); }
+
+// Kernels that take more than 64 KB of dynamic LDS say so once per process.
+int lds_limits_once() {
+    static int status = [] {
+        hipError_t e = hipSuccess;
+        e = e == hipSuccess ? hipFuncSetAttribute((const void *)k_pair_eig<128>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)eig_lds_bytes(128))
+                            : e;
+        e = e == hipSuccess ? hipFuncSetAttribute((const void *)k_merged_weight<128>,
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)weight_lds_bytes(128))
+                            : e;
+        return e == hipSuccess ? (int)SAGA_OK : (int)SAGA_ERR_HIP;
+    }();
+    return status;
+}
+
+template <int D>
+int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
+              const int32_t *pairs_in, float *W_merged, int32_t *pairs, double *pair_loss,
+              double *total_loss, char *ws, hipStream_t s) {
+    float *K = (float *)(ws + p.off_K);
+    float *part = (float *)(ws + p.off_part);
+    float *SG = (float *)(ws + p.off_SG);
+    float *V = (float *)(ws + p.off_V);
+    float *lam = (float *)(ws + p.off_lam);
+    float *Sp = (float *)(ws + p.off_Sp);
+    float *Pm = (float *)(ws + p.off_Pm);
+
+    ProjArgs pa{(const uint16_t *)X, (const uint16_t *)W_K, K, p.n, p.dm, p.h_kt * D};
+    hipLaunchKernelGGL(k_kproj, dim3((unsigned)ceil_div(p.n, kPBM), (unsigned)(p.h_kt * D / kPBN)),
+                       dim3(kThreads), 0, s, pa);
+
+    GramArgs ga{};
+    ga.Q = (const uint16_t *)Q;
+    ga.K = K;
+    ga.part = part;
+    ga.n = p.n;
+    ga.chunk_tokens = p.chunk_tokens;
+    ga.n_chunk = p.n_chunk;
+    ga.h_q = p.h_q;
+    ga.h_kt = p.h_kt;
+    pair_table(p.h_kt, ga.pa, ga.pb);
+    hipLaunchKernelGGL(k_gram<D>, dim3((unsigned)p.n_chunk, (unsigned)p.items), dim3(kThreads), 0,
+                       s, ga);
+
+    ReduceArgs ra{part, SG, p.n_chunk, D * D};
+    hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)ceil_div(D * D, kThreads), (unsigned)p.items),
+                       dim3(kThreads), 0, s, ra);
+
+    EigArgs ea{};
+    ea.SG = SG;
+    ea.V = V;
+    ea.lam = lam;
+    ea.h_kt = p.h_kt;
+    pair_table(p.h_kt, ea.pa, ea.pb);
+    hipLaunchKernelGGL(k_pair_eig<D>, dim3((unsigned)p.P), dim3(kThreads), eig_lds_bytes(D), s, ea);
+
+    LossArgs la{};
+    la.SG = SG;
+    la.V = V;
+    la.lam = lam;
+    la.Sp = Sp;
+    la.Pm = Pm;
+    la.w = pair_loss;
+    la.h_kt = p.h_kt;
+    pair_table(p.h_kt, la.pa, la.pb);
+    hipLaunchKernelGGL(k_pair_loss<D>, dim3((unsigned)p.P), dim3(kThreads), 0, s, la);
+
+    MatchArgs ma{};
+    ma.w = pair_loss;
+    ma.dp = (double *)(ws + p.off_dp);
+    ma.choice = (uint8_t *)(ws + p.off_choice);
+    ma.pairs = pairs;
+    ma.total = total_loss;
+    ma.h_kt = p.h_kt;
+    ma.forced = pairs_in != nullptr;
+    if (pairs_in) {
+        // canonical order: a < b within a pair, pairs sorted by a
+        int a_of[kMaxHeads / 2], b_of[kMaxHeads / 2];
+        for (int i = 0; i < p.h_kt / 2; ++i) {
+            const int x = pairs_in[2 * i], y = pairs_in[2 * i + 1];
+            a_of[i] = x < y ? x : y;
+            b_of[i] = x < y ? y : x;
+        }
+        for (int i = 0; i < p.h_kt / 2; ++i)
+            for (int j = i + 1; j < p.h_kt / 2; ++j)
+                if (a_of[j] < a_of[i]) {
+                    int t = a_of[i]; a_of[i] = a_of[j]; a_of[j] = t;
+                    t = b_of[i]; b_of[i] = b_of[j]; b_of[j] = t;
+                }
+        for (int i = 0; i < p.h_kt / 2; ++i) {
+            ma.fa[i] = (uint8_t)a_of[i];
+            ma.fb[i] = (uint8_t)b_of[i];
+        }
+    }
+    hipLaunchKernelGGL(k_match, dim3(1), dim3(kThreads), 0, s, ma);
+
+    WeightArgs wa{(const uint16_t *)W_K, Pm, pairs, W_merged, p.dm, p.h_kt};
+    hipLaunchKernelGGL(k_merged_weight<D>, dim3((unsigned)(p.h_kt / 2), (unsigned)ceil_div(p.dm, kThreads)),
+                       dim3(kThreads), weight_lds_bytes(D), s, wa);
+    return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t saga_merge_workspace_bytes(int64_t n, int h_q, int h_kt, int d, int d_model) {
+    MergePlan p;
+    return make_merge_plan(n, h_q, h_kt, d, d_model, &p) == SAGA_OK ? p.bytes : 0;
+}
+
+int saga_merge_key_heads(const void *X, const void *Q, const void *W_K, int64_t n, int h_q,
+                         int h_kt, int d, int d_model, const int32_t *pairs_in, float *W_merged,
+                         int32_t *pairs, double *pair_loss, double *total_loss, void *ws,
+                         size_t ws_bytes, void *hip_stream) {
+    MergePlan p;
+    const int st = make_merge_plan(n, h_q, h_kt, d, d_model, &p);
+    if (st != SAGA_OK) return st;
+    const void *ptrs16[] = {X, Q, W_K, W_merged, pair_loss, total_loss, ws};
+    for (const void *ptr : ptrs16)
+        if (!ptr || !aligned(ptr, 16)) return SAGA_ERR_INVALID_ARG;
+    if (!pairs || !aligned(pairs, 4)) return SAGA_ERR_INVALID_ARG;
+    if (pairs_in) {
+        int seen[kMaxHeads] = {0};
+        for (int i = 0; i < h_kt; ++i) {
+            const int x = pairs_in[i];
+            if (x < 0 || x >= h_kt || seen[x]) return SAGA_ERR_INVALID_ARG;
+            seen[x] = 1;
+        }
+    }
+    if (ws_bytes < p.bytes) return SAGA_ERR_WORKSPACE;
+    if (lds_limits_once() != SAGA_OK) return SAGA_ERR_HIP;
+    hipStream_t s = (hipStream_t)hip_stream;
+    char *w = (char *)ws;
+    return d == 64 ? run_merge<64>(p, X, Q, W_K, pairs_in, W_merged, pairs, pair_loss, total_loss,
+                                   w, s)
+                   : run_merge<128>(p, X, Q, W_K, pairs_in, W_merged, pairs, pair_loss,
+                                    total_loss, w, s);
+}
+
+}  // extern "C"

@@ -28,7 +28,7 @@ EXPORTS = (
     "saga_dense_gqa_baseline", "saga_workspace_layout", "saga_selection_mask", "saga_select",
     "saga_attend", "saga_read_probe", "saga_decode_step_pivot", "saga_full_attention",
     "saga_full_attention_workspace_bytes", "saga_cache_workspace_bytes", "saga_append_kv",
-    "saga_decode_step_cache",
+    "saga_decode_step_cache", "saga_merge_workspace_bytes", "saga_merge_key_heads",
 )
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
@@ -109,6 +109,11 @@ def lib(path: str | None = None):
     L.saga_decode_step_cache.restype = i32
     L.saga_read_probe.argtypes = [vp, i64, vp, vp]
     L.saga_read_probe.restype = i32
+    L.saga_merge_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.saga_merge_workspace_bytes.restype = sz
+    L.saga_merge_key_heads.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32,
+                                       ctypes.POINTER(ctypes.c_int32), vp, vp, vp, vp, vp, sz, vp]
+    L.saga_merge_key_heads.restype = i32
     if path is None:
         _lib = L
     return L

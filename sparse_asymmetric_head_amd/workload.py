@@ -159,3 +159,61 @@ def make_random(B: int, h_q: int, h_k: int, h_v: int, d: int, l_kv: int, seed: i
     Q = make_queries(B, h_q, d, steps, q_scale, drift, g, device)
     K, V = make_cache(B, h_q, h_k, h_v, d, l_kv, Q[0], planted, heavy_tail, g, device)
     return {"Q": Q, "K": K, "V": V}
+
+
+# ------------------------------------------------------ key-merge (conversion)
+#
+# Recipe for the GQA -> SAGA key-merge inputs (the pages convert pretrained
+# Llama/Qwen GQA models with calibration data; no weights or data are used, these
+# tensors stand in for one attention layer of that shape):
+#   * X [n][d_model]: i.i.d. N(0, 1), rounded to bf16 (normalised hidden states);
+#   * teacher key heads come in h_kt/2 hidden families assigned by a seeded
+#     permutation: W_K^r = B_family(r) + spread * E_r with B, E i.i.d.
+#     N(0, 1/d_model), so some pairs are much closer than others and the best
+#     pairing is not the identity;
+#   * queries Q_j = X W_Q^j with W_Q^j i.i.d. N(0, 1/d_model) scaled by
+#     exp(-c/decay) on channel c (anisotropic query statistics, condition
+#     number about exp(2 d/decay) over the channels), rounded to bf16;
+#   * the planted variant makes the two heads of every family identical.
+# The generator holds none of the conversion's arithmetic.
+
+
+@dataclass(frozen=True)
+class MergeConfig:
+    name: str
+    n: int
+    h_q: int
+    h_kt: int
+    d: int
+    d_model: int
+    spread: float = 0.5
+    decay: float = 32.0
+
+    def with_(self, **kw) -> "MergeConfig":
+        return replace(self, **kw)
+
+
+MERGE_CONFIGS = [
+    MergeConfig("merge-tiny", n=300, h_q=32, h_kt=8, d=64, d_model=256),
+    MergeConfig("merge-llama32-1b-16k", n=16384, h_q=32, h_kt=8, d=64, d_model=2048),
+    MergeConfig("merge-qwen25-1.5b-16k", n=16384, h_q=12, h_kt=2, d=128, d_model=1536, decay=64.0),
+]
+
+
+def make_merge_inputs(cfg: MergeConfig, seed: int, device="cpu", planted: bool = False):
+    """(X [n][d_model], Q [n][h_q][d], W_K [h_kt*d][d_model]) in bf16.  The random
+    draws come from one CPU generator (identical on every host); the query
+    projection runs on ``device``."""
+    g = _gen(seed, "cpu")
+    n, dm, d, h_kt, h_q = cfg.n, cfg.d_model, cfg.d, cfg.h_kt, cfg.h_q
+    X = _normal((n, dm), g, "cpu").to(torch.bfloat16)
+    fam = torch.randperm(h_kt, generator=g) // 2
+    base = _normal((h_kt // 2, d, dm), g, "cpu") / dm ** 0.5
+    dev = _normal((h_kt, d, dm), g, "cpu") / dm ** 0.5
+    W = base[fam] + (0.0 if planted else cfg.spread) * dev
+    scale = torch.exp(-torch.arange(d, dtype=torch.float32) / cfg.decay)
+    WQ = _normal((h_q, d, dm), g, "cpu") / dm ** 0.5 * scale[None, :, None]
+    Xd = X.to(device)
+    Q = (Xd.to(torch.float32) @ WQ.reshape(h_q * d, dm).to(device).t()).reshape(n, h_q, d)
+    return (Xd.contiguous(), Q.to(torch.bfloat16).contiguous(),
+            W.reshape(h_kt * d, dm).to(torch.bfloat16).to(device).contiguous())

@@ -1,20 +1,23 @@
-"""The C-ABI library: it loads, exports every entry point include/saga.h
+"""The C-ABI library: it loads, exports every entry point include/*.h
 declares, and validates arguments on the host (no GPU needed: an invalid call
 returns its status before anything is enqueued)."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "saga.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(saga_\w+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(saga_\w+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
     names = declared_functions()
     for n in names:
-        assert hasattr(L, n), f"{n} declared in saga.h but not exported"
+        assert hasattr(L, n), f"{n} declared in include/*.h but not exported"
     assert set(names) == set(saga.EXPORTS)
 
 
@@ -217,3 +220,42 @@ def test_product_path_does_not_import_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in src and "from oracle" not in src, f
                 assert "saga_oracle" not in src and "sao_" not in src, f
+
+
+def test_merge_validates_before_launch(L):
+    """The key-merge entry point rejects bad arguments on the host (no GPU needed)."""
+    from sparse_asymmetric_head_amd import saga
+
+    mw = L.saga_merge_workspace_bytes
+    assert mw(4096, 32, 8, 64, 2048) > 0
+    assert mw(4096, 12, 2, 128, 1536) > 0
+    assert mw(8192, 32, 8, 64, 2048) > mw(4096, 32, 8, 64, 2048)
+    assert mw(0, 32, 8, 64, 2048) == 0            # no tokens
+    assert mw(4096, 32, 7, 64, 2048) == 0         # odd number of teacher key heads
+    assert mw(4096, 32, 18, 64, 2048) == 0        # more than 16 teacher key heads
+    assert mw(4096, 4, 8, 64, 2048) == 0          # fewer query heads than key heads
+    assert mw(4096, 32, 8, 96, 2048) == 0         # d unsupported
+    assert mw(4096, 32, 8, 64, 2000) == 0         # d_model not a multiple of 64
+    n, h_q, h_kt, d, dm = 1000, 32, 8, 64, 256
+    need = mw(n, h_q, h_kt, d, dm)
+    fake = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)
+    f = L.saga_merge_key_heads
+    args = [fake, fake, fake, n, h_q, h_kt, d, dm, None, fake, fake, fake, fake, fake, need, None]
+    bad = list(args); bad[0] = None
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[9] = mis
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[10] = None
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[14] = need - 256
+    assert f(*bad) == saga.SAGA_ERR_WORKSPACE
+    bad = list(args); bad[6] = 80
+    assert f(*bad) == saga.SAGA_ERR_UNSUPPORTED
+    bad = list(args); bad[3] = 0
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+    pin = ctypes.c_int32 * 8
+    bad = list(args); bad[8] = pin(0, 1, 2, 3, 4, 5, 6, 6)       # head 6 twice
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+    bad = list(args); bad[8] = pin(0, 1, 2, 3, 4, 5, 6, 8)       # head 8 does not exist
+    assert f(*bad) == saga.SAGA_ERR_INVALID_ARG

@@ -1,0 +1,270 @@
+"""GQA -> SAGA key merge on the GPU against the fp64 oracle (oracle/key_merge.py),
+through the C ABI (saga_merge_key_heads).
+
+Tolerances, from the arithmetic: keys are fp32 sums of exact bf16 products;
+the second moments are fp32 sums of exact fp32 products (relative error about
+1e-6); the cyclic Jacobi eigendecomposition in fp32 gets eigenpairs to about
+1e-5 of the largest eigenvalue, so the pseudoinverse, the merge maps and the
+costs carry about 1e-5 * cond(S_a + S_b) relative error.  The synthetic query
+statistics have cond <= ~100 (channel scales exp(-c/decay)), hence 2e-3 on the
+costs and on the merged weights (relative to their largest entry).  The
+pairing is compared exactly when the oracle's best pairing beats every other
+by more than that; otherwise the GPU's pairing must cost (on the oracle's
+weights) no more than the optimum within the same tolerance.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import key_merge as km
+from sparse_asymmetric_head_amd.merge import KeyMerge
+from sparse_asymmetric_head_amd.workload import MERGE_CONFIGS, MergeConfig, make_merge_inputs
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-3
+
+
+def _f64(t):
+    return t.detach().to("cpu", torch.float32).to(torch.float64).numpy()
+
+
+def _oracle(X, Q, W, h_kt, d, pairs=None):
+    Xn, Qn, Wn = _f64(X), _f64(Q), _f64(W)
+    Wp = Wn.reshape(h_kt, d, -1).transpose(0, 2, 1).copy()   # pages' W_K^r: d_model x d
+    return km.convert(Xn, Qn, Wp, pairs=pairs)
+
+
+def _run(cfg, seed, planted=False, pairs_in=None, mutate=None):
+    X, Q, W = make_merge_inputs(cfg, seed, "cpu", planted=planted)
+    if mutate:
+        X, Q, W = mutate(X, Q, W)
+    print(f"[merge] {cfg} seed={seed} planted={planted} pairs_in={pairs_in}", flush=True)
+    m = KeyMerge(cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model)
+    m(X.cuda(), Q.cuda(), W.cuda(), pairs_in=pairs_in)
+    torch.cuda.synchronize()
+    got = {
+        "w": m.pair_loss.cpu().numpy(),
+        "pairs": [tuple(p) for p in m.pairs.cpu().tolist()],
+        "total": float(m.total_loss.cpu()[0]),
+        "W_merged": m.W_merged.cpu().numpy(),
+    }
+    return X, Q, W, got
+
+
+def _matchings_sorted(w):
+    costs = sorted((sum(w[a, b] for a, b in m), m) for m in km.perfect_matchings(range(w.shape[0])))
+    return costs
+
+
+def _check(cfg, got, want):
+    h_kt, d = cfg.h_kt, cfg.d
+    w, ww = got["w"], want["w"]
+    assert np.all(np.isfinite(w))
+    assert np.allclose(w, w.T, rtol=0, atol=0)
+    assert np.all(np.diag(w) == 0)
+    scale = np.abs(ww).max()
+    err = np.abs(w - ww) / (np.abs(ww) + 1e-6 * scale)
+    assert err.max() <= RTOL, (err.max(), np.unravel_index(err.argmax(), err.shape))
+    gap = 0.0                                    # unknown: only the cost bound applies
+    if h_kt <= 10:
+        ranked = _matchings_sorted(ww)
+        gap = np.inf if len(ranked) == 1 else \
+            (ranked[1][0] - ranked[0][0]) / max(ranked[0][0], 1e-30 * scale)
+    gpu_pairs = got["pairs"]
+    assert sorted(x for p in gpu_pairs for x in p) == list(range(h_kt))
+    assert all(a < b for a, b in gpu_pairs) and gpu_pairs == sorted(gpu_pairs)
+    cost_on_oracle = sum(ww[a, b] for a, b in gpu_pairs)
+    if gap > 10 * RTOL:
+        assert gpu_pairs == want["pairs"], (gpu_pairs, want["pairs"], gap)
+    assert cost_on_oracle <= want["total"] * (1 + RTOL) + 1e-9 * scale
+    assert abs(got["total"] - sum(w[a, b] for a, b in gpu_pairs)) <= 1e-9 * max(scale, 1.0)
+    return got["W_merged"].reshape(h_kt // 2, d, -1)
+
+
+def _check_weights(cfg, Wm, X, Q, W, pairs):
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d, pairs=pairs)
+    for i, (a, b) in enumerate(pairs):
+        ref = want["W_merged"][i].T                      # d x d_model
+        tol = RTOL * np.abs(ref).max()
+        assert np.abs(Wm[i] - ref).max() <= tol, (i, (a, b), np.abs(Wm[i] - ref).max(), tol)
+
+
+CASES = [
+    ("llama-tiny", MERGE_CONFIGS[0], 1),
+    ("llama-ragged", MergeConfig("t", n=517, h_q=32, h_kt=8, d=64, d_model=192), 2),
+    ("qwen-tiny", MergeConfig("t", n=250, h_q=12, h_kt=2, d=128, d_model=256, decay=64.0), 3),
+    ("uneven-groups", MergeConfig("t", n=200, h_q=10, h_kt=4, d=64, d_model=128), 4),
+    ("d128-six-heads", MergeConfig("t", n=160, h_q=12, h_kt=6, d=128, d_model=128, decay=64.0), 5),
+]
+
+
+@pytest.mark.parametrize("name,cfg,seed", CASES, ids=[c[0] for c in CASES])
+def test_merge_matches_oracle(name, cfg, seed):
+    X, Q, W, got = _run(cfg, seed)
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    Wm = _check(cfg, got, want)
+    _check_weights(cfg, Wm, X, Q, W, got["pairs"])
+
+
+def test_merge_sixteen_heads():
+    """h_kt = 16 (the largest supported): 120 pair costs and the 2^16-state matching."""
+    cfg = MergeConfig("t", n=96, h_q=16, h_kt=16, d=64, d_model=128)
+    X, Q, W, got = _run(cfg, 6)
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    _check(cfg, got, want)
+    # exhaustive enumeration of 2027025 matchings is the oracle's optimum
+    assert got["total"] <= want["total"] * (1 + RTOL)
+
+
+def test_merge_planted_pairs_are_found_exactly():
+    """Identical teacher heads in pairs: the GPU finds that pairing with zero cost,
+    and each merged key is the shared projection."""
+    cfg = MERGE_CONFIGS[0]
+    X, Q, W, got = _run(cfg, 7, planted=True)
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    assert got["pairs"] == want["pairs"]
+    off = min(want["w"][a, b] for a, b in itertools.combinations(range(cfg.h_kt), 2)
+              if (a, b) not in want["pairs"])
+    assert 0.0 <= got["total"] <= 1e-7 * off
+    Wm = got["W_merged"].reshape(cfg.h_kt // 2, cfg.d, -1)
+    Wt = _f64(W).reshape(cfg.h_kt, cfg.d, -1)
+    for i, (a, b) in enumerate(got["pairs"]):
+        assert np.array_equal(Wt[a], Wt[b])
+        assert np.abs(Wm[i] - Wt[a]).max() <= RTOL * np.abs(Wt[a]).max()
+
+
+def test_merge_forced_pairing():
+    """A caller-chosen pairing: costs are unchanged, the total and the merged keys
+    follow that pairing (given in any order)."""
+    cfg = MERGE_CONFIGS[0]
+    forced = [(7, 0), (2, 5), (1, 6), (4, 3)]
+    X, Q, W, got = _run(cfg, 8, pairs_in=forced)
+    canon = sorted((min(a, b), max(a, b)) for a, b in forced)
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d, pairs=canon)
+    assert got["pairs"] == canon
+    scale = np.abs(want["w"]).max()
+    assert np.abs(got["w"] - want["w"]).max() <= RTOL * scale
+    assert abs(got["total"] - want["total"]) <= RTOL * want["total"]
+    _check_weights(cfg, got["W_merged"].reshape(cfg.h_kt // 2, cfg.d, -1), X, Q, W, canon)
+
+
+def _blind(channels):
+    def f(X, Q, W):
+        Q = Q.clone()
+        Q[:, :, channels:] = 0
+        return X, Q, W
+    return f
+
+
+def test_merge_exact_null_space():
+    """Queries never read channels 40..63 (exact zeros): S_a + S_b is singular, so
+    the pseudoinverse, not an inverse, decides the merge, and the merged keys are
+    exactly zero on those channels."""
+    cfg = MergeConfig("t", n=300, h_q=8, h_kt=4, d=64, d_model=128)
+    X, Q, W, got = _run(cfg, 9, mutate=_blind(40))
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    Wm = _check(cfg, got, want)
+    _check_weights(cfg, Wm, X, Q, W, got["pairs"])
+    assert np.all(Wm[:, 40:, :] == 0.0)
+
+
+def test_merge_pseudoinverse_cutoff():
+    """Queries confined to a random 40-dimensional subspace not aligned with the
+    channels: after bf16 rounding the other 24 directions keep eigenvalues about
+    1e-6 of the largest.  The kernel counts eigenvalues at or below 2^-14 of the
+    largest as zero; the oracle is run with that same cutoff here."""
+    cfg = MergeConfig("t", n=300, h_q=8, h_kt=4, d=64, d_model=128)
+    g = torch.Generator().manual_seed(14)
+    R, _ = torch.linalg.qr(torch.randn(cfg.d, cfg.d, generator=g, dtype=torch.float64))
+
+    def rotate(X, Q, W):
+        Qb = Q.clone()
+        Qb[:, :, 40:] = 0
+        Qr = (Qb.to(torch.float64) @ R).to(torch.bfloat16).contiguous()
+        return X, Qr, W
+
+    X, Q, W, got = _run(cfg, 9, mutate=rotate)
+    Qn = _f64(Q)
+    for a, b in itertools.combinations(range(cfg.h_kt), 2):
+        lam = np.linalg.eigvalsh(km.second_moment(Qn, a, cfg.h_kt) + km.second_moment(Qn, b, cfg.h_kt))
+        lam = lam / lam.max()
+        assert np.sort(lam)[24] > 1e-3 and np.sort(lam)[23] < 1e-5, "no clear gap at the cutoff"
+    Xn, Wn = _f64(X), _f64(W)
+    Wp = Wn.reshape(cfg.h_kt, cfg.d, -1).transpose(0, 2, 1).copy()
+    want = km.convert(Xn, Qn, Wp, rtol=2.0 ** -14)
+    Wm = _check(cfg, got, want)
+    ref = km.convert(Xn, Qn, Wp, pairs=got["pairs"], rtol=2.0 ** -14)
+    for i in range(cfg.h_kt // 2):
+        r = ref["W_merged"][i].T
+        assert np.abs(Wm[i] - r).max() <= RTOL * np.abs(r).max()
+
+
+def test_merge_unqueried_group_costs_nothing():
+    """A teacher head none of whose query heads ever fires merges with any head for free."""
+    cfg = MergeConfig("t", n=128, h_q=16, h_kt=4, d=64, d_model=128)
+
+    def silence(X, Q, W):
+        Q = Q.clone()
+        Q[:, 8:12] = 0
+        return X, Q, W
+
+    X, Q, W, got = _run(cfg, 10, mutate=silence)
+    assert np.all(got["w"][2] == 0.0) and np.all(got["w"][:, 2] == 0.0)
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    Wm = _check(cfg, got, want)
+    _check_weights(cfg, Wm, X, Q, W, got["pairs"])
+
+
+def test_merge_repeat_is_deterministic():
+    cfg = MERGE_CONFIGS[0]
+    X, Q, W = [t.cuda() for t in make_merge_inputs(cfg, 11, "cpu")]
+    m = KeyMerge(cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model)
+    m(X, Q, W)
+    first = (m.W_merged.clone(), m.pair_loss.clone(), m.pairs.clone())
+    m(X, Q, W)
+    assert torch.equal(first[0], m.W_merged) and torch.equal(first[1], m.pair_loss)
+    assert torch.equal(first[2], m.pairs)
+
+
+@pytest.mark.parametrize("cfg", MERGE_CONFIGS[1:], ids=[c.name for c in MERGE_CONFIGS[1:]])
+def test_merge_full_size_properties(cfg):
+    """At the benchmark sizes (16384 calibration tokens, the Llama-3.2-1B and
+    Qwen2.5-1.5B layer shapes), where eq. 13 as written is out of the oracle's
+    reach: with planted identical families the pairing is the planted one at
+    (numerically) zero cost, each merged key is the shared projection, and the
+    pair costs are symmetric, finite and non-negative."""
+    X, Q, W = make_merge_inputs(cfg, 12, "cuda", planted=True)
+    print(f"[merge] full size {cfg}", flush=True)
+    m = KeyMerge(cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model)
+    m(X, Q, W)
+    torch.cuda.synchronize()
+    w = m.pair_loss.cpu().numpy()
+    assert np.all(np.isfinite(w)) and np.array_equal(w, w.T)
+    assert w.min() >= -1e-6 * w.max()
+    Wt = W.float().cpu().numpy().reshape(cfg.h_kt, cfg.d, -1)
+    fams = {}
+    for r in range(cfg.h_kt):
+        fams.setdefault(Wt[r].tobytes(), []).append(r)
+    planted = sorted(tuple(v) for v in fams.values())
+    assert [tuple(p) for p in m.pairs.cpu().tolist()] == planted
+    off = [w[a, b] for a, b in itertools.combinations(range(cfg.h_kt), 2) if (a, b) not in planted]
+    if off:
+        assert min(off) > 0
+        assert 0.0 <= float(m.total_loss.cpu()[0]) <= 1e-7 * min(off)
+    Wm = m.W_merged.cpu().numpy().reshape(cfg.h_kt // 2, cfg.d, -1)
+    for i, (a, b) in enumerate(planted):
+        assert np.abs(Wm[i] - Wt[a]).max() <= RTOL * np.abs(Wt[a]).max()
+
+
+@pytest.mark.parametrize("cfg", MERGE_CONFIGS[1:], ids=[c.name for c in MERGE_CONFIGS[1:]])
+def test_merge_full_width_prefix_matches_oracle(cfg):
+    """The benchmark layer width (d_model 2048 / 1536, all heads) on a 384-token
+    prefix of its calibration set: element-wise parity with the oracle."""
+    sub = cfg.with_(n=384)
+    X, Q, W, got = _run(sub, 13)
+    want = _oracle(X, Q, W, sub.h_kt, sub.d)
+    Wm = _check(sub, got, want)
+    _check_weights(sub, Wm, X, Q, W, got["pairs"])
