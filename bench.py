@@ -114,12 +114,60 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--cpu-sample-layers", type=int, default=16)
     ap.add_argument("--kernel-timing-steps", type=int, default=8)
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the GQA -> SAGA key-merge (conversion) timing")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="time only the GQA -> SAGA key merge and print its JSON")
+    ap.add_argument("--merge-reps", type=int, default=20)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the dominant kernel's counter traffic summary and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 4 plain device-to-device copies of MIB MiB (a reference "
                          "kernel of known traffic for hardware counter runs)")
     return ap.parse_args()
+
+
+def merge_bench(torch, reps: int, warmup: int = 2) -> dict:
+    """Whole-call time of the GQA -> SAGA key merge (eqs. 13-15, Theorem 4.2) on
+    one attention layer of each converted model's shape, 16384 calibration tokens,
+    inputs resident in HBM; HIP events on the stream the library launches on."""
+    from sparse_asymmetric_head_amd import workload as wl
+    from sparse_asymmetric_head_amd.merge import KeyMerge
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    res = {}
+    for cfg in wl.MERGE_CONFIGS[1:]:
+        n, h_q, h_kt, d, dm = cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model
+        X, Q, W = wl.make_merge_inputs(cfg, 1, dev)
+        m = KeyMerge(n, h_q, h_kt, d, dm, device=dev)
+        torch.cuda.synchronize()
+        times = []
+        with torch.cuda.stream(stream):
+            for i in range(warmup + reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                m(X, Q, W, stream=stream)
+                e1.record(stream)
+                stream.synchronize()
+                if i >= warmup:
+                    times.append(e0.elapsed_time(e1) * 1e3)
+        times.sort()
+        us = times[len(times) // 2]
+        P = h_kt * (h_kt - 1) // 2
+        proj_flop = 2 * n * dm * h_kt * d
+        gram_flop = 2 * (n * h_q + n * P) * d * d
+        in_bytes = 2 * (n * dm + n * h_q * d + h_kt * d * dm)
+        res[cfg.name] = {"n": n, "h_q": h_q, "h_kt": h_kt, "d": d, "d_model": dm,
+                         "us_per_layer": round(us, 1), "us_p10": round(times[len(times) // 10], 1),
+                         "pairs": [tuple(p) for p in m.pairs.cpu().tolist()],
+                         "projection_gflop": round(proj_flop / 1e9, 2),
+                         "gram_gflop": round(gram_flop / 1e9, 2),
+                         "input_mb": round(in_bytes / 1e6, 1)}
+        log(f"key merge {cfg.name}: {us:.1f} us per layer (p10 {times[len(times) // 10]:.1f})")
+        del X, Q, W, m
+    return res
 
 
 def main() -> int:
@@ -143,6 +191,9 @@ def main() -> int:
     from sparse_asymmetric_head_amd import workload as wl
 
     saga.lib()  # fails loudly when the HIP library is missing
+    if args.merge_only:
+        print(json.dumps({"gqa_to_saga_merge": merge_bench(torch, args.merge_reps)}), flush=True)
+        return 0
     cfg = next((c for c in wl.CONFIGS if c.name == args.config), None)
     if cfg is None:
         print(f"unknown config {args.config}", file=sys.stderr)
@@ -458,6 +509,10 @@ def main() -> int:
                           f"layer-step, {t_one + t_all:.1f} s of oracle time)")}
         log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads")
 
+    merge = None
+    if not args.no_merge:
+        merge = merge_bench(torch, args.merge_reps)
+
     out = {
         "metric": METRIC,
         "value": round(us_per_step, 2),
@@ -488,6 +543,7 @@ def main() -> int:
         "per_step_us": per_step,
         "dense_gqa": dense,
         "saga_full_attention": full,
+        "gqa_to_saga_merge": merge,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

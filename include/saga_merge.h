@@ -18,9 +18,12 @@
  *     minimum-weight perfect matching on the complete graph of pair costs.
  * Readings of this library (the pages leave them open):
  *   - group r = the query heads j with floor(j*h_kt/h_q) == r (the GQA map);
- *   - the pseudoinverse counts eigenvalues of S_a + S_b at or below 2^-14
- *     times the largest as zero (fp32 arithmetic; a spectrum with no gap
- *     near that level makes the result depend on rounding);
+ *   - the pseudoinverse's numerical rank is the number of steps a
+ *     diagonally pivoted Cholesky factorisation of S_a + S_b takes before
+ *     the largest remaining pivot falls to 2^-14 times the largest diagonal
+ *     entry; with S = L L^T at that rank, S^+ = L (L^T L)^-2 L^T (fp32
+ *     arithmetic; a spectrum with no gap near that level makes the result
+ *     depend on rounding);
  *   - equal-cost pairings: the one whose lowest head takes the lowest
  *     partner wins, recursively;
  *   - merged head i serves the query heads of teacher groups pairs[i][0]
@@ -41,8 +44,9 @@
  *   total_loss fp64 [1]                summed cost of the pairing
  * Arithmetic: keys X W_K^T from bf16 products accumulated in fp32; second
  * moments of queries and key differences from exact fp32 products summed in
- * fp32 per block and fp64 across blocks; eigendecomposition (cyclic Jacobi)
- * and the d x d products in fp32; costs summed in fp64.
+ * fp32 per block and fp64 across blocks; the pseudoinverse (pivoted
+ * Cholesky, Gauss-Jordan inverse of L^T L) and the d x d products in fp32;
+ * costs summed in fp64.
  * Supported: d in {64, 128}; h_kt even, 2 <= h_kt <= 16; h_kt <= h_q <= 1024;
  * d_model a multiple of 64, 64 <= d_model <= 32768; 1 <= n <= 2^26.
  */

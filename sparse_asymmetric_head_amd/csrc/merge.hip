@@ -2,12 +2,13 @@
 //
 // Launch sequence on one stream:
 //   k_kproj          K = X W_K^T                                  (n/128 x h_kt*d/128 blocks)
-//   k_gram<D>        per-chunk second moments: S_r (h_kt items) and G_p of K_a - K_b (pairs)
+//   k_gram<D,1>      per-chunk second moments S_r of each group's queries (h_kt items)
+//   k_gram<D,0>      per-chunk second moments G_p of K_a - K_b         (one item per pair)
 //   k_gram_reduce    fixed-order fp64 sum over chunks
-//   k_pair_eig<D>    eigenpairs of S_a + S_b                      (one block per pair)
-//   k_pair_loss<D>   S^+, P_a, P_b and the eq. 13 cost            (one block per pair)
-//   k_match          minimum-weight perfect matching              (one block)
-//   k_merged_weight  eq. 15 in the weight layout                  (h_kt/2 x d_model/256 blocks)
+//   k_pair_pinv<D>   (S_a + S_b)^+ by a rank-revealing Cholesky        (one block per pair)
+//   k_pair_loss<D>   P_a, P_b and the eq. 13 cost                      (one block per pair)
+//   k_match          minimum-weight perfect matching                   (one block)
+//   k_merged_weight  eq. 15 in the weight layout     (h_kt/2 x d/8 x d_model/256 blocks)
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -24,14 +25,13 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kTargetGramBlocks = 1024;   // about four blocks per compute unit
-constexpr int64_t kMinChunkTokens = 64;
+constexpr int64_t kTargetGramBlocks = 1024;   // about four blocks per compute unit
 
 struct MergePlan {
     int64_t n;
-    int h_q, h_kt, d, dm, P, items, n_chunk;
-    int64_t chunk_tokens;
-    size_t off_K, off_part, off_SG, off_V, off_lam, off_Sp, off_Pm, off_dp, off_choice, bytes;
+    int h_q, h_kt, d, dm, P, items, nq, nd;
+    int64_t ct_q, ct_d;   // tokens per Gram block: query items, key-difference items
+    size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_rank, off_dp, off_choice, bytes;
 };
 
 int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan *p) {
@@ -48,21 +48,24 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     p->dm = d_model;
     p->P = h_kt * (h_kt - 1) / 2;
     p->items = h_kt + p->P;
-    int64_t nc = ceil_div(kTargetGramBlocks, p->items);
-    const int64_t max_nc = ceil_div(n, kMinChunkTokens);
-    nc = nc < max_nc ? nc : max_nc;
-    nc = nc < 1 ? 1 : nc;
-    p->chunk_tokens = ceil_div(n, nc);
-    p->n_chunk = (int)ceil_div(n, p->chunk_tokens);
+    // Samples per Gram block: enough that a block's input outweighs its d x d
+    // partial (at least 16 d samples), and about kTargetGramBlocks blocks overall.
+    const int64_t g_max = ceil_div(h_q, h_kt);
+    const int64_t total = n * h_q + n * p->P;
+    int64_t s_blk = ceil_div(total, kTargetGramBlocks);
+    s_blk = s_blk > 16 * d ? s_blk : 16 * d;
+    p->ct_q = ceil_div(s_blk, g_max);
+    p->ct_d = s_blk;
+    p->nq = (int)ceil_div(n, p->ct_q);
+    p->nd = (int)ceil_div(n, p->ct_d);
     const size_t dd = (size_t)d * d * sizeof(float);
     size_t o = 0;
     p->off_K = o;      o = align_up(o + (size_t)n * h_kt * d * sizeof(float));
-    p->off_part = o;   o = align_up(o + (size_t)p->items * p->n_chunk * dd);
+    p->off_part = o;   o = align_up(o + ((size_t)h_kt * p->nq + (size_t)p->P * p->nd) * dd);
     p->off_SG = o;     o = align_up(o + (size_t)p->items * dd);
-    p->off_V = o;      o = align_up(o + (size_t)p->P * dd);
-    p->off_lam = o;    o = align_up(o + (size_t)p->P * d * sizeof(float));
     p->off_Sp = o;     o = align_up(o + (size_t)p->P * dd);
     p->off_Pm = o;     o = align_up(o + (size_t)p->P * 2 * dd);
+    p->off_rank = o;   o = align_up(o + (size_t)p->P * sizeof(int));
     p->off_dp = o;     o = align_up(o + ((size_t)1 << h_kt) * sizeof(double));
     p->off_choice = o; o = align_up(o + ((size_t)1 << h_kt));
     p->bytes = o;
@@ -80,23 +83,17 @@ void pair_table(int h_kt, uint8_t *pa, uint8_t *pb) {
         }
 }
 
-size_t eig_lds_bytes(int d) {
-    return (size_t)2 * d * (d + 1) * sizeof(float) + (size_t)(d / 2) * 16 + 4 + 16;
+size_t pinv_lds_bytes(int d) {
+    return (size_t)2 * d * (d + 4) * sizeof(float) + (size_t)2 * d * sizeof(float);
 }
-size_t weight_lds_bytes(int d) { return (size_t)2 * d * d * sizeof(float); }
 
-// Kernels that take more than 64 KB of dynamic LDS say so once per process.
+// The pseudoinverse kernel for d = 128 takes more than 64 KB of dynamic LDS;
+// say so once per process.
 int lds_limits_once() {
     static int status = [] {
-        hipError_t e = hipSuccess;
-        e = e == hipSuccess ? hipFuncSetAttribute((const void *)k_pair_eig<128>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)eig_lds_bytes(128))
-                            : e;
-        e = e == hipSuccess ? hipFuncSetAttribute((const void *)k_merged_weight<128>,
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  (int)weight_lds_bytes(128))
-                            : e;
+        const hipError_t e = hipFuncSetAttribute((const void *)k_pair_pinv<128>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)pinv_lds_bytes(128));
         return e == hipSuccess ? (int)SAGA_OK : (int)SAGA_ERR_HIP;
     }();
     return status;
@@ -109,8 +106,6 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     float *K = (float *)(ws + p.off_K);
     float *part = (float *)(ws + p.off_part);
     float *SG = (float *)(ws + p.off_SG);
-    float *V = (float *)(ws + p.off_V);
-    float *lam = (float *)(ws + p.off_lam);
     float *Sp = (float *)(ws + p.off_Sp);
     float *Pm = (float *)(ws + p.off_Pm);
 
@@ -121,38 +116,41 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     GramArgs ga{};
     ga.Q = (const uint16_t *)Q;
     ga.K = K;
-    ga.part = part;
     ga.n = p.n;
-    ga.chunk_tokens = p.chunk_tokens;
-    ga.n_chunk = p.n_chunk;
     ga.h_q = p.h_q;
     ga.h_kt = p.h_kt;
     pair_table(p.h_kt, ga.pa, ga.pb);
-    hipLaunchKernelGGL(k_gram<D>, dim3((unsigned)p.n_chunk, (unsigned)p.items), dim3(kThreads), 0,
+    ga.part = part;
+    ga.chunk_tokens = p.ct_q;
+    ga.n_chunk = p.nq;
+    hipLaunchKernelGGL((k_gram<D, true>), dim3((unsigned)p.nq, (unsigned)p.h_kt), dim3(kThreads), 0,
+                       s, ga);
+    ga.part = part + (size_t)p.h_kt * p.nq * D * D;
+    ga.chunk_tokens = p.ct_d;
+    ga.n_chunk = p.nd;
+    hipLaunchKernelGGL((k_gram<D, false>), dim3((unsigned)p.nd, (unsigned)p.P), dim3(kThreads), 0,
                        s, ga);
 
-    ReduceArgs ra{part, SG, p.n_chunk, D * D};
+    ReduceArgs ra{part, SG, p.h_kt, p.nq, p.nd, D * D};
     hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)ceil_div(D * D, kThreads), (unsigned)p.items),
                        dim3(kThreads), 0, s, ra);
 
-    EigArgs ea{};
-    ea.SG = SG;
-    ea.V = V;
-    ea.lam = lam;
-    ea.h_kt = p.h_kt;
-    pair_table(p.h_kt, ea.pa, ea.pb);
-    hipLaunchKernelGGL(k_pair_eig<D>, dim3((unsigned)p.P), dim3(kThreads), eig_lds_bytes(D), s, ea);
+    PinvArgs ia{};
+    ia.SG = SG;
+    ia.Sp = Sp;
+    ia.rank = (int *)(ws + p.off_rank);
+    ia.h_kt = p.h_kt;
+    pair_table(p.h_kt, ia.pa, ia.pb);
+    hipLaunchKernelGGL(k_pair_pinv<D>, dim3((unsigned)p.P), dim3(kThreads), pinv_lds_bytes(D), s, ia);
 
     LossArgs la{};
     la.SG = SG;
-    la.V = V;
-    la.lam = lam;
     la.Sp = Sp;
     la.Pm = Pm;
     la.w = pair_loss;
     la.h_kt = p.h_kt;
     pair_table(p.h_kt, la.pa, la.pb);
-    hipLaunchKernelGGL(k_pair_loss<D>, dim3((unsigned)p.P), dim3(kThreads), 0, s, la);
+    hipLaunchKernelGGL(k_pair_loss<D>, dim3((unsigned)p.P), dim3(kLossThreads), 0, s, la);
 
     MatchArgs ma{};
     ma.w = pair_loss;
@@ -184,8 +182,10 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     hipLaunchKernelGGL(k_match, dim3(1), dim3(kThreads), 0, s, ma);
 
     WeightArgs wa{(const uint16_t *)W_K, Pm, pairs, W_merged, p.dm, p.h_kt};
-    hipLaunchKernelGGL(k_merged_weight<D>, dim3((unsigned)(p.h_kt / 2), (unsigned)ceil_div(p.dm, kThreads)),
-                       dim3(kThreads), weight_lds_bytes(D), s, wa);
+    hipLaunchKernelGGL(k_merged_weight<D>,
+                       dim3((unsigned)(p.h_kt / 2), (unsigned)(D / kWCh),
+                            (unsigned)ceil_div(p.dm, kThreads)),
+                       dim3(kThreads), 0, s, wa);
     return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP;
 }
 

@@ -16,7 +16,7 @@
 //   1. the key projection K = X W^T               (bf16 MFMA GEMM, fp32 out),
 //   2. d x d Gram matrices over the calibration tokens: S_r for every group
 //      and G for every head pair                  (fp32 MFMA, exact products),
-// and the rest is small dense algebra per head pair (an eigendecomposition
+// and the rest is small dense algebra per head pair (a rank-revealing Cholesky
 // for the pseudoinverse, a handful of d x d products) plus a 2^h_kt-state
 // matching.
 #pragma once
@@ -29,8 +29,7 @@ namespace merge {
 constexpr int kThreads = 256;
 constexpr int kMaxHeads = 16;                       // teacher key heads (h_kt)
 constexpr int kMaxPairs = kMaxHeads * (kMaxHeads - 1) / 2;
-constexpr float kEigRtol = 6.103515625e-05f;        // 2^-14: eigenvalues <= this * max are zero
-constexpr int kMaxSweeps = 16;
+constexpr float kPivotRtol = 6.103515625e-05f;      // 2^-14: rank cut, relative to max_i S_ii
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_kproj(ProjArgs a) {
 struct GramArgs {
     const uint16_t *Q;   // [n][h_q][D] bf16 calibration queries
     const float *K;      // [n][h_kt*D] fp32 projected keys
-    float *part;         // [items][n_chunk][D][D] per-block partial sums
+    float *part;         // per-block partial sums: [item][chunk][D][D] of this launch's items
     int64_t n;
     int64_t chunk_tokens;
     int n_chunk;
@@ -156,13 +155,14 @@ struct GramArgs {
 // channel order and un-permuted when written out.
 __device__ __forceinline__ int chan(int I, int i) { return 64 * (I >> 2) + 4 * i + (I & 3); }
 
-// One block per (item, token chunk).  Items 0..h_kt-1: S_r, the second moment of
-// group r's query vectors (samples = (token, query head of the group)).  Items
-// h_kt..: G_p for pair p, the second moment of K_a - K_b (samples = tokens).
+// One block per (item, token chunk).  IS_Q: item r = blockIdx.y, S_r, the second
+// moment of group r's query vectors (samples = (token, query head of the group)).
+// Otherwise item p = blockIdx.y, G_p, the second moment of K_a - K_b over tokens.
 // MFMA 16x16x4 fp32: lane (k = lane/16, i = lane%16) supplies sample k's channel
 // chan(I, i) as both the A (row) and B (column) operand, so each instruction adds
-// 4 samples' outer products to a 16 x 16 tile; only tiles I <= J are formed.
-template <int D>
+// 4 samples' outer products to a 16 x 16 tile; only tiles I <= J are formed.  The
+// next 4 samples are loaded while the current ones are multiplied.
+template <int D, bool IS_Q>
 __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     constexpr int NB = D / 16;                     // feature blocks
     constexpr int NT = NB * (NB + 1) / 2;          // tiles I <= J
@@ -171,41 +171,35 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int k = lane >> 4, i = lane & 15;
     const int item = blockIdx.y;
-    const bool is_q = item < a.h_kt;
     const int64_t t_beg = (int64_t)blockIdx.x * a.chunk_tokens;
     int64_t t_end = t_beg + a.chunk_tokens;
     t_end = t_end < a.n ? t_end : a.n;
-    const int64_t ntok = t_end > t_beg ? t_end - t_beg : 0;
+    const int ntok = (int)(t_end > t_beg ? t_end - t_beg : 0);
 
     int lo = 0, g = 1, ka = 0, kb = 0;
-    if (is_q) {
+    if (IS_Q) {
         lo = (item * a.h_q + a.h_kt - 1) / a.h_kt;                 // first j with j*h_kt/h_q >= item
         const int hi = ((item + 1) * a.h_q + a.h_kt - 1) / a.h_kt;
         g = hi - lo;
     } else {
-        ka = a.pa[item - a.h_kt];
-        kb = a.pb[item - a.h_kt];
+        ka = a.pa[item];
+        kb = a.pb[item];
     }
-    const int64_t n_samp = ntok * g;
-    const int64_t per_wave = ((n_samp + 15) / 16) * 4;             // multiple of 4
-    const int64_t s_beg = wave * per_wave;
-    int64_t s_end = s_beg + per_wave;
-    s_end = s_end < n_samp ? s_end : n_samp;
+    const int n_samp = ntok * g;                                    // block-local sample count
+    const int per_wave = ((n_samp + 15) / 16) * 4;                  // multiple of 4
+    const int s_beg = wave * per_wave;
+    const int s_end = min(s_beg + per_wave, n_samp);
     const int64_t ldk = (int64_t)a.h_kt * D;
 
-    f32x4v acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t s0 = s_beg; s0 < s_end; s0 += 4) {
-        const int64_t s = s0 + k;
+    // sample s (block-local) -> channel values of this lane, zero beyond s_end
+    auto load = [&](int s0, float (&x)[NB]) {
+        const int s = s0 + k;
         const bool ok = s < s_end;
-        const int64_t sc = ok ? s : s_beg;
-        float x[NB];
-        if (is_q) {
-            const int64_t t = t_beg + sc / g;
-            const int j = lo + (int)(sc % g);
-            const uint16_t *src = a.Q + (t * a.h_q + j) * D + 4 * i;
+        const int sc = ok ? s : s_beg;
+        if (IS_Q) {
+            const int tl = sc / g;
+            const int j = lo + (sc - tl * g);
+            const uint16_t *src = a.Q + ((t_beg + tl) * a.h_q + j) * D + 4 * i;
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 const uint2 w = *(const uint2 *)(src + 64 * h);
@@ -230,6 +224,12 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
 #pragma unroll
             for (int I = 0; I < NB; ++I) x[I] = 0.f;
         }
+    };
+
+    f32x4v acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    auto accumulate = [&](const float (&x)[NB]) {
 #pragma unroll
         for (int I = 0; I < NB; ++I)
 #pragma unroll
@@ -237,16 +237,29 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
                 const int t = I * NB - I * (I - 1) / 2 + (J - I);   // tile index of (I, J)
                 acc[t] = mfma4(x[I], x[J], acc[t]);
             }
+    };
+
+    if (s_beg < s_end) {
+        float xa[NB], xb[NB];
+        load(s_beg, xa);
+        for (int s0 = s_beg;; s0 += 8) {
+            load(s0 + 4, xb);
+            accumulate(xa);
+            if (s0 + 4 >= s_end) break;
+            load(s0 + 8, xa);
+            accumulate(xb);
+            if (s0 + 8 >= s_end) break;
+        }
     }
 
     // Sum the four waves' tiles into LDS one wave at a time, mirroring I < J tiles.
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
-            int t = 0;
 #pragma unroll
             for (int I = 0; I < NB; ++I)
 #pragma unroll
-                for (int J = I; J < NB; ++J, ++t)
+                for (int J = I; J < NB; ++J) {
+                    const int t = I * NB - I * (I - 1) / 2 + (J - I);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = chan(I, 4 * k + r), col = chan(J, i);
@@ -259,6 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
                             if (I != J) red[col * D + row] += v;
                         }
                     }
+                }
         }
         __syncthreads();
     }
@@ -267,9 +281,9 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
 }
 
 struct ReduceArgs {
-    const float *part;   // [items][n_chunk][D*D]
-    float *out;          // [items][D*D]
-    int n_chunk;
+    const float *part;   // [h_kt][nq][D*D] then [P][nd][D*D]
+    float *out;          // [h_kt + P][D*D]
+    int h_kt, nq, nd;
     int dd;              // D*D
 };
 
@@ -278,227 +292,327 @@ __global__ __launch_bounds__(kThreads) void k_gram_reduce(ReduceArgs a) {
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= a.dd) return;
     const int item = blockIdx.y;
-    const float *p = a.part + (int64_t)item * a.n_chunk * a.dd + e;
-    double s = 0.0;
-    for (int c = 0; c < a.n_chunk; ++c) s += (double)p[(int64_t)c * a.dd];
-    a.out[(int64_t)item * a.dd + e] = (float)s;
+    const bool q = item < a.h_kt;
+    const int nc = q ? a.nq : a.nd;
+    const int64_t base = q ? (int64_t)item * a.nq * a.dd
+                           : ((int64_t)a.h_kt * a.nq + (int64_t)(item - a.h_kt) * a.nd) * a.dd;
+    const float *p = a.part + base + e;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+        s0 += (double)p[(int64_t)(c + 0) * a.dd];
+        s1 += (double)p[(int64_t)(c + 1) * a.dd];
+        s2 += (double)p[(int64_t)(c + 2) * a.dd];
+        s3 += (double)p[(int64_t)(c + 3) * a.dd];
+    }
+    for (; c < nc; ++c) s0 += (double)p[(int64_t)c * a.dd];
+    a.out[(int64_t)item * a.dd + e] = (float)((s0 + s1) + (s2 + s3));
 }
 
-// --------------------------------------------- 3. eigendecomposition per pair
+// --------------------------------------------- 3. pseudoinverse per pair
 
-struct EigArgs {
+struct PinvArgs {
     const float *SG;     // [h_kt + P][D][D]: S_r, then G_p
-    float *V;            // [P][D][D] eigenvectors (column i = vector i)
-    float *lam;          // [P][D]
+    float *Sp;           // [P][D][D] output: (S_a + S_b)^+
+    int *rank;           // [P] numerical rank
     int h_kt;
     uint8_t pa[kMaxPairs], pb[kMaxPairs];
 };
 
-// Partner slots of the round-robin (circle) schedule: in round k of a sweep the
-// D indices are split into D/2 disjoint pairs (slot(k, m), slot(k, D-1-m));
-// over D-1 rounds every pair of indices meets once.
-__device__ __forceinline__ int rr_slot(int k, int m, int D) {
-    return m == 0 ? 0 : 1 + (m - 1 + k) % (D - 1);
+// C tile (i0, j0) of a product of two LDS matrices (row stride LD), MFMA 16x16x4:
+// C[i][j] = sum_k X(i, k) Y(k, j) with X(i, k) = XT ? X[k][i] : X[i][k] and
+// Y(k, j) = YT ? Y[j][k] : Y[k][j].
+template <int D, int LD, bool XT, bool YT>
+__device__ __forceinline__ f32x4v lds_tile_mm(const float *X, const float *Y, int i0, int j0,
+                                              int lane) {
+    const int k = lane >> 4, i = lane & 15;
+    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k0 = 0; k0 < D; k0 += 4) {
+        const float xa = XT ? X[(k0 + k) * LD + i0 + i] : X[(i0 + i) * LD + k0 + k];
+        const float yb = YT ? Y[(j0 + i) * LD + k0 + k] : Y[(k0 + k) * LD + j0 + i];
+        acc = mfma4(xa, yb, acc);
+    }
+    return acc;
 }
 
-// Cyclic Jacobi eigenvalue method (two-sided rotations, parallel round-robin
-// ordering) on S = S_a + S_b, one block per pair, A and V in LDS with rows
-// padded to D+1 words (row and column sweeps then hit distinct banks).  A
-// rotation is skipped when |a_pq| is at rounding level relative to the
-// geometric mean of its diagonal pair (or to ||S||_F); the sweeps stop when a
-// whole sweep rotates nothing.
+// Up to 64 floats held in four separate 16-entry register vectors (unused ones
+// are dead code).  vget/vput with a compile-time m fold to a plain register; with
+// a wave-uniform runtime m they compile to one M0-relative register move.
+typedef float vec16 __attribute__((ext_vector_type(16)));
+template <int NV>
+__device__ __forceinline__ float vget(const vec16 &v0, const vec16 &v1, const vec16 &v2,
+                                      const vec16 &v3, int m) {
+    if (NV == 1 || m < 16) return v0[m & 15];
+    if (NV == 2 || m < 32) return v1[m & 15];
+    if (NV == 3 || m < 48) return v2[m & 15];
+    return v3[m & 15];
+}
+template <int NV>
+__device__ __forceinline__ void vput(vec16 &v0, vec16 &v1, vec16 &v2, vec16 &v3, int m, float x) {
+    if (NV == 1 || m < 16) v0[m & 15] = x;
+    else if (NV == 2 || m < 32) v1[m & 15] = x;
+    else if (NV == 3 || m < 48) v2[m & 15] = x;
+    else v3[m & 15] = x;
+}
+
+// Moore-Penrose pseudoinverse of S = S_a + S_b, one block per pair:
+//  1. diagonally pivoted Cholesky, S ~ L L^T with L's rows in the original
+//     order: each step takes the largest remaining diagonal of the Schur
+//     complement as pivot j, column k of L is that complement's column j over
+//     sqrt(pivot), and its outer product is subtracted; the factorisation stops
+//     when the pivot is at or below kPivotRtol * max_i S_ii (numerical rank r);
+//  2. M = L^T L (r x r, positive definite) is inverted by r symmetric sweeps
+//     (the SWEEP operator keeps the matrix symmetric, so a sweep's pivot column
+//     is its pivot row; after all r sweeps the block holds -M^-1);
+//  3. S^+ = (L L^T)^+ = Y Y^T with Y = L M^-1 (L has full column rank).
+// The working matrix lives in registers: thread t owns column c = t % D and the
+// R consecutive rows d0 .. d0+R-1, d0 = (t / D) R, the same for a whole wave.
+// Both the Schur complement and the swept matrix are symmetric, so a step's
+// pivot column is its pivot row: the waves holding that row publish it with
+// one store per lane (a wave-uniform register index), and every thread reads
+// its rows' entries back as broadcasts.  Each wave keeps its own copy of the
+// diagonal (lane e holds entries e, e + 64) for the pivot search, so a step
+// costs one barrier.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_pair_eig(EigArgs a) {
-    constexpr int LD = D + 1;
-    constexpr int H = D / 2;
+__global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
+    constexpr int LD = D + 4;          // 16-byte rows; 16 x 4 MFMA operand reads hit 64 banks
+    constexpr int NB = D / 16;
+    constexpr int R = D * D / kThreads;
+    constexpr int EPL = D / 64;        // diagonal entries per lane
+    constexpr int NT = NB * NB / 4;    // output tiles per wave
     extern __shared__ float sm[];
-    float *A = sm;
-    float *V = sm + D * LD;
-    float *rc = V + D * LD;          // [H] cos
-    float *rs = rc + H;              // [H] sin
-    int *rp = (int *)(rs + H);       // [H]
-    int *rq = rp + H;                // [H]
-    int *flag = rq + H;              // [1]
-    float *wsum = (float *)(flag + 1);   // [4]
-    const int tid = threadIdx.x;
+    float *Lt = sm;                    // [D][LD] row k = column k of L; later Y (row-major)
+    float *Mb = sm + D * LD;           // [D][LD] M, later M^-1
+    float *cb = Mb + D * LD;           // [2][D] published pivot row of the sweep
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = tid % D;
+    const int d0 = (tid / D) * R;      // wave-uniform
     const int p = blockIdx.x;
     const float *Sa = a.SG + (int64_t)a.pa[p] * D * D;
     const float *Sb = a.SG + (int64_t)a.pb[p] * D * D;
 
-    float fro = 0.f;
-    for (int e = tid; e < D * D; e += kThreads) {
-        const int r = e / D, c = e % D;
-        const float v = 0.5f * ((Sa[r * D + c] + Sb[r * D + c]) + (Sa[c * D + r] + Sb[c * D + r]));
-        A[r * LD + c] = v;
-        V[r * LD + c] = (r == c) ? 1.f : 0.f;
-        fro += v * v;
+    // The owned rows sit in separate 16-entry register vectors: an entry picked
+    // by a wave-uniform index compiles to M0-relative register moves.
+    constexpr int NV = R / 16;
+    vec16 A0 = {}, A1 = {}, A2 = {}, A3 = {};
+#define AGET(m) vget<NV>(A0, A1, A2, A3, (m))
+#define APUT(m, x) vput<NV>(A0, A1, A2, A3, (m), (x))
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+        const int r = d0 + m;
+        APUT(m, 0.5f * ((Sa[r * D + c] + Sb[r * D + c]) + (Sa[c * D + r] + Sb[c * D + r])));
     }
-    fro = wave_sum(fro);
-    if ((tid & 63) == 0) wsum[tid >> 6] = fro;
-    __syncthreads();
-    fro = sqrtf(wsum[0] + wsum[1] + wsum[2] + wsum[3]);
-    const float abs_floor = 1.4901161193847656e-08f * fro;   // 2^-26 ||S||_F
+    float dg[EPL];
+    bool ddone[EPL];
+#pragma unroll
+    for (int h = 0; h < EPL; ++h) {
+        const int e = lane + 64 * h;
+        dg[h] = Sa[e * D + e] + Sb[e * D + e];
+        ddone[h] = false;
+    }
+    bool cdone = false;                // this thread's column already eliminated
+    for (int e = tid; e < D * LD; e += kThreads) Lt[e] = 0.f;
+    float mx = 0.f;
+#pragma unroll
+    for (int h = 0; h < EPL; ++h) mx = fmaxf(mx, dg[h]);
+    const float stop = kPivotRtol * fkey_inv(wave_max_u32_dpp(fkey(mx)));
 
-    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-        if (tid == 0) *flag = 0;
-        __syncthreads();
-        for (int k = 0; k < D - 1; ++k) {
-            if (tid < H) {
-                int pp = rr_slot(k, tid, D), qq = rr_slot(k, D - 1 - tid, D);
-                if (pp > qq) { const int x = pp; pp = qq; qq = x; }
-                const float app = A[pp * LD + pp], aqq = A[qq * LD + qq], apq = A[pp * LD + qq];
-                float c = 1.f, s = 0.f;
-                const float thr = 1.1920928955078125e-07f * sqrtf(fabsf(app * aqq)) + abs_floor;
-                if (fabsf(apq) > thr) {
-                    const float theta = (aqq - app) / (2.f * apq);
-                    // tan of the rotation angle, the root of t^2 + 2 theta t - 1 = 0 of
-                    // smaller magnitude (1/(2 theta) once theta^2 would overflow)
-                    const float t = fabsf(theta) > 1e18f
-                                        ? 0.5f / theta
-                                        : (theta >= 0.f ? 1.f : -1.f) /
-                                              (fabsf(theta) + sqrtf(1.f + theta * theta));
-                    c = 1.f / sqrtf(1.f + t * t);
-                    s = t * c;
-                    *flag = 1;
-                }
-                rp[tid] = pp;
-                rq[tid] = qq;
-                rc[tid] = c;
-                rs[tid] = s;
-            }
-            __syncthreads();
-            // columns: A <- A J, V <- V J
-            for (int u = tid; u < D * H; u += kThreads) {
-                const int m = u % H, r = u / H;
-                const int pp = rp[m], qq = rq[m];
-                const float c = rc[m], s = rs[m];
-                const float x = A[r * LD + pp], y = A[r * LD + qq];
-                A[r * LD + pp] = c * x - s * y;
-                A[r * LD + qq] = s * x + c * y;
-                const float vx = V[r * LD + pp], vy = V[r * LD + qq];
-                V[r * LD + pp] = c * vx - s * vy;
-                V[r * LD + qq] = s * vx + c * vy;
-            }
-            __syncthreads();
-            // rows: A <- J^T A
-            for (int u = tid; u < D * H; u += kThreads) {
-                const int m = u % H, r = u / H;
-                const int pp = rp[m], qq = rq[m];
-                const float c = rc[m], s = rs[m];
-                const float x = A[pp * LD + r], y = A[qq * LD + r];
-                A[pp * LD + r] = c * x - s * y;
-                A[qq * LD + r] = s * x + c * y;
-            }
-            __syncthreads();
+    auto pivot = [&](float &pv, int &j) {
+        uint32_t best = 0u;
+        int bi = 0;
+#pragma unroll
+        for (int h = 0; h < EPL; ++h) {
+            const uint32_t key = ddone[h] ? 0u : fkey(dg[h]);
+            if (key > best) { best = key; bi = lane + 64 * h; }
         }
-        if (*flag == 0) break;
+        const uint32_t top = wave_max_u32_dpp(best);
+        const uint64_t who = ballot(best == top);
+        j = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(who));
+        pv = top ? fkey_inv(top) : -INFINITY;
+    };
+    __syncthreads();                   // Lt cleared
+
+    float pv;
+    int j;
+    pivot(pv, j);
+    int r = 0;
+    for (int k = 0; k < D; ++k) {
+        if (!(pv > stop)) break;       // uniform: every wave found the same pivot
+        const float inv = __builtin_amdgcn_rsqf(pv);
+        const float ljj = pv * inv;
+        float *lk = Lt + k * LD;
+        if (j >= d0 && j < d0 + R) {   // this wave holds row j (= column j)
+            const float aj = AGET(__builtin_amdgcn_readfirstlane(j - d0));
+            const float v = (c == j) ? ljj : (cdone ? 0.f : aj * inv);
+            lk[c] = v;
+        }
         __syncthreads();
+        const float cc = lk[c];
+        const float4 *cr = (const float4 *)(lk + d0);
+#pragma unroll
+        for (int q = 0; q < R / 4; ++q) {
+            const float4 v = cr[q];
+            APUT(4 * q + 0, AGET(4 * q + 0) - v.x * cc);
+            APUT(4 * q + 1, AGET(4 * q + 1) - v.y * cc);
+            APUT(4 * q + 2, AGET(4 * q + 2) - v.z * cc);
+            APUT(4 * q + 3, AGET(4 * q + 3) - v.w * cc);
+        }
+#pragma unroll
+        for (int h = 0; h < EPL; ++h) {
+            const float ce = lk[lane + 64 * h];
+            dg[h] -= ce * ce;
+            ddone[h] = ddone[h] || (lane + 64 * h == j);
+        }
+        cdone = cdone || (c == j);
+        r = k + 1;
+        pivot(pv, j);
     }
-    float *Vo = a.V + (int64_t)p * D * D;
-    for (int e = tid; e < D * D; e += kThreads) Vo[e] = V[(e / D) * LD + e % D];
-    if (tid < D) a.lam[(int64_t)p * D + tid] = A[tid * LD + tid];
+    __syncthreads();
+
+    // M = L^T L = Lt Lt^T into Mb (zero outside the leading r x r block)
+    for (int t = wave; t < NB * NB; t += 4) {
+        const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
+        const f32x4v v = lds_tile_mm<D, LD, false, true>(Lt, Lt, i0, j0, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Mb[(i0 + 4 * (lane >> 4) + q) * LD + j0 + (lane & 15)] = v[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < R; ++m) APUT(m, Mb[(d0 + m) * LD + c]);
+    // r symmetric sweeps: entry (i, c) -> A - f_i f_c / f_k off row/column k,
+    // f_i / f_k in column k (and row k), -1 / f_k at (k, k), f = pivot row k
+    for (int k = 0; k < r; ++k) {
+        float *f = cb + (k & 1) * D;
+        const bool own = k >= d0 && k < d0 + R;
+        if (own) f[c] = AGET(__builtin_amdgcn_readfirstlane(k - d0));
+        __syncthreads();
+        const float ip = 1.f / f[k];
+        const float fc = f[c];
+        const float s = (c == k) ? 0.f : 1.f;
+        const float t = (c == k) ? ip : -fc * ip;
+        const float4 *fr = (const float4 *)(f + d0);
+#pragma unroll
+        for (int q = 0; q < R / 4; ++q) {
+            const float4 v = fr[q];
+            APUT(4 * q + 0, AGET(4 * q + 0) * s + v.x * t);
+            APUT(4 * q + 1, AGET(4 * q + 1) * s + v.y * t);
+            APUT(4 * q + 2, AGET(4 * q + 2) * s + v.z * t);
+            APUT(4 * q + 3, AGET(4 * q + 3) * s + v.w * t);
+        }
+        if (own) APUT(__builtin_amdgcn_readfirstlane(k - d0), (c == k) ? -ip : fc * ip);
+    }
+    __syncthreads();                   // every thread is done reading Mb and cb
+#pragma unroll
+    for (int m = 0; m < R; ++m) Mb[(d0 + m) * LD + c] = -AGET(m);
+    __syncthreads();
+    // Y = L M^-1 (Y(i, c) = sum_k Lt[k][i] M^-1[k][c]); each wave keeps its tiles
+    // in registers until every wave has finished reading Lt
+    f32x4v y[NT];
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = wave + 4 * q;
+        y[q] = lds_tile_mm<D, LD, true, false>(Lt, Mb, (t / NB) * 16, (t % NB) * 16, lane);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = wave + 4 * q;
+        const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Lt[(i0 + 4 * (lane >> 4) + u) * LD + j0 + (lane & 15)] = y[q][u];
+    }
+    __syncthreads();
+    // S^+ = Y Y^T
+    float *out = a.Sp + (int64_t)p * D * D;
+    for (int t = wave; t < NB * NB; t += 4) {
+        const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
+        const f32x4v v = lds_tile_mm<D, LD, false, true>(Lt, Lt, i0, j0, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[(i0 + 4 * (lane >> 4) + q) * D + j0 + (lane & 15)] = v[q];
+    }
+    if (tid == 0) a.rank[p] = r;
+#undef AGET
+#undef APUT
 }
 
 // ------------------------------------------------ 4. pair loss and merge maps
 
 struct LossArgs {
     const float *SG;     // [h_kt + P][D][D]
-    const float *V;      // [P][D][D]
-    const float *lam;    // [P][D]
-    float *Sp;           // [P][D][D] scratch: S^+
+    const float *Sp;     // [P][D][D] (S_a + S_b)^+
     float *Pm;           // [P][2][D][D]: P_a = S_a S^+, P_b = S_b S^+
     double *w;           // [h_kt][h_kt] pair losses (output)
     int h_kt;
     uint8_t pa[kMaxPairs], pb[kMaxPairs];
 };
 
-// C tile (i0, j0) of X Y (or X Y^T) with MFMA 16x16x4, operands read from
-// global memory (each block's matrices are a few tens of KB, L2/L1 resident).
-template <int D, bool YT>
-__device__ __forceinline__ f32x4v tile_mm(const float *X, const float *Y, int i0, int j0, int lane,
-                                          const float *colscale = nullptr) {
+// C tile (i0, j0) of X Y with MFMA 16x16x4, operands (row-major D x D, global
+// memory, L2/L1 resident) all loaded before the multiply chain starts.
+template <int D>
+__device__ __forceinline__ f32x4v tile_mm(const float *X, const float *Y, int i0, int j0, int lane) {
     const int k = lane >> 4, i = lane & 15;
-    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-        float xa = X[(i0 + i) * D + k0 + k];
-        if (colscale) xa *= colscale[k0 + k];
-        const float yb = YT ? Y[(j0 + i) * D + k0 + k] : Y[(k0 + k) * D + j0 + i];
-        acc = mfma4(xa, yb, acc);
+    float xa[D / 4], yb[D / 4];
+#pragma unroll
+    for (int s = 0; s < D / 4; ++s) {
+        xa[s] = X[(i0 + i) * D + 4 * s + k];
+        yb[s] = Y[(4 * s + k) * D + j0 + i];
     }
+    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 4; ++s) acc = mfma4(xa[s], yb[s], acc);
     return acc;
 }
 
-template <int D>
-__device__ __forceinline__ void tile_store(float *C, f32x4v v, int i0, int j0, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) C[(i0 + 4 * (lane >> 4) + r) * D + j0 + (lane & 15)] = v[r];
-}
+constexpr int kLossThreads = 512;
 
-// One block per pair: S^+ from the eigenpairs (cutoff kEigRtol * max eigenvalue),
-// P_a, P_b, and the pair's eq. 13 cost as <G P_b, P_b S_a> + <G P_a, P_a S_b>.
+// One block per pair: P_a = S_a S^+, P_b = S_b S^+, and the pair's eq. 13 cost as
+// <G P_b, P_b S_a> + <G P_a, P_a S_b>.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_pair_loss(LossArgs a) {
+__global__ __launch_bounds__(kLossThreads) void k_pair_loss(LossArgs a) {
     constexpr int NB = D / 16;
-    __shared__ float inv[D];
-    __shared__ double dsum[4];
+    constexpr int NW = kLossThreads / 64;
+    __shared__ double dsum[NW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = blockIdx.x;
     const int ia = a.pa[p], ib = a.pb[p];
-    const int P = a.h_kt * (a.h_kt - 1) / 2;
     const float *Sa = a.SG + (int64_t)ia * D * D;
     const float *Sb = a.SG + (int64_t)ib * D * D;
     const float *G = a.SG + (int64_t)(a.h_kt + p) * D * D;
-    const float *V = a.V + (int64_t)p * D * D;
-    const float *lam = a.lam + (int64_t)p * D;
-    float *Sp = a.Sp + (int64_t)p * D * D;
+    const float *Sp = a.Sp + (int64_t)p * D * D;
     float *Pa = a.Pm + (int64_t)p * 2 * D * D;
     float *Pb = Pa + D * D;
 
-    if (tid < 64) {
-        float m = -INFINITY;
-        for (int e = tid; e < D; e += 64) m = fmaxf(m, lam[e]);
-        m = wave_max(m);
-        for (int e = tid; e < D; e += 64) {
-            const float l = lam[e];
-            inv[e] = (m > 0.f && l > kEigRtol * m) ? 1.f / l : 0.f;
-        }
-    }
-    __syncthreads();
-    // S^+ = V diag(inv) V^T
-    for (int t = wave; t < NB * NB; t += 4) {
-        const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
-        tile_store<D>(Sp, tile_mm<D, true>(V, V, i0, j0, lane, inv), i0, j0, lane);
-    }
-    __syncthreads();
-    for (int t = wave; t < 2 * NB * NB; t += 4) {
+    for (int t = wave; t < 2 * NB * NB; t += NW) {
         const int which = t / (NB * NB), tt = t % (NB * NB);
         const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
-        tile_store<D>(which ? Pb : Pa, tile_mm<D, false>(which ? Sb : Sa, Sp, i0, j0, lane), i0, j0,
-                      lane);
+        const f32x4v v = tile_mm<D>(which ? Sb : Sa, Sp, i0, j0, lane);
+        float *C = which ? Pb : Pa;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) C[(i0 + 4 * (lane >> 4) + q) * D + j0 + (lane & 15)] = v[q];
     }
     __syncthreads();
     double part = 0.0;
-    for (int t = wave; t < 2 * NB * NB; t += 4) {
+    for (int t = wave; t < 2 * NB * NB; t += NW) {
         const int which = t / (NB * NB), tt = t % (NB * NB);
         const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
         const float *Pm = which ? Pa : Pb;           // term a uses P_b, term b uses P_a
         const float *Sx = which ? Sb : Sa;
-        const f32x4v u = tile_mm<D, false>(G, Pm, i0, j0, lane);
-        const f32x4v v = tile_mm<D, false>(Pm, Sx, i0, j0, lane);
+        const f32x4v u = tile_mm<D>(G, Pm, i0, j0, lane);
+        const f32x4v v = tile_mm<D>(Pm, Sx, i0, j0, lane);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += (double)u[r] * (double)v[r];
+        for (int q = 0; q < 4; ++q) part += (double)u[q] * (double)v[q];
     }
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if (lane == 0) dsum[wave] = part;
     __syncthreads();
     if (tid == 0) {
-        const double L = dsum[0] + dsum[1] + dsum[2] + dsum[3];
+        double L = 0.0;
+        for (int w = 0; w < NW; ++w) L += dsum[w];
         a.w[ia * a.h_kt + ib] = L;
         a.w[ib * a.h_kt + ia] = L;
     }
     if (p == 0 && tid < a.h_kt) a.w[tid * a.h_kt + tid] = 0.0;
-    (void)P;
 }
 
 // ------------------------------------------------------------ 5. matching
@@ -576,34 +690,44 @@ struct WeightArgs {
     int dm, h_kt;
 };
 
+constexpr int kWCh = 8;   // output channels per thread
+
 // out row i*D + c, column x = sum_e W[a*D+e][x] P_a[e][c] + W[b*D+e][x] P_b[e][c]
-// (eq. 15 in the weight layout: merged head i = pair (a, b) = pairs[i]).
+// (eq. 15 in the weight layout: merged head i = pair (a, b) = pairs[i]).  Block
+// (i, channel group, column range): the group's columns of P_a and P_b sit in LDS,
+// each thread owns one column x of the output and kWCh channels.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_merged_weight(WeightArgs a) {
-    extern __shared__ float sm[];
-    float *Pa = sm, *Pb = sm + D * D;
+    __shared__ float Pa[D][kWCh], Pb[D][kWCh];
     const int tid = threadIdx.x;
-    const int hi = blockIdx.x;
+    const int hi = blockIdx.x, c0 = blockIdx.y * kWCh;
     const int ia = a.pairs[2 * hi], ib = a.pairs[2 * hi + 1];
     if (ia < 0 || ib <= ia || ib >= a.h_kt) return;      // uniform per block
     const int p = ia * (2 * a.h_kt - ia - 1) / 2 + (ib - ia - 1);
     const float *src = a.Pm + (int64_t)p * 2 * D * D;
-    for (int e = tid; e < 2 * D * D; e += kThreads) sm[e] = src[e];
-    __syncthreads();
-    const int x = blockIdx.y * kThreads + tid;
-    if (x >= a.dm) return;
-    float acc[D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] = 0.f;
-    for (int e = 0; e < D; ++e) {
-        const float wa = __uint_as_float((uint32_t)a.W[(int64_t)(ia * D + e) * a.dm + x] << 16);
-        const float wb = __uint_as_float((uint32_t)a.W[(int64_t)(ib * D + e) * a.dm + x] << 16);
-#pragma unroll
-        for (int c = 0; c < D; ++c) acc[c] += wa * Pa[e * D + c] + wb * Pb[e * D + c];
+    for (int e = tid; e < D * kWCh; e += kThreads) {
+        const int r = e / kWCh, c = e % kWCh;
+        Pa[r][c] = src[r * D + c0 + c];
+        Pb[r][c] = src[D * D + r * D + c0 + c];
     }
-    float *o = a.out + (int64_t)hi * D * a.dm + x;
+    __syncthreads();
+    const int x = blockIdx.z * kThreads + tid;
+    if (x >= a.dm) return;
+    float acc[kWCh];
 #pragma unroll
-    for (int c = 0; c < D; ++c) o[(int64_t)c * a.dm] = acc[c];
+    for (int c = 0; c < kWCh; ++c) acc[c] = 0.f;
+    const uint16_t *wa = a.W + (int64_t)ia * D * a.dm + x;
+    const uint16_t *wb = a.W + (int64_t)ib * D * a.dm + x;
+#pragma unroll 4
+    for (int e = 0; e < D; ++e) {
+        const float va = __uint_as_float((uint32_t)wa[(int64_t)e * a.dm] << 16);
+        const float vb = __uint_as_float((uint32_t)wb[(int64_t)e * a.dm] << 16);
+#pragma unroll
+        for (int c = 0; c < kWCh; ++c) acc[c] += va * Pa[e][c] + vb * Pb[e][c];
+    }
+    float *o = a.out + (int64_t)(hi * D + c0) * a.dm + x;
+#pragma unroll
+    for (int c = 0; c < kWCh; ++c) o[(int64_t)c * a.dm] = acc[c];
 }
 
 }  // namespace merge
