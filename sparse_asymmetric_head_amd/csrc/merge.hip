@@ -6,13 +6,17 @@
 //   k_gram<D,0>      per-chunk second moments G_p of K_a - K_b         (one item per pair)
 //   k_gram_reduce    fixed-order fp64 sum over chunks
 //   k_pair_pinv<D>   (S_a + S_b)^+ by a rank-revealing Cholesky        (one block per pair)
-//   k_pair_loss<D>   P_a, P_b and the eq. 13 cost                      (one block per pair)
-//   k_match          minimum-weight perfect matching                   (one block)
+//   k_pair_maps<D>   P_a = S_a S^+, P_b = S_b S^+               (pairs x tile groups)
+//   k_pair_cost<D>   partial eq. 13 costs                          (pairs x tile groups)
+//   k_match          pair costs from the partials, then the minimum-weight perfect
+//                    matching                                          (one block)
 //   k_merged_weight  eq. 15 in the weight layout     (h_kt/2 x d/8 x d_model/256 blocks)
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
+
+#include <algorithm>
 
 #include "../../include/saga_merge.h"
 #include "merge_kernels.hpp"
@@ -25,13 +29,17 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int64_t kTargetGramBlocks = 1024;   // about four blocks per compute unit
+constexpr int64_t kGramBlockBudget = 32768;   // Gram blocks per launch times d
+constexpr int64_t kMinGramBlocks = 128;
+
+// tile groups per pair in the map and cost kernels (2 (d/16)^2 tiles, 4 per block)
+int cost_parts(int d) { return 2 * (d / 16) * (d / 16) / kTilesPerBlock; }
 
 struct MergePlan {
     int64_t n;
     int h_q, h_kt, d, dm, P, items, nq, nd;
     int64_t ct_q, ct_d;   // tokens per Gram block: query items, key-difference items
-    size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_rank, off_dp, off_choice, bytes;
+    size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_cost, off_rank, off_dp, off_choice, bytes;
 };
 
 int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan *p) {
@@ -48,14 +56,19 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     p->dm = d_model;
     p->P = h_kt * (h_kt - 1) / 2;
     p->items = h_kt + p->P;
-    // Samples per Gram block: enough that a block's input outweighs its d x d
-    // partial (at least 16 d samples), and about kTargetGramBlocks blocks overall.
+    // Samples per Gram block, per launch (measured on both layer shapes): about
+    // kGramBlockBudget / d blocks -- a d x d partial costs d^2 words to write and
+    // reduce, and the d = 128 kernel runs one wave per SIMD -- with at least 4 d
+    // samples per block; key-difference blocks take at least 16 d samples unless
+    // that leaves fewer than kMinGramBlocks blocks.
     const int64_t g_max = ceil_div(h_q, h_kt);
-    const int64_t total = n * h_q + n * p->P;
-    int64_t s_blk = ceil_div(total, kTargetGramBlocks);
-    s_blk = s_blk > 16 * d ? s_blk : 16 * d;
-    p->ct_q = ceil_div(s_blk, g_max);
-    p->ct_d = s_blk;
+    const int64_t target = kGramBlockBudget / d;
+    const int64_t s_q = std::max<int64_t>(4 * d, ceil_div(n * h_q, target));
+    int64_t s_d = std::max<int64_t>(16 * d, ceil_div(n * p->P, target));
+    if (p->P * ceil_div(n, s_d) < kMinGramBlocks)
+        s_d = std::max<int64_t>(4 * d, ceil_div(n * p->P, kMinGramBlocks));
+    p->ct_q = ceil_div(s_q, g_max);
+    p->ct_d = s_d;
     p->nq = (int)ceil_div(n, p->ct_q);
     p->nd = (int)ceil_div(n, p->ct_d);
     const size_t dd = (size_t)d * d * sizeof(float);
@@ -65,6 +78,7 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     p->off_SG = o;     o = align_up(o + (size_t)p->items * dd);
     p->off_Sp = o;     o = align_up(o + (size_t)p->P * dd);
     p->off_Pm = o;     o = align_up(o + (size_t)p->P * 2 * dd);
+    p->off_cost = o;   o = align_up(o + (size_t)p->P * cost_parts(d) * sizeof(double));
     p->off_rank = o;   o = align_up(o + (size_t)p->P * sizeof(int));
     p->off_dp = o;     o = align_up(o + ((size_t)1 << h_kt) * sizeof(double));
     p->off_choice = o; o = align_up(o + ((size_t)1 << h_kt));
@@ -123,13 +137,13 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     ga.part = part;
     ga.chunk_tokens = p.ct_q;
     ga.n_chunk = p.nq;
-    hipLaunchKernelGGL((k_gram<D, true>), dim3((unsigned)p.nq, (unsigned)p.h_kt), dim3(kThreads), 0,
-                       s, ga);
+    hipLaunchKernelGGL((k_gram<D, true>), dim3((unsigned)p.nq, (unsigned)p.h_kt, gram_groups(D)),
+                       dim3(kThreads), 0, s, ga);
     ga.part = part + (size_t)p.h_kt * p.nq * D * D;
     ga.chunk_tokens = p.ct_d;
     ga.n_chunk = p.nd;
-    hipLaunchKernelGGL((k_gram<D, false>), dim3((unsigned)p.nd, (unsigned)p.P), dim3(kThreads), 0,
-                       s, ga);
+    hipLaunchKernelGGL((k_gram<D, false>), dim3((unsigned)p.nd, (unsigned)p.P, gram_groups(D)),
+                       dim3(kThreads), 0, s, ga);
 
     ReduceArgs ra{part, SG, p.h_kt, p.nq, p.nd, D * D};
     hipLaunchKernelGGL(k_gram_reduce, dim3((unsigned)ceil_div(D * D, kThreads), (unsigned)p.items),
@@ -147,12 +161,18 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     la.SG = SG;
     la.Sp = Sp;
     la.Pm = Pm;
-    la.w = pair_loss;
+    la.part = (double *)(ws + p.off_cost);
     la.h_kt = p.h_kt;
+    la.n_part = cost_parts(D);
     pair_table(p.h_kt, la.pa, la.pb);
-    hipLaunchKernelGGL(k_pair_loss<D>, dim3((unsigned)p.P), dim3(kLossThreads), 0, s, la);
+    hipLaunchKernelGGL(k_pair_maps<D>, dim3((unsigned)p.P, (unsigned)cost_parts(D)), dim3(kThreads),
+                       0, s, la);
+    hipLaunchKernelGGL(k_pair_cost<D>, dim3((unsigned)p.P, (unsigned)cost_parts(D)), dim3(kThreads),
+                       0, s, la);
 
     MatchArgs ma{};
+    ma.part = (const double *)(ws + p.off_cost);
+    ma.n_part = cost_parts(D);
     ma.w = pair_loss;
     ma.dp = (double *)(ws + p.off_dp);
     ma.choice = (uint8_t *)(ws + p.off_choice);

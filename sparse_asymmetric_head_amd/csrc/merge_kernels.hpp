@@ -155,22 +155,32 @@ struct GramArgs {
 // channel order and un-permuted when written out.
 __device__ __forceinline__ int chan(int I, int i) { return 64 * (I >> 2) + 4 * i + (I & 3); }
 
-// One block per (item, token chunk).  IS_Q: item r = blockIdx.y, S_r, the second
-// moment of group r's query vectors (samples = (token, query head of the group)).
-// Otherwise item p = blockIdx.y, G_p, the second moment of K_a - K_b over tokens.
-// MFMA 16x16x4 fp32: lane (k = lane/16, i = lane%16) supplies sample k's channel
-// chan(I, i) as both the A (row) and B (column) operand, so each instruction adds
-// 4 samples' outer products to a 16 x 16 tile; only tiles I <= J are formed.  The
-// next 4 samples are loaded while the current ones are multiplied.
+// Tile groups of a Gram block: the (D/16)(D/16+1)/2 tiles I <= J of one item's
+// second moment are dealt round-robin to gram_groups(D) blocks (blockIdx.z) that
+// read the same samples, so that a d = 128 block holds a quarter of the
+// accumulators and the grid has four times the blocks.
+__host__ __device__ constexpr int gram_groups(int D) { return D >= 128 ? 4 : 1; }
+
+// One block per (item, token chunk, tile group).  IS_Q: item r = blockIdx.y, S_r,
+// the second moment of group r's query vectors (samples = (token, query head of
+// the group)).  Otherwise item p = blockIdx.y, G_p, the second moment of
+// K_a - K_b over tokens.  MFMA 16x16x4 fp32: lane (k = lane/16, i = lane%16)
+// supplies sample k's channel chan(I, i) as both the A (row) and B (column)
+// operand, so each instruction adds 4 samples' outer products to a 16 x 16 tile.
+// The next 4 samples are loaded while the current ones are multiplied.  The block
+// writes its tiles (and their mirror images) into the (item, chunk) partial.
 template <int D, bool IS_Q>
 __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     constexpr int NB = D / 16;                     // feature blocks
     constexpr int NT = NB * (NB + 1) / 2;          // tiles I <= J
+    constexpr int TG = gram_groups(D);
+    constexpr int NA = (NT + TG - 1) / TG;         // accumulator tiles per block
     constexpr int NH = D / 64;                     // float4 chunks per lane per sample
-    __shared__ float red[D * D];
+    __shared__ float red[NA * 256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int k = lane >> 4, i = lane & 15;
     const int item = blockIdx.y;
+    const int grp = blockIdx.z;
     const int64_t t_beg = (int64_t)blockIdx.x * a.chunk_tokens;
     int64_t t_end = t_beg + a.chunk_tokens;
     t_end = t_end < a.n ? t_end : a.n;
@@ -226,16 +236,17 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
         }
     };
 
-    f32x4v acc[NT];
+    f32x4v acc[NA];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NA; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    // tile t (row-major over I <= J) belongs to group t % TG, slot t / TG
     auto accumulate = [&](const float (&x)[NB]) {
 #pragma unroll
         for (int I = 0; I < NB; ++I)
 #pragma unroll
             for (int J = I; J < NB; ++J) {
-                const int t = I * NB - I * (I - 1) / 2 + (J - I);   // tile index of (I, J)
-                acc[t] = mfma4(x[I], x[J], acc[t]);
+                const int t = I * NB - I * (I - 1) / 2 + (J - I);
+                if (t % TG == grp) acc[t / TG] = mfma4(x[I], x[J], acc[t / TG]);
             }
     };
 
@@ -252,32 +263,34 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
         }
     }
 
-    // Sum the four waves' tiles into LDS one wave at a time, mirroring I < J tiles.
+    // Sum the four waves' tiles in LDS (slot-major, 256 words per tile), one wave
+    // at a time.
     for (int w = 0; w < 4; ++w) {
         if (wave == w) {
 #pragma unroll
-            for (int I = 0; I < NB; ++I)
+            for (int q = 0; q < NA; ++q)
 #pragma unroll
-                for (int J = I; J < NB; ++J) {
-                    const int t = I * NB - I * (I - 1) / 2 + (J - I);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = chan(I, 4 * k + r), col = chan(J, i);
-                        const float v = acc[t][r];
-                        if (w == 0) {
-                            red[row * D + col] = v;
-                            if (I != J) red[col * D + row] = v;
-                        } else {
-                            red[row * D + col] += v;
-                            if (I != J) red[col * D + row] += v;
-                        }
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const int e = q * 256 + (4 * k + r) * 16 + i;
+                    red[e] = (w == 0 ? 0.f : red[e]) + acc[q][r];
                 }
         }
         __syncthreads();
     }
+    // write the block's tiles and their mirror images into the partial
     float *dst = a.part + ((int64_t)item * a.n_chunk + blockIdx.x) * (D * D);
-    for (int e = tid; e < D * D; e += kThreads) dst[e] = red[e];
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+#pragma unroll
+        for (int J = I; J < NB; ++J) {
+            const int t = I * NB - I * (I - 1) / 2 + (J - I);
+            if (t % TG != grp) continue;
+            const int rr = tid >> 4, cc = tid & 15;              // 256 threads: one entry each
+            const float v = red[(t / TG) * 256 + rr * 16 + cc];
+            const int row = chan(I, rr), col = chan(J, cc);
+            dst[row * D + col] = v;
+            if (I != J) dst[col * D + row] = v;
+        }
 }
 
 struct ReduceArgs {
@@ -542,8 +555,8 @@ struct LossArgs {
     const float *SG;     // [h_kt + P][D][D]
     const float *Sp;     // [P][D][D] (S_a + S_b)^+
     float *Pm;           // [P][2][D][D]: P_a = S_a S^+, P_b = S_b S^+
-    double *w;           // [h_kt][h_kt] pair losses (output)
-    int h_kt;
+    double *part;        // [P][n_part] partial costs
+    int h_kt, n_part;
     uint8_t pa[kMaxPairs], pb[kMaxPairs];
 };
 
@@ -564,61 +577,58 @@ __device__ __forceinline__ f32x4v tile_mm(const float *X, const float *Y, int i0
     return acc;
 }
 
-constexpr int kLossThreads = 512;
+// Tiles of the 2 (D/16)^2-tile job of one pair handled by one 4-wave block.
+constexpr int kTilesPerBlock = 4;
 
-// One block per pair: P_a = S_a S^+, P_b = S_b S^+, and the pair's eq. 13 cost as
-// <G P_b, P_b S_a> + <G P_a, P_a S_b>.
+// P_a = S_a S^+ and P_b = S_b S^+: block (pair p, tile group), one tile per wave.
 template <int D>
-__global__ __launch_bounds__(kLossThreads) void k_pair_loss(LossArgs a) {
+__global__ __launch_bounds__(kThreads) void k_pair_maps(LossArgs a) {
     constexpr int NB = D / 16;
-    constexpr int NW = kLossThreads / 64;
-    __shared__ double dsum[NW];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = blockIdx.x;
-    const int ia = a.pa[p], ib = a.pb[p];
-    const float *Sa = a.SG + (int64_t)ia * D * D;
-    const float *Sb = a.SG + (int64_t)ib * D * D;
-    const float *G = a.SG + (int64_t)(a.h_kt + p) * D * D;
-    const float *Sp = a.Sp + (int64_t)p * D * D;
-    float *Pa = a.Pm + (int64_t)p * 2 * D * D;
-    float *Pb = Pa + D * D;
+    const int t = blockIdx.y * kTilesPerBlock + wave;          // < 2 NB^2 by the grid
+    const int which = t / (NB * NB), tt = t % (NB * NB);
+    const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
+    const float *S = a.SG + (int64_t)(which ? a.pb[p] : a.pa[p]) * D * D;
+    const f32x4v v = tile_mm<D>(S, a.Sp + (int64_t)p * D * D, i0, j0, lane);
+    float *C = a.Pm + ((int64_t)p * 2 + which) * D * D;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) C[(i0 + 4 * (lane >> 4) + q) * D + j0 + (lane & 15)] = v[q];
+}
 
-    for (int t = wave; t < 2 * NB * NB; t += NW) {
-        const int which = t / (NB * NB), tt = t % (NB * NB);
-        const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
-        const f32x4v v = tile_mm<D>(which ? Sb : Sa, Sp, i0, j0, lane);
-        float *C = which ? Pb : Pa;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) C[(i0 + 4 * (lane >> 4) + q) * D + j0 + (lane & 15)] = v[q];
-    }
-    __syncthreads();
+// Partial eq. 13 costs: the pair's cost is <G P_b, P_b S_a> + <G P_a, P_a S_b>;
+// block (pair p, tile group) forms one tile of both factors of one term per wave
+// and writes the group's fp64 partial sum.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_pair_cost(LossArgs a) {
+    constexpr int NB = D / 16;
+    __shared__ double dsum[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int p = blockIdx.x;
+    const int t = blockIdx.y * kTilesPerBlock + wave;
+    const int which = t / (NB * NB), tt = t % (NB * NB);
+    const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
+    const float *G = a.SG + (int64_t)(a.h_kt + p) * D * D;
+    const float *Pm = a.Pm + ((int64_t)p * 2 + (which ? 0 : 1)) * D * D;   // term a: P_b
+    const float *Sx = a.SG + (int64_t)(which ? a.pb[p] : a.pa[p]) * D * D;
+    const f32x4v u = tile_mm<D>(G, Pm, i0, j0, lane);
+    const f32x4v v = tile_mm<D>(Pm, Sx, i0, j0, lane);
     double part = 0.0;
-    for (int t = wave; t < 2 * NB * NB; t += NW) {
-        const int which = t / (NB * NB), tt = t % (NB * NB);
-        const int i0 = (tt / NB) * 16, j0 = (tt % NB) * 16;
-        const float *Pm = which ? Pa : Pb;           // term a uses P_b, term b uses P_a
-        const float *Sx = which ? Sb : Sa;
-        const f32x4v u = tile_mm<D>(G, Pm, i0, j0, lane);
-        const f32x4v v = tile_mm<D>(Pm, Sx, i0, j0, lane);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) part += (double)u[q] * (double)v[q];
-    }
+    for (int q = 0; q < 4; ++q) part += (double)u[q] * (double)v[q];
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if (lane == 0) dsum[wave] = part;
     __syncthreads();
-    if (tid == 0) {
-        double L = 0.0;
-        for (int w = 0; w < NW; ++w) L += dsum[w];
-        a.w[ia * a.h_kt + ib] = L;
-        a.w[ib * a.h_kt + ia] = L;
-    }
-    if (p == 0 && tid < a.h_kt) a.w[tid * a.h_kt + tid] = 0.0;
+    if (threadIdx.x == 0)
+        a.part[(int64_t)p * a.n_part + blockIdx.y] = (dsum[0] + dsum[1]) + (dsum[2] + dsum[3]);
 }
 
 // ------------------------------------------------------------ 5. matching
 
 struct MatchArgs {
-    const double *w;     // [h_kt][h_kt]
+    const double *part;  // [P][n_part] partial pair costs
+    int n_part;
+    double *w;           // [h_kt][h_kt] pair costs (written here)
     double *dp;          // [2^h_kt]
     uint8_t *choice;     // [2^h_kt]
     int32_t *pairs;      // [h_kt/2][2] output
@@ -634,6 +644,18 @@ struct MatchArgs {
 __global__ __launch_bounds__(kThreads) void k_match(MatchArgs a) {
     const int tid = threadIdx.x;
     const int h = a.h_kt;
+    // pair costs: fixed-order sums of the partials, mirrored, zero diagonal
+    for (int p = tid; p < h * (h - 1) / 2; p += kThreads) {
+        int i = 0, rest = p;
+        while (rest >= h - 1 - i) { rest -= h - 1 - i; ++i; }
+        const int j = i + 1 + rest;
+        double L = 0.0;
+        for (int q = 0; q < a.n_part; ++q) L += a.part[(int64_t)p * a.n_part + q];
+        a.w[i * h + j] = L;
+        a.w[j * h + i] = L;
+    }
+    if (tid < h) a.w[tid * h + tid] = 0.0;
+    __syncthreads();
     if (a.forced) {
         if (tid == 0) {
             double tot = 0.0;
