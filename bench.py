@@ -33,16 +33,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_select_traffic_llama32-1b-128k-
 DOMINANT = "saga::k_select<64, 1, false>"
 
 
+# The sources the decode-step kernels are built from (the key-merge sources,
+# merge.hip and merge_kernels.hpp, do not touch them).
+DECODE_SOURCES = ("saga.hip", "saga_device.hpp", "saga_kernels.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources, so counter figures taken for other code are not reused."""
+    """sha256 over the decode path's HIP sources, so counter figures taken for other
+    code are not reused."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_asymmetric_head_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in sorted(DECODE_SOURCES):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
