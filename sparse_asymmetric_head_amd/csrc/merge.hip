@@ -39,6 +39,7 @@ struct MergePlan {
     int64_t n;
     int h_q, h_kt, d, dm, P, items, nq, nd;
     int64_t ct_q, ct_d;   // tokens per Gram block: query items, key-difference items
+    int64_t ldt;          // token stride of the channel-major keys (n rounded up to 128)
     size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_cost, off_rank, off_dp, off_choice, bytes;
 };
 
@@ -58,22 +59,23 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     p->items = h_kt + p->P;
     // Samples per Gram block, per launch (measured on both layer shapes): about
     // kGramBlockBudget / d blocks -- a d x d partial costs d^2 words to write and
-    // reduce, and the d = 128 kernel runs one wave per SIMD -- with at least 4 d
-    // samples per block; key-difference blocks take at least 16 d samples unless
-    // that leaves fewer than kMinGramBlocks blocks.
+    // reduce -- with at least 8 d samples per query block; key-difference blocks
+    // take at least 16 d samples unless that leaves fewer than kMinGramBlocks
+    // blocks, and then at least 4 d.
     const int64_t g_max = ceil_div(h_q, h_kt);
     const int64_t target = kGramBlockBudget / d;
-    const int64_t s_q = std::max<int64_t>(4 * d, ceil_div(n * h_q, target));
+    const int64_t s_q = std::max<int64_t>(8 * d, ceil_div(n * h_q, target));
     int64_t s_d = std::max<int64_t>(16 * d, ceil_div(n * p->P, target));
     if (p->P * ceil_div(n, s_d) < kMinGramBlocks)
         s_d = std::max<int64_t>(4 * d, ceil_div(n * p->P, kMinGramBlocks));
     p->ct_q = ceil_div(s_q, g_max);
-    p->ct_d = s_d;
+    p->ct_d = ceil_div(s_d, kPBM) * kPBM;   // four waves x whole 32-token MFMA steps
+    p->ldt = ceil_div(n, kPBM) * kPBM;
     p->nq = (int)ceil_div(n, p->ct_q);
-    p->nd = (int)ceil_div(n, p->ct_d);
+    p->nd = (int)ceil_div(p->ldt, p->ct_d);
     const size_t dd = (size_t)d * d * sizeof(float);
     size_t o = 0;
-    p->off_K = o;      o = align_up(o + (size_t)n * h_kt * d * sizeof(float));
+    p->off_K = o;      o = align_up(o + (size_t)p->ldt * h_kt * d * sizeof(float));
     p->off_part = o;   o = align_up(o + ((size_t)h_kt * p->nq + (size_t)p->P * p->nd) * dd);
     p->off_SG = o;     o = align_up(o + (size_t)p->items * dd);
     p->off_Sp = o;     o = align_up(o + (size_t)p->P * dd);
@@ -123,13 +125,14 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     float *Sp = (float *)(ws + p.off_Sp);
     float *Pm = (float *)(ws + p.off_Pm);
 
-    ProjArgs pa{(const uint16_t *)X, (const uint16_t *)W_K, K, p.n, p.dm, p.h_kt * D};
+    ProjArgs pa{(const uint16_t *)X, (const uint16_t *)W_K, K, p.n, p.ldt, p.dm, p.h_kt * D};
     hipLaunchKernelGGL(k_kproj, dim3((unsigned)ceil_div(p.n, kPBM), (unsigned)(p.h_kt * D / kPBN)),
                        dim3(kThreads), 0, s, pa);
 
     GramArgs ga{};
     ga.Q = (const uint16_t *)Q;
-    ga.K = K;
+    ga.Kt = K;
+    ga.ldt = p.ldt;
     ga.n = p.n;
     ga.h_q = p.h_q;
     ga.h_kt = p.h_kt;
@@ -137,12 +140,12 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     ga.part = part;
     ga.chunk_tokens = p.ct_q;
     ga.n_chunk = p.nq;
-    hipLaunchKernelGGL((k_gram<D, true>), dim3((unsigned)p.nq, (unsigned)p.h_kt, gram_groups(D)),
+    hipLaunchKernelGGL((k_gram<D, true>), dim3((unsigned)p.nq, (unsigned)p.h_kt, gram_groups(D, true)),
                        dim3(kThreads), 0, s, ga);
     ga.part = part + (size_t)p.h_kt * p.nq * D * D;
     ga.chunk_tokens = p.ct_d;
     ga.n_chunk = p.nd;
-    hipLaunchKernelGGL((k_gram<D, false>), dim3((unsigned)p.nd, (unsigned)p.P, gram_groups(D)),
+    hipLaunchKernelGGL((k_gram<D, false>), dim3((unsigned)p.nd, (unsigned)p.P, gram_groups(D, false)),
                        dim3(kThreads), 0, s, ga);
 
     ReduceArgs ra{part, SG, p.h_kt, p.nq, p.nd, D * D};

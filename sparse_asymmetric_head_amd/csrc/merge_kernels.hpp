@@ -15,7 +15,8 @@
 // so the identity holds for singular S too).  So the data-parallel work is
 //   1. the key projection K = X W^T               (bf16 MFMA GEMM, fp32 out),
 //   2. d x d Gram matrices over the calibration tokens: S_r for every group
-//      and G for every head pair                  (fp32 MFMA, exact products),
+//      and G for every head pair                  (bf16 MFMA: exact products for
+//      the queries, a split high/low bf16 pair for the fp32 key differences),
 // and the rest is small dense algebra per head pair (a rank-revealing Cholesky
 // for the pseudoinverse, a handful of d x d products) plus a 2^h_kt-state
 // matching.
@@ -42,8 +43,8 @@ __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
 struct ProjArgs {
     const uint16_t *X;  // [n][dm] bf16
     const uint16_t *W;  // [cols][dm] bf16 (row r*D + c = channel c of teacher key head r)
-    float *K;           // [n][cols] fp32
-    int64_t n;
+    float *Kt;          // [cols][ldt] fp32, channel-major; tokens n .. ldt-1 written as zero
+    int64_t n, ldt;     // ldt: n rounded up to kPBM
     int dm;
     int cols;
 };
@@ -122,25 +123,27 @@ __global__ __launch_bounds__(kThreads) void k_kproj(ProjArgs a) {
         if (kt + 1 < nk) lstore(cur ^ 1);
         __syncthreads();
     }
-    // lane holds rows 4*(lane/16)+r, column lane%16 of each 16 x 16 tile
+    // lane holds rows (tokens) 4*(lane/16)+r, column lane%16 of each 16 x 16 tile:
+    // four consecutive tokens of one channel, one 16-byte store (zero past n)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-            if (t < a.n) {
-                float *row = a.K + t * a.cols + n0 + wn * 64 + (lane & 15);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) row[j * 16] = acc[i][j][r];
-            }
+        for (int j = 0; j < 4; ++j) {
+            const f32x4v v = acc[i][j];
+            const float4 o = {t + 0 < a.n ? v[0] : 0.f, t + 1 < a.n ? v[1] : 0.f,
+                              t + 2 < a.n ? v[2] : 0.f, t + 3 < a.n ? v[3] : 0.f};
+            *(float4 *)(a.Kt + (int64_t)(n0 + wn * 64 + j * 16 + (lane & 15)) * a.ldt + t) = o;
         }
+    }
 }
 
 // ------------------------------------------------------------ 2. Grams
 
 struct GramArgs {
     const uint16_t *Q;   // [n][h_q][D] bf16 calibration queries
-    const float *K;      // [n][h_kt*D] fp32 projected keys
+    const float *Kt;     // [h_kt*D][ldt] fp32 projected keys, channel-major, zero past n
+    int64_t ldt;         // a multiple of 128, >= n
     float *part;         // per-block partial sums: [item][chunk][D][D] of this launch's items
     int64_t n;
     int64_t chunk_tokens;
@@ -149,129 +152,197 @@ struct GramArgs {
     uint8_t pa[kMaxPairs], pb[kMaxPairs];  // pair p = (pa[p], pb[p]), pa < pb
 };
 
-// Channel held by row/column i (0..15) of feature block I: lane (k, i) loads
-// the float4 at channels 64h + 4i .. 4i+3 of its sample, and register c of that
-// chunk feeds block I = 4h + c.  The Gram is accumulated in this permuted
-// channel order and un-permuted when written out.
-__device__ __forceinline__ int chan(int I, int i) { return 64 * (I >> 2) + 4 * i + (I & 3); }
-
 // Tile groups of a Gram block: the (D/16)(D/16+1)/2 tiles I <= J of one item's
-// second moment are dealt round-robin to gram_groups(D) blocks (blockIdx.z) that
-// read the same samples, so that a d = 128 block holds a quarter of the
-// accumulators and the grid has four times the blocks.
-__host__ __device__ constexpr int gram_groups(int D) { return D >= 128 ? 4 : 1; }
+// second moment are dealt round-robin to gram_groups blocks (blockIdx.z) that
+// read the same samples, so that a d = 128 block holds a half (queries) or a
+// quarter (key differences, whose double-buffered fp32 loads take the other
+// half of the registers) of the accumulators.
+__host__ __device__ constexpr int gram_groups(int D, bool is_q) {
+    return D >= 128 ? (is_q ? 2 : 4) : 1;
+}
 
-// One block per (item, token chunk, tile group).  IS_Q: item r = blockIdx.y, S_r,
-// the second moment of group r's query vectors (samples = (token, query head of
-// the group)).  Otherwise item p = blockIdx.y, G_p, the second moment of
-// K_a - K_b over tokens.  MFMA 16x16x4 fp32: lane (k = lane/16, i = lane%16)
-// supplies sample k's channel chan(I, i) as both the A (row) and B (column)
-// operand, so each instruction adds 4 samples' outer products to a 16 x 16 tile.
-// The next 4 samples are loaded while the current ones are multiplied.  The block
-// writes its tiles (and their mirror images) into the (item, chunk) partial.
+constexpr int kGramStep = 32;   // samples per MFMA 16x16x32 k-step
+constexpr int kGramWaves = kThreads / 64;
+constexpr int kQtStride = 40;   // LDS row stride of the transposed query tile, bf16 (80 bytes)
+
+// Round x to bf16 (nearest even) as the high part and the rounded remainder as
+// the low part: x = hi + lo to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+    hi = (__bf16)x;
+    lo = (__bf16)(x - (float)hi);
+}
+
+// One block per (item, token chunk, tile group).  MFMA 16x16x32 bf16 with the
+// sample as the contraction index: lane (q = lane/16, i = lane%16) supplies, for
+// feature block I, channel 16 I + i of samples 8 q .. 8 q + 7 as both the A
+// (row) and the B (column) operand, so each instruction adds 32 samples' outer
+// products to a 16 x 16 tile; only tiles I <= J are formed.
+//  IS_Q: item r = blockIdx.y, S_r over the (token, query head of group r)
+//   samples.  Query rows are channel-contiguous, so each wave stages 32 samples
+//   through a wave-private LDS tile (lane (sg, c8) loads channels 8 c8 .. +7 of
+//   samples 4 sg .. +3 and writes them as 4-sample runs of each channel; the
+//   80-byte rows make the 16-byte fragment reads conflict-free).  bf16 inputs:
+//   the products are exact.
+//  else: item p = blockIdx.y, G_p over tokens of the fp32 key difference
+//   K_a - K_b, read channel-major (a lane's 8 tokens are contiguous, no
+//   staging), split into bf16 high and low parts; hi hi + hi lo + lo hi per tile.
+// Loads of the next step are issued before the current step's multiplies.  The
+// block writes its tiles (and their mirror images) into the (item, chunk) partial.
 template <int D, bool IS_Q>
 __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     constexpr int NB = D / 16;                     // feature blocks
     constexpr int NT = NB * (NB + 1) / 2;          // tiles I <= J
-    constexpr int TG = gram_groups(D);
+    constexpr int TG = gram_groups(D, IS_Q);
     constexpr int NA = (NT + TG - 1) / TG;         // accumulator tiles per block
-    constexpr int NH = D / 64;                     // float4 chunks per lane per sample
+    constexpr int NH = D / 64;                     // 8-channel chunks per lane (queries)
     __shared__ float red[NA * 256];
+    __shared__ uint16_t qt[IS_Q ? kGramWaves : 1][IS_Q ? D * kQtStride : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int k = lane >> 4, i = lane & 15;
+    const int q4 = lane >> 4, i16 = lane & 15;
     const int item = blockIdx.y;
     const int grp = blockIdx.z;
     const int64_t t_beg = (int64_t)blockIdx.x * a.chunk_tokens;
-    int64_t t_end = t_beg + a.chunk_tokens;
-    t_end = t_end < a.n ? t_end : a.n;
-    const int ntok = (int)(t_end > t_beg ? t_end - t_beg : 0);
-
-    int lo = 0, g = 1, ka = 0, kb = 0;
-    if (IS_Q) {
-        lo = (item * a.h_q + a.h_kt - 1) / a.h_kt;                 // first j with j*h_kt/h_q >= item
-        const int hi = ((item + 1) * a.h_q + a.h_kt - 1) / a.h_kt;
-        g = hi - lo;
-    } else {
-        ka = a.pa[item];
-        kb = a.pb[item];
-    }
-    const int n_samp = ntok * g;                                    // block-local sample count
-    const int per_wave = ((n_samp + 15) / 16) * 4;                  // multiple of 4
-    const int s_beg = wave * per_wave;
-    const int s_end = min(s_beg + per_wave, n_samp);
-    const int64_t ldk = (int64_t)a.h_kt * D;
-
-    // sample s (block-local) -> channel values of this lane, zero beyond s_end
-    auto load = [&](int s0, float (&x)[NB]) {
-        const int s = s0 + k;
-        const bool ok = s < s_end;
-        const int sc = ok ? s : s_beg;
-        if (IS_Q) {
-            const int tl = sc / g;
-            const int j = lo + (sc - tl * g);
-            const uint16_t *src = a.Q + ((t_beg + tl) * a.h_q + j) * D + 4 * i;
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const uint2 w = *(const uint2 *)(src + 64 * h);
-                x[4 * h + 0] = bf_lo(w.x);
-                x[4 * h + 1] = bf_hi(w.x);
-                x[4 * h + 2] = bf_lo(w.y);
-                x[4 * h + 3] = bf_hi(w.y);
-            }
-        } else {
-            const float *src = a.K + (t_beg + sc) * ldk + 4 * i;
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const float4 u = *(const float4 *)(src + ka * D + 64 * h);
-                const float4 v = *(const float4 *)(src + kb * D + 64 * h);
-                x[4 * h + 0] = u.x - v.x;
-                x[4 * h + 1] = u.y - v.y;
-                x[4 * h + 2] = u.z - v.z;
-                x[4 * h + 3] = u.w - v.w;
-            }
-        }
-        if (!ok) {
-#pragma unroll
-            for (int I = 0; I < NB; ++I) x[I] = 0.f;
-        }
-    };
 
     f32x4v acc[NA];
 #pragma unroll
     for (int t = 0; t < NA; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
     // tile t (row-major over I <= J) belongs to group t % TG, slot t / TG
-    auto accumulate = [&](const float (&x)[NB]) {
+    auto tiles = [&](auto &&fn) {
 #pragma unroll
         for (int I = 0; I < NB; ++I)
 #pragma unroll
             for (int J = I; J < NB; ++J) {
                 const int t = I * NB - I * (I - 1) / 2 + (J - I);
-                if (t % TG == grp) acc[t / TG] = mfma4(x[I], x[J], acc[t / TG]);
+                if (t % TG == grp) fn(I, J, t / TG);
             }
     };
 
-    if (s_beg < s_end) {
-        float xa[NB], xb[NB];
-        load(s_beg, xa);
-        for (int s0 = s_beg;; s0 += 8) {
-            load(s0 + 4, xb);
-            accumulate(xa);
-            if (s0 + 4 >= s_end) break;
-            load(s0 + 8, xa);
-            accumulate(xb);
-            if (s0 + 8 >= s_end) break;
+    if constexpr (IS_Q) {
+        const int lo = (item * a.h_q + a.h_kt - 1) / a.h_kt;     // first j with j*h_kt/h_q >= item
+        const int g = ((item + 1) * a.h_q + a.h_kt - 1) / a.h_kt - lo;
+        int64_t t_end = t_beg + a.chunk_tokens;
+        t_end = t_end < a.n ? t_end : a.n;
+        const int ntok = (int)(t_end > t_beg ? t_end - t_beg : 0);
+        const int n_samp = ntok * g;
+        const int per_wave = (n_samp + kGramWaves * kGramStep - 1) / (kGramWaves * kGramStep) * kGramStep;
+        const int s_beg = wave * per_wave;
+        const int s_end = min(s_beg + per_wave, n_samp);
+        const int sg = lane >> 3, c8 = lane & 7;
+        uint16_t *tile = qt[wave];
+        // raw[h][u]: channels 8 (c8 + 8 h) .. +7 of sample s0 + 4 sg + u
+        auto load = [&](int s0, u32x4 (&raw)[NH][4]) {
+            int s = s0 + 4 * sg;
+            int tl = s / g, jj = s - tl * g;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = s + u < s_end;
+                const uint16_t *src = a.Q + ((t_beg + (ok ? tl : 0)) * a.h_q + lo + (ok ? jj : 0)) * D + 8 * c8;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    const u32x4 v = ld16(src + 64 * h);
+                    raw[h][u] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+                }
+                if (++jj == g) { jj = 0; ++tl; }
+            }
+        };
+        auto process = [&](const u32x4 (&raw)[NH][4]) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {          // channels 2 w2, 2 w2 + 1 of the chunk
+                    const uint32_t x0 = raw[h][0][w2], x1 = raw[h][1][w2];
+                    const uint32_t x2 = raw[h][2][w2], x3 = raw[h][3][w2];
+                    const uint2 ev = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
+                    const uint2 od = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
+                    const int ch = 8 * (c8 + 8 * h) + 2 * w2;
+                    *(uint2 *)(tile + ch * kQtStride + 4 * sg) = ev;
+                    *(uint2 *)(tile + (ch + 1) * kQtStride + 4 * sg) = od;
+                }
+            bf16x8 f[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+                f[I] = as_bf16x8(*(const u32x4 *)(tile + (16 * I + i16) * kQtStride + 8 * q4));
+            tiles([&](int I, int J, int sl) {
+                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[I], f[J], acc[sl], 0, 0, 0);
+            });
+        };
+        if (s_beg < s_end) {
+            u32x4 ra[NH][4], rb[NH][4];
+            load(s_beg, ra);
+            for (int s0 = s_beg;; s0 += 2 * kGramStep) {
+                load(s0 + kGramStep, rb);
+                process(ra);
+                if (s0 + kGramStep >= s_end) break;
+                load(s0 + 2 * kGramStep, ra);
+                process(rb);
+                if (s0 + 2 * kGramStep >= s_end) break;
+            }
+        }
+    } else {
+        const int ka = a.pa[item], kb = a.pb[item];
+        int64_t t_end = t_beg + a.chunk_tokens;
+        t_end = t_end < a.ldt ? t_end : a.ldt;                  // past n the keys are zero
+        const int64_t ntok = t_end > t_beg ? t_end - t_beg : 0;  // a multiple of 128
+        const int64_t per_wave = ntok / kGramWaves;
+        const int64_t w_beg = t_beg + wave * per_wave, w_end = w_beg + per_wave;
+        const float *Ka = a.Kt + (int64_t)(ka * D + i16) * a.ldt + 8 * q4;
+        const float *Kb = a.Kt + (int64_t)(kb * D + i16) * a.ldt + 8 * q4;
+        // raw[I][0..1]: tokens t0 + 8 q4 .. +7 of channel 16 I + i16, heads a, b
+        auto load = [&](int64_t t0, float4 (&ra)[NB][2], float4 (&rb)[NB][2]) {
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                const int64_t off = (int64_t)16 * I * a.ldt + t0;
+                ra[I][0] = *(const float4 *)(Ka + off);
+                ra[I][1] = *(const float4 *)(Ka + off + 4);
+                rb[I][0] = *(const float4 *)(Kb + off);
+                rb[I][1] = *(const float4 *)(Kb + off + 4);
+            }
+        };
+        auto process = [&](const float4 (&ra)[NB][2], const float4 (&rb)[NB][2]) {
+            bf16x8 hi[NB], lo[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                const float x[8] = {ra[I][0].x - rb[I][0].x, ra[I][0].y - rb[I][0].y,
+                                    ra[I][0].z - rb[I][0].z, ra[I][0].w - rb[I][0].w,
+                                    ra[I][1].x - rb[I][1].x, ra[I][1].y - rb[I][1].y,
+                                    ra[I][1].z - rb[I][1].z, ra[I][1].w - rb[I][1].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 h, l;
+                    split_bf16(x[e], h, l);
+                    hi[I][e] = h;
+                    lo[I][e] = l;
+                }
+            }
+            tiles([&](int I, int J, int sl) {
+                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[I], hi[J], acc[sl], 0, 0, 0);
+                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[I], lo[J], acc[sl], 0, 0, 0);
+                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[I], hi[J], acc[sl], 0, 0, 0);
+            });
+        };
+        if (w_beg < w_end) {
+            float4 aa[NB][2], ab[NB][2], ba[NB][2], bb[NB][2];
+            load(w_beg, aa, ab);
+            for (int64_t t0 = w_beg;; t0 += 2 * kGramStep) {
+                if (t0 + kGramStep < w_end) load(t0 + kGramStep, ba, bb);
+                process(aa, ab);
+                if (t0 + kGramStep >= w_end) break;
+                if (t0 + 2 * kGramStep < w_end) load(t0 + 2 * kGramStep, aa, ab);
+                process(ba, bb);
+                if (t0 + 2 * kGramStep >= w_end) break;
+            }
         }
     }
 
     // Sum the four waves' tiles in LDS (slot-major, 256 words per tile), one wave
-    // at a time.
-    for (int w = 0; w < 4; ++w) {
+    // at a time; lane holds rows 4 q4 + r, column i16 of each tile.
+    for (int w = 0; w < kGramWaves; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int q = 0; q < NA; ++q)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int e = q * 256 + (4 * k + r) * 16 + i;
+                    const int e = q * 256 + (4 * q4 + r) * 16 + i16;
                     red[e] = (w == 0 ? 0.f : red[e]) + acc[q][r];
                 }
         }
@@ -279,18 +350,13 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     }
     // write the block's tiles and their mirror images into the partial
     float *dst = a.part + ((int64_t)item * a.n_chunk + blockIdx.x) * (D * D);
-#pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-        for (int J = I; J < NB; ++J) {
-            const int t = I * NB - I * (I - 1) / 2 + (J - I);
-            if (t % TG != grp) continue;
-            const int rr = tid >> 4, cc = tid & 15;              // 256 threads: one entry each
-            const float v = red[(t / TG) * 256 + rr * 16 + cc];
-            const int row = chan(I, rr), col = chan(J, cc);
-            dst[row * D + col] = v;
-            if (I != J) dst[col * D + row] = v;
-        }
+    const int rr = tid >> 4, cc = tid & 15;              // 256 threads: one entry each
+    tiles([&](int I, int J, int sl) {
+        const float v = red[sl * 256 + rr * 16 + cc];
+        const int row = 16 * I + rr, col = 16 * J + cc;
+        dst[row * D + col] = v;
+        if (I != J) dst[col * D + row] = v;
+    });
 }
 
 struct ReduceArgs {
