@@ -43,9 +43,10 @@
  *                                      zero diagonal)
  *   total_loss fp64 [1]                summed cost of the pairing
  * Arithmetic: keys X W_K^T from bf16 products accumulated in fp32; second
- * moments of queries and key differences from exact fp32 products summed in
- * fp32 per block and fp64 across blocks; the pseudoinverse (pivoted
- * Cholesky, Gauss-Jordan inverse of L^T L) and the d x d products in fp32;
+ * moments of the queries from exact bf16 products, of the fp32 key
+ * differences from a bf16 high/low split (about 2^-16 relative), both summed
+ * in fp32 per block and fp64 across blocks; the pseudoinverse (pivoted
+ * Cholesky, symmetric sweeps inverting L^T L) and the d x d products in fp32;
  * costs summed in fp64.
  * Supported: d in {64, 128}; h_kt even, 2 <= h_kt <= 16; h_kt <= h_q <= 1024;
  * d_model a multiple of 64, 64 <= d_model <= 32768; 1 <= n <= 2^26.
