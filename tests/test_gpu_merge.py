@@ -4,8 +4,8 @@ through the C ABI (saga_merge_key_heads).
 Tolerances, from the arithmetic: keys are fp32 sums of exact bf16 products;
 the query second moments are fp32 sums of exact bf16 products, the key
 difference ones carry a bf16 high/low split (about 2^-16 relative); the fp32
-pseudoinverse (pivoted Cholesky, then a Gauss-Jordan inverse
-of L^T L) carries about 1e-7 * cond(S_a + S_b) relative error, and so do the
+pseudoinverse (pivoted Cholesky, then symmetric sweeps that invert
+L^T L) carries about 1e-7 * cond(S_a + S_b) relative error, and so do the
 merge maps and the costs built from it.  The synthetic query statistics have
 cond <= ~400 (channel scales exp(-c/decay)), so 2e-3 on the costs and on the
 merged weights (relative to their largest entry) leaves a wide margin.  The
