@@ -505,14 +505,40 @@ def main() -> int:
         # the full trajectory holds 2 refresh steps and steps - 2 non-refresh ones
         t_norm = max((t_all / S - 2 * t_ref) / (steps - 2), 0.0)
         cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
-        cpu = {"value": round(cpu_us, 1), "unit": "us/step", "cores": oracle.num_threads(lib),
+        # the same oracle on one core: one layer's refresh step and one plain step
+        cores = oracle.num_threads(lib)
+        oracle.set_num_threads(1, lib)
+        x = wl.make_layer(cfg, 0, device=dev, cfg_index=ci, steps=2)
+        Qh, Kh, Vh = (oracle._u16(x[k]) for k in ("Q", "K", "V"))
+        del x
+        c0 = time.perf_counter()
+        oracle.trajectory(Qh[:1], Kh, Vh, h_k, h_v, N, R, lib=lib)
+        c1 = time.perf_counter()
+        oracle.trajectory(Qh[:2], Kh, Vh, h_k, h_v, N, max(R, 2), lib=lib)
+        c2 = time.perf_counter()
+        oracle.set_num_threads(cores, lib)
+        one_ref, one_norm = c1 - c0, max((c2 - c1) - (c1 - c0), 0.0)
+        one_us = L * (one_ref + (R - 1) * one_norm) / R * 1e6
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                                 "")
+        except OSError:
+            pass
+        cpu = {"value": round(cpu_us, 1), "unit": "us/step", "cores": cores,
                "kind": "oracle",
+               "single_core_value": round(one_us, 1),
+               "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()},
                "sample": (f"{S} of {L} layers x {steps + 1} oracle layer-steps each (one refresh "
                           f"step alone, then {steps} steps with refreshes at 0 and {R}) of "
                           f"{cfg.name}; per-layer costs amortised over R={R} and scaled to {L} "
                           f"layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
-                          f"layer-step, {t_one + t_all:.1f} s of oracle time)")}
-        log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads")
+                          f"layer-step, {t_one + t_all:.1f} s of oracle time); single_core_value "
+                          f"from layer 0's refresh step and one plain step on one thread "
+                          f"(refresh {one_ref:.3f} s, non-refresh {one_norm:.3f} s), scaled alike")}
+        log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads, "
+            f"{one_us / 1e3:.1f} ms/step on one ({cpu_model})")
 
     merge = None
     if not args.no_merge:
