@@ -435,7 +435,8 @@ __device__ __forceinline__ void vput(vec16 &v0, vec16 &v1, vec16 &v2, vec16 &v3,
     else v3[m & 15] = x;
 }
 
-// Moore-Penrose pseudoinverse of S = S_a + S_b, one block per pair:
+// Moore-Penrose pseudoinverse of S = S_a + S_b, one block per pair.  A full-rank
+// S is inverted directly by D pivoted symmetric sweeps; otherwise:
 //  1. diagonally pivoted Cholesky, S ~ L L^T with L's rows in the original
 //     order: each step takes the largest remaining diagonal of the Schur
 //     complement as pivot j, column k of L is that complement's column j over
@@ -510,7 +511,67 @@ __global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
         j = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(who));
         pv = top ? fkey_inv(top) : -INFINITY;
     };
-    __syncthreads();                   // Lt cleared
+    float *out = a.Sp + (int64_t)p * D * D;
+
+    // Full rank first: D symmetric sweeps of S itself, each on the largest
+    // unswept diagonal entry, leave -S^-1.  The unswept diagonal is the Schur
+    // complement's, so the pivots and the rank cut are those of the pivoted
+    // Cholesky below; if the cut stops the sweeps early, the block starts over
+    // on the rank-revealing path.
+    {
+        float pv;
+        int j;
+        pivot(pv, j);
+        int swept = 0;
+        for (int k = 0; k < D; ++k) {
+            if (!(pv > stop)) break;   // uniform
+            float *f = cb + (k & 1) * D;
+            const bool own = j >= d0 && j < d0 + R;
+            if (own) f[c] = AGET(__builtin_amdgcn_readfirstlane(j - d0));
+            __syncthreads();
+            const float ip = 1.f / f[j];
+            const float fc = f[c];
+            const float s = (c == j) ? 0.f : 1.f;
+            const float t = (c == j) ? ip : -fc * ip;
+            const float4 *fr = (const float4 *)(f + d0);
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q) {
+                const float4 v = fr[q];
+                APUT(4 * q + 0, AGET(4 * q + 0) * s + v.x * t);
+                APUT(4 * q + 1, AGET(4 * q + 1) * s + v.y * t);
+                APUT(4 * q + 2, AGET(4 * q + 2) * s + v.z * t);
+                APUT(4 * q + 3, AGET(4 * q + 3) * s + v.w * t);
+            }
+            if (own) APUT(__builtin_amdgcn_readfirstlane(j - d0), (c == j) ? -ip : fc * ip);
+#pragma unroll
+            for (int h = 0; h < EPL; ++h) {
+                const float fe = f[lane + 64 * h];
+                dg[h] -= fe * fe * ip;
+                ddone[h] = ddone[h] || (lane + 64 * h == j);
+            }
+            ++swept;
+            pivot(pv, j);
+        }
+        if (swept == D) {              // uniform
+#pragma unroll
+            for (int m = 0; m < R; ++m) out[(d0 + m) * D + c] = -AGET(m);
+            if (tid == 0) a.rank[p] = D;
+            return;
+        }
+    }
+    // rank deficient: start over from S
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+        const int r = d0 + m;
+        APUT(m, 0.5f * ((Sa[r * D + c] + Sb[r * D + c]) + (Sa[c * D + r] + Sb[c * D + r])));
+    }
+#pragma unroll
+    for (int h = 0; h < EPL; ++h) {
+        const int e = lane + 64 * h;
+        dg[h] = Sa[e * D + e] + Sb[e * D + e];
+        ddone[h] = false;
+    }
+    __syncthreads();                   // Lt cleared; every read of the sweeps' cb is done
 
     float pv;
     int j;
@@ -603,7 +664,6 @@ __global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
     }
     __syncthreads();
     // S^+ = Y Y^T
-    float *out = a.Sp + (int64_t)p * D * D;
     for (int t = wave; t < NB * NB; t += 4) {
         const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
         const f32x4v v = lds_tile_mm<D, LD, false, true>(Lt, Lt, i0, j0, lane);
