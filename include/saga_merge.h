@@ -18,12 +18,12 @@
  *     minimum-weight perfect matching on the complete graph of pair costs.
  * Readings of this library (the pages leave them open):
  *   - group r = the query heads j with floor(j*h_kt/h_q) == r (the GQA map);
- *   - the pseudoinverse's numerical rank is the number of steps a
- *     diagonally pivoted Cholesky factorisation of S_a + S_b takes before
- *     the largest remaining pivot falls to 2^-14 times the largest diagonal
- *     entry; with S = L L^T at that rank, S^+ = L (L^T L)^-2 L^T (fp32
- *     arithmetic; a spectrum with no gap near that level makes the result
- *     depend on rounding);
+ *   - the pseudoinverse's numerical rank is the number of pivots, taken on
+ *     the largest remaining Schur-complement diagonal of S_a + S_b, before
+ *     that diagonal falls to 2^-14 times the largest diagonal entry of S; at
+ *     full rank S^+ = S^-1, else with S = L L^T at that rank (pivoted
+ *     Cholesky) S^+ = L (L^T L)^-2 L^T (fp32 arithmetic; a spectrum with no
+ *     gap near that level makes the result depend on rounding);
  *   - equal-cost pairings: the one whose lowest head takes the lowest
  *     partner wins, recursively;
  *   - merged head i serves the query heads of teacher groups pairs[i][0]
