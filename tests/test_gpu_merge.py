@@ -99,6 +99,7 @@ CASES = [
     ("qwen-tiny", MergeConfig("t", n=250, h_q=12, h_kt=2, d=128, d_model=256, decay=64.0), 3),
     ("uneven-groups", MergeConfig("t", n=200, h_q=10, h_kt=4, d=64, d_model=128), 4),
     ("d128-six-heads", MergeConfig("t", n=160, h_q=12, h_kt=6, d=128, d_model=128, decay=64.0), 5),
+    ("d128-eight-heads", MergeConfig("t", n=200, h_q=16, h_kt=8, d=128, d_model=192, decay=64.0), 15),
 ]
 
 
