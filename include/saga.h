@@ -36,8 +36,8 @@
  *   - Arguments are validated on the host before anything is enqueued; an
  *     invalid call returns a negative saga_status and enqueues nothing.
  *     Launch failures are reported as SAGA_ERR_HIP.
- *   - Supported: d in {64, 128}; 1 <= h_k <= h_v <= h_q; h_q/h_k rounded up
- *     <= 64; 1 <= N <= l_kv; l_kv * d * 2 < 2^31; B*h_q < 2^20.
+ *   - Supported: d in {64, 128}; 1 <= h_k <= h_v <= h_q <= 32768; h_q/h_k
+ *     rounded up <= 64; 1 <= N <= l_kv; l_kv * d * 2 < 2^31; B*h_q < 2^20.
  */
 #ifndef SAGA_H
 #define SAGA_H

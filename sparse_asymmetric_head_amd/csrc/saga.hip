@@ -21,6 +21,9 @@ using namespace saga;
 #define SAGA_SELECT_BLOCKS 256
 #endif
 constexpr int kTargetSelectBlocks = SAGA_SELECT_BLOCKS;  // streaming blocks per launch
+// Head-index products (g * h_q, j * h_v) stay below 2^30 in the kernels' 32-bit
+// arithmetic.
+constexpr int kMaxQueryHeads = 32768;
 #ifndef SAGA_DENSE_BLOCKS
 #define SAGA_DENSE_BLOCKS 512
 #endif
@@ -58,6 +61,7 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
     if (ceil_div(h_q, h_k) > 64) return SAGA_ERR_UNSUPPORTED;
     if (l_kv * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)B * h_q >= (int64_t(1) << 20)) return SAGA_ERR_UNSUPPORTED;
+    if (h_q > kMaxQueryHeads) return SAGA_ERR_UNSUPPORTED;
     return SAGA_OK;
 }
 
@@ -144,6 +148,7 @@ int make_dense_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, Dense
     if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
     if (l_kv * (int64_t)d * 2 >= (int64_t(1) << 31)) return SAGA_ERR_UNSUPPORTED;
     if ((int64_t)B * h_q >= (int64_t(1) << 20)) return SAGA_ERR_UNSUPPORTED;
+    if (h_q > kMaxQueryHeads) return SAGA_ERR_UNSUPPORTED;
     auto vh = [&](int64_t j) { return j * h_v / h_q; };
     int64_t maxv = 1;
     for (int g = 0; g < h_k; ++g) {

@@ -149,8 +149,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int *red, int *total) {
 
 // First query head of key head g's group: ceil(g*h_q/h_k), so that
 // floor(j*h_k/h_q) == g  <=>  group_lo(g) <= j < group_lo(g+1).
+// 32-bit arithmetic: the plan admits h_q <= 32768, so g * h_q < 2^30.
 __device__ __forceinline__ int group_lo(int g, int h_q, int h_k) {
-    return (int)(((int64_t)g * h_q + h_k - 1) / h_k);
+    return (g * h_q + h_k - 1) / h_k;
 }
 
 }  // namespace saga

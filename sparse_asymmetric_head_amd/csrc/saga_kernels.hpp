@@ -62,11 +62,13 @@ constexpr int kRecHead = 15;  // survivors held in a record's first 128 bytes
 // segment); the wave's groups of grp = 16*U rows (wave w takes groups w,
 // w+4, ...); the 16-row tile within the group; inside a tile, output
 // register r = row % 4 first, then lane quarter row / 4 (the ballot order).
-__host__ __device__ inline int64_t record_order_key(int64_t t, int64_t chunk_len, int64_t grp) {
-    const int64_t c = t / chunk_len, o = t % chunk_len;
-    const int64_t gi = o / grp, i = o % grp;
-    const int64_t w = gi % kWaves, k = gi / kWaves;
-    const int64_t q = i % 16;
+// 32-bit arithmetic: positions, chunk lengths and keys stay below 2^25
+// (l_kv * d * 2 < 2^31).
+__host__ __device__ inline int record_order_key(int t, int chunk_len, int grp) {
+    const int c = t / chunk_len, o = t - c * chunk_len;
+    const int gi = o / grp, i = o - gi * grp;
+    const int w = gi % kWaves, k = gi / kWaves;
+    const int q = i % 16;
     return c * chunk_len + w * (chunk_len / kWaves) + k * grp + (i - q) + (q % 4) * 4 + q / 4;
 }
 
@@ -408,10 +410,20 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
 #else
     const int row = blockIdx.x / kAttendSplit, csl = blockIdx.x % kAttendSplit;
 #endif
-    const int b = row / a.h_q, j = row % a.h_q;
-    const int vh = (int)(((int64_t)j * a.h_v) / a.h_q);
     const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
     const int h = lane & 1;
+    // The two lanes of a pair load the halves of their segment's 128-byte head.
+    u32x4 own[4];
+    auto load_heads = [&](int p0) {
+        const int sg = p0 + (tid >> 1);
+        const int32_t *rs = rb + (int64_t)sg * a.seg_w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            own[q] = sg < a.n_sub ? ld16(rs + h * 16 + q * 4) : u32x4{0u, 0u, 0u, 0u};
+    };
+    load_heads(0);  // first, so the row's setup overlaps the load latency
+    const int b = row / a.h_q, j = row % a.h_q;
+    const int vh = j * a.h_v / a.h_q;  // j * h_v < 2^30 (h_q <= 32768)
     const int e_in = lane / LPE, cl = lane % LPE;
     const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + csl * DC + cl * 8;
     int *lt = wlt[wave];
@@ -424,11 +436,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     int cnt_w = 0;
     for (int p0 = 0; p0 < a.n_sub; p0 += SEGP) {
         const int sg = p0 + (tid >> 1);
-        const bool has = sg < a.n_sub;
-        const int32_t *rs = rb + (int64_t)sg * a.seg_w;
-        u32x4 own[4], hd[8];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) own[q] = has ? ld16(rs + h * 16 + q * 4) : u32x4{0u, 0u, 0u, 0u};
+        if (p0 > 0) load_heads(p0);
+        u32x4 hd[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const u32x4 oth = swap_pairs(own[q]);
@@ -815,7 +824,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
     __shared__ float wmin[NW];
     __shared__ int wbad[NW];
     const int row = blockIdx.x, b = row / a.h_q, j = row % a.h_q;
-    const int g = (int)(((int64_t)j * a.h_k) / a.h_q);
+    const int g = j * a.h_k / a.h_q;  // j * h_k < 2^30 (h_q <= 32768)
     float qf[D];
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
@@ -836,16 +845,18 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
         const int p = P[ii];
         const int prev = ii > 0 ? P[ii - 1] : -1;
         const bool in = p >= 0 && p < a.l_kv;
-        const int64_t kp = in ? record_order_key(p, a.chunk_len, a.grp) : -1;
-        const int64_t kq = ii == 0 ? -1
-                         : (prev >= 0 && prev < a.l_kv ? record_order_key(prev, a.chunk_len, a.grp)
-                                                        : INT64_MAX);
-        const bool ok = in && kp > kq;  // inside the cache, distinct (increasing keys)
-        if (i < a.N) bad |= !ok;
-        const uint16_t *kr = Kg + (int64_t)(ok ? p : 0) * D;
+        // The key row goes out as soon as p is known to be inside the cache;
+        // a pivot that fails the order check makes the bound -inf anyway.
+        const uint16_t *kr = Kg + (int64_t)(in ? p : 0) * D;
         u32x4 kv[D / 8];
 #pragma unroll
         for (int c = 0; c < D / 8; ++c) kv[c] = ld16(kr + c * 8);
+        const int cl = (int)a.chunk_len, gp = (int)a.grp;
+        const int kp = in ? record_order_key(p, cl, gp) : -1;
+        const int kq = ii == 0 ? -1
+                     : (prev >= 0 && prev < a.l_kv ? record_order_key(prev, cl, gp) : INT32_MAX);
+        const bool ok = in && kp > kq;  // inside the cache, distinct (increasing keys)
+        if (i < a.N) bad |= !ok;
         float s = 0.f, e = 0.f;
 #pragma unroll
         for (int c = 0; c < D / 8; ++c)
@@ -1181,7 +1192,7 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     const int b = bg / a.h_k, g = bg % a.h_k;
     int j_lo = group_lo(g, a.h_q, a.h_k), j_hi = group_lo(g + 1, a.h_q, a.h_k);
     // this block's value heads [v_lo, v_lo + NV) and their query heads
-    const int v_lo = (int)(((int64_t)j_lo * a.h_v) / a.h_q) + vsub * NV;
+    const int v_lo = j_lo * a.h_v / a.h_q + vsub * NV;  // j * h_v < 2^30 (h_q <= 32768)
     if (NV > 1 || a.n_vsub > 1) {
         j_lo = max(j_lo, group_lo(v_lo, a.h_q, a.h_v));
         j_hi = min(j_hi, group_lo(v_lo + NV, a.h_q, a.h_v));
@@ -1220,7 +1231,7 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     if constexpr (NV > 1) {
 #pragma unroll
         for (int h = 0; h < GMAX; ++h)
-            vix[h] = (int)(((int64_t)(j_lo + h) * a.h_v) / a.h_q) - v_lo;
+            vix[h] = (j_lo + h) * a.h_v / a.h_q - v_lo;
     }
     const int vr = lane / LPR, vc = (lane % LPR) * 8;
     const int64_t last = t_end - 1;
