@@ -118,6 +118,9 @@ def test_invalid_shapes_rejected(L):
     assert f(1, 4, 1, 2, 64, 1024, 1025) == 0     # N > l_kv
     assert f(1, 130, 2, 2, 64, 1024, 64) == 0     # group of 65 query heads
     assert f(1, 4, 1, 2, 128, 1 << 23, 64) == 0   # cache rows beyond 2^31 bytes
+    assert f(1, 32768, 512, 512, 64, 1024, 64) > 0       # the largest head count
+    assert f(1, 32769, 513, 513, 64, 1024, 64) == 0      # head products past 32-bit range
+    assert L.saga_dense_workspace_bytes(1, 32769, 4096, 64, 1024) == 0
     assert L.saga_dense_workspace_bytes(1, 32, 8, 64, 4096) > 0
     assert L.saga_dense_workspace_bytes(1, 32, 1, 64, 4096) == 0  # group of 32 > 16
     fw = L.saga_full_attention_workspace_bytes
