@@ -902,11 +902,13 @@ constexpr int kRefineCap = 8192;  // listed scores staged in LDS
 
 // One block per row.  The listed scores (up to kRefineCap staged in LDS with
 // their positions and segments, else read from the records on every pass)
-// go through three radix digits (11, 11 and 10 bits of the order key, from
-// the top) to the exact key of rank N.  The survivors (score >= tau) are
-// then walked in record order: the first N positions go to pivot, and every
-// record is rewritten in place to its survivors (same order; the max key
-// stays right, since a record that keeps any survivor keeps its largest).
+// go through radix digits of their order keys, from the highest bit in which
+// they differ, until the bucket holding rank N is small enough to rank its
+// keys against each other directly; that gives the exact key of rank N.
+// The survivors (score >= tau) are then walked in record
+// order: the first N positions go to pivot, and every record is rewritten in
+// place to its survivors (same order; the max key stays right, since a record
+// that keeps any survivor keeps its largest).
 __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     constexpr int SPT = kMaxSub / kThreads;  // segments per thread (4)
     constexpr int SU = 8;                    // staging loads in flight per thread
@@ -919,6 +921,10 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     __shared__ int red[kWaves];
     __shared__ int sel_bin;
     __shared__ uint32_t above;
+    __shared__ uint32_t cand[kThreads];
+    __shared__ int ncand;
+    __shared__ uint32_t sel_key;
+    __shared__ uint32_t rmn[kWaves], rmx[kWaves];
     const int row = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
@@ -934,7 +940,8 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         mine += n;
     }
     int total;
-    int pre = block_excl_scan<kWaves>(mine, red, &total);
+    const int pre0 = block_excl_scan<kWaves>(mine, red, &total);
+    int pre = pre0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int sgi = tid * SPT + i;
@@ -948,6 +955,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         soff[a.n_sub] = total;
         sel_bin = 0;
         above = 0u;
+        ncand = 0;
     }
     __syncthreads();
     if (total == 0) return;  // block-uniform; no survivors listed (cannot happen for N >= 1)
@@ -966,14 +974,21 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     };
     const bool staged = total <= kRefineCap;
     if (staged) {
+        // the segment of every flattened entry, written by the thread that
+        // owns the segment, so each staging load needs one LDS read
+        int o = pre0;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            for (int k = 0; k < c[i]; ++k) eseg[o + k] = (uint16_t)(tid * SPT + i);
+            o += c[i];
+        }
+        __syncthreads();
         for (int base = 0; base < total; base += kThreads * SU) {
-            int sgs[SU];
             int2 v[SU];
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
                 const int i = min(total - 1, base + u * kThreads + tid);
-                sgs[u] = seg_of(i);
-                v[u] = *entry_ptr(sgs[u], i);
+                v[u] = *entry_ptr(eseg[i], i);
             }
 #pragma unroll
             for (int u = 0; u < SU; ++u) {
@@ -981,7 +996,6 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
                 if (i < total) {
                     epos[i] = v[u].x;
                     ekey[i] = fkey(__int_as_float(v[u].y));
-                    eseg[i] = (uint16_t)sgs[u];
                 }
             }
         }
@@ -991,34 +1005,79 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         return staged ? ekey[i] : fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
     };
 
-    // digit 1: bits 31..21
-    for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
-    __syncthreads();
-    for (int i = tid; i < total; i += kThreads) atomicAdd(&h[key_at(i) >> 21], 1u);
-    __syncthreads();
-    find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
-    const uint32_t d0 = (uint32_t)sel_bin, k0 = (uint32_t)a.N - above;
-    // digit 2: bits 20..10 among keys with digit 1 = d0
-    for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
-    __syncthreads();
+    // The listed keys agree above their highest differing bit hi.  Radix
+    // digits of up to 11 bits go down from there (2048-bin LDS histograms)
+    // until the bucket holding the wanted rank has at most kThreads keys,
+    // which are then ranked against each other, or until every bit is fixed.
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
     for (int i = tid; i < total; i += kThreads) {
         const uint32_t k = key_at(i);
-        if ((k >> 21) == d0) atomicAdd(&h[(k >> 10) & 2047u], 1u);
+        kmn = kmn < k ? kmn : k;
+        kmx = kmx > k ? kmx : k;
+    }
+    kmn = ~wave_max_u32_dpp(~kmn);
+    kmx = wave_max_u32_dpp(kmx);
+    if (lane == 0) {
+        rmn[wave] = kmn;
+        rmx[wave] = kmx;
     }
     __syncthreads();
-    find_bin_desc(h, kHistBins, k0, &sel_bin, &above, red);
-    const uint32_t d1 = (uint32_t)sel_bin, k1 = k0 - above;
-    // digit 3: bits 9..0
-    for (int i = tid; i < 1024; i += kThreads) h[i] = 0u;
-    __syncthreads();
-    const uint32_t pfx = (d0 << 11) | d1;
-    for (int i = tid; i < total; i += kThreads) {
-        const uint32_t k = key_at(i);
-        if ((k >> 10) == pfx) atomicAdd(&h[k & 1023u], 1u);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        kmn = kmn < rmn[w] ? kmn : rmn[w];
+        kmx = kmx > rmx[w] ? kmx : rmx[w];
     }
-    __syncthreads();
-    find_bin_desc(h, 1024, k1, &sel_bin, &above, red);
-    const uint32_t tkey = (pfx << 10) | (uint32_t)sel_bin;
+    if (tid == 0) sel_key = kmn;  // (the bound lists at least N keys; this is never kept)
+    // keys that agree with p above bit h (h = -1: equal keys)
+    auto agrees = [](uint32_t k, uint32_t p, int h) { return ((uint64_t)(k ^ p) >> (h + 1)) == 0; };
+    uint32_t tkey = kmn;  // every listed key equal
+    if (kmn != kmx) {     // block-uniform
+        int hi = 31 - __clz(kmn ^ kmx);
+        uint32_t pfx = kmn;            // right above bit hi; lower bits fixed digit by digit
+        uint32_t rank = (uint32_t)a.N;  // rank wanted among the keys that agree with pfx above hi
+        int cnt = total;
+        while (hi >= 0 && cnt > kThreads) {  // block-uniform
+            const int lo = hi > 10 ? hi - 10 : 0;
+            const uint32_t dm = (2u << (hi - lo)) - 1u;  // digit = bits lo..hi
+            __syncthreads();  // every read of the previous digit's histogram is done
+            for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < total; i += kThreads) {
+                const uint32_t k = key_at(i);
+                if (agrees(k, pfx, hi)) atomicAdd(&h[(k >> lo) & dm], 1u);
+            }
+            __syncthreads();
+            find_bin_desc(h, kHistBins, rank, &sel_bin, &above, red);
+            const uint32_t bin = (uint32_t)sel_bin;
+            rank -= above;
+            cnt = (int)h[bin];
+            pfx = (pfx & ~(dm << lo)) | (bin << lo);
+            hi = lo - 1;
+        }
+        if (hi < 0) {
+            tkey = pfx;  // every bit fixed: the bucket holds equal keys
+        } else {
+            // the cnt keys that agree with pfx above hi (any order), each
+            // ranked against the others
+            for (int i = tid; i < total; i += kThreads) {
+                const uint32_t k = key_at(i);
+                if (agrees(k, pfx, hi)) cand[atomicAdd(&ncand, 1)] = k;
+            }
+            __syncthreads();
+            if (tid < cnt) {
+                const uint32_t mine = cand[tid];
+                int gt = 0, ge = 0;
+                for (int q = 0; q < cnt; ++q) {
+                    const uint32_t o = cand[q];
+                    gt += o > mine;
+                    ge += o >= mine;
+                }
+                if (gt < (int)rank && (int)rank <= ge) sel_key = mine;  // equal keys write equal values
+            }
+            __syncthreads();
+            tkey = sel_key;
+        }
+    }
     if (tid == 0) a.tau[row] = fkey_inv(tkey);
 
     // survivors per segment, their record-order ranks, the first N -> pivot
@@ -1032,7 +1091,8 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         }
     }
     int tot_pass;
-    int r = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+    const int r0 = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+    int r = r0;
     int32_t *P = a.pivot + (int64_t)row * a.N;
     for (int i = i0; i < i1 && r < a.N; ++i) {
         if (key_at(i) >= tkey) {
@@ -1061,7 +1121,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
             pb += pc[i];
         }
         __syncthreads();
-        int rr = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+        int rr = r0;
         for (int i = i0; i < i1; ++i) {
             const uint32_t k = ekey[i];
             if (k >= tkey) {
