@@ -158,7 +158,8 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     ia.rank = (int *)(ws + p.off_rank);
     ia.h_kt = p.h_kt;
     pair_table(p.h_kt, ia.pa, ia.pb);
-    hipLaunchKernelGGL(k_pair_pinv<D>, dim3((unsigned)p.P), dim3(kThreads), pinv_lds_bytes(D), s, ia);
+    hipLaunchKernelGGL(k_pair_pinv<D>, dim3((unsigned)p.P), dim3(pinv_threads(D)), pinv_lds_bytes(D), s,
+                       ia);
 
     LossArgs la{};
     la.SG = SG;

@@ -435,6 +435,11 @@ __device__ __forceinline__ void vput(vec16 &v0, vec16 &v1, vec16 &v2, vec16 &v3,
     else v3[m & 15] = x;
 }
 
+// Threads of a pseudoinverse block: each thread holds 16 entries (one register
+// vector) of the D x D working matrix, so a step's update is short and the
+// block's waves split it evenly (d = 64: 256 threads, d = 128: 1024).
+__host__ __device__ constexpr int pinv_threads(int D) { return D * D / 16; }
+
 // Moore-Penrose pseudoinverse of S = S_a + S_b, one block per pair.  A full-rank
 // S is inverted directly by D pivoted symmetric sweeps; otherwise:
 //  1. diagonally pivoted Cholesky, S ~ L L^T with L's rows in the original
@@ -455,12 +460,14 @@ __device__ __forceinline__ void vput(vec16 &v0, vec16 &v1, vec16 &v2, vec16 &v3,
 // diagonal (lane e holds entries e, e + 64) for the pivot search, so a step
 // costs one barrier.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
+__global__ __launch_bounds__(pinv_threads(D)) void k_pair_pinv(PinvArgs a) {
+    constexpr int TH = pinv_threads(D);
+    constexpr int NW = TH / 64;        // waves
     constexpr int LD = D + 4;          // 16-byte rows; 16 x 4 MFMA operand reads hit 64 banks
     constexpr int NB = D / 16;
-    constexpr int R = D * D / kThreads;
+    constexpr int R = D * D / TH;     // rows per thread (16: one register vector)
     constexpr int EPL = D / 64;        // diagonal entries per lane
-    constexpr int NT = NB * NB / 4;    // output tiles per wave
+    constexpr int NT = NB * NB / NW;   // output tiles per wave
     extern __shared__ float sm[];
     float *Lt = sm;                    // [D][LD] row k = column k of L; later Y (row-major)
     float *Mb = sm + D * LD;           // [D][LD] M, later M^-1
@@ -492,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
         ddone[h] = false;
     }
     bool cdone = false;                // this thread's column already eliminated
-    for (int e = tid; e < D * LD; e += kThreads) Lt[e] = 0.f;
+    for (int e = tid; e < D * LD; e += TH) Lt[e] = 0.f;
     float mx = 0.f;
 #pragma unroll
     for (int h = 0; h < EPL; ++h) mx = fmaxf(mx, dg[h]);
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
     __syncthreads();
 
     // M = L^T L = Lt Lt^T into Mb (zero outside the leading r x r block)
-    for (int t = wave; t < NB * NB; t += 4) {
+    for (int t = wave; t < NB * NB; t += NW) {
         const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
         const f32x4v v = lds_tile_mm<D, LD, false, true>(Lt, Lt, i0, j0, lane);
 #pragma unroll
@@ -651,20 +658,20 @@ __global__ __launch_bounds__(kThreads) void k_pair_pinv(PinvArgs a) {
     f32x4v y[NT];
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-        const int t = wave + 4 * q;
+        const int t = wave + NW * q;
         y[q] = lds_tile_mm<D, LD, true, false>(Lt, Mb, (t / NB) * 16, (t % NB) * 16, lane);
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
-        const int t = wave + 4 * q;
+        const int t = wave + NW * q;
         const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
 #pragma unroll
         for (int u = 0; u < 4; ++u) Lt[(i0 + 4 * (lane >> 4) + u) * LD + j0 + (lane & 15)] = y[q][u];
     }
     __syncthreads();
     // S^+ = Y Y^T
-    for (int t = wave; t < NB * NB; t += 4) {
+    for (int t = wave; t < NB * NB; t += NW) {
         const int i0 = (t / NB) * 16, j0 = (t % NB) * 16;
         const f32x4v v = lds_tile_mm<D, LD, false, true>(Lt, Lt, i0, j0, lane);
 #pragma unroll
