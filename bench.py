@@ -488,7 +488,11 @@ def main() -> int:
 
         lib = oracle.load()
         S = max(1, min(args.cpu_sample_layers, L))
-        steps = 2 * R + 1  # refreshes at 0 and R, 2R - 1 non-refresh steps per layer
+        # the oracle refreshes at every step t with t % R == 0: at least two refreshes
+        # and about 10-30 s of oracle work over the sample
+        steps = min(4 * R, max(R + 1, 64))
+        n_ref = -(-steps // R)
+        n_norm = steps - n_ref
         t_one = t_all = 0.0
         for l in range(S):
             x = wl.make_layer(cfg, l, device=dev, cfg_index=ci, steps=steps)
@@ -502,8 +506,8 @@ def main() -> int:
             t_one += c1 - c0
             t_all += c2 - c1
         t_ref = t_one / S
-        # the full trajectory holds 2 refresh steps and steps - 2 non-refresh ones
-        t_norm = max((t_all / S - 2 * t_ref) / (steps - 2), 0.0)
+        # the full trajectory holds n_ref refresh steps and n_norm non-refresh ones
+        t_norm = max((t_all / S - n_ref * t_ref) / n_norm, 0.0) if n_norm else 0.0
         cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
         # the same oracle on one core: one layer's refresh step and one plain step
         cores = oracle.num_threads(lib)
@@ -531,7 +535,8 @@ def main() -> int:
                "single_core_value": round(one_us, 1),
                "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()},
                "sample": (f"{S} of {L} layers x {steps + 1} oracle layer-steps each (one refresh "
-                          f"step alone, then {steps} steps with refreshes at 0 and {R}) of "
+                          f"step alone, then {steps} steps with {n_ref} refreshes, at multiples "
+                          f"of {R}) of "
                           f"{cfg.name}; per-layer costs amortised over R={R} and scaled to {L} "
                           f"layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
                           f"layer-step, {t_one + t_all:.1f} s of oracle time); single_core_value "
