@@ -71,6 +71,7 @@ SMALL = [
     (1, 8, 2, 2, 64, 1500, 1500, 1, 2, 0),     # N = l_kv: dense GQA
     (1, 4, 1, 2, 64, 300, 1, 1, 2, 0),         # N = 1
     (3, 4, 2, 3, 128, 17, 5, 2, 3, 2),         # l_kv shorter than one tile
+    (1, 32768, 512, 1024, 64, 40, 6, 2, 2, 0),  # the largest head count, groups of 64
 ]
 
 
@@ -509,6 +510,7 @@ PIVOT_CASES = [
     (2, 12, 1, 4, 128, 20000, 100, 3, 7, 32, 0.05),
     (2, 6, 4, 5, 64, 3001, 37, 2, 5, 8, 0.05),
     (1, 8, 2, 4, 64, 30000, 64, 2, 5, 0, 3.0),   # the query changes a lot between refreshes
+    (1, 32768, 512, 1024, 64, 300, 8, 2, 4, 0, 0.05),  # the largest head count
 ]
 
 
