@@ -83,6 +83,16 @@ def test_small_trajectories(case):
     full_check(x["Q"], x["K"], x["V"], N, R, "small")
 
 
+def test_longest_cache():
+    """The longest cache the plan accepts at d = 128 (l_kv d 2 bytes just below 2^31 per
+    head): 64-bit offsets, 1024 segments per row, a ragged last chunk; every position
+    checked against the oracle."""
+    l_kv = (1 << 23) - 5
+    x = wl.make_random(1, 2, 1, 1, 128, l_kv, seed=11, device="cuda", steps=2, planted=64,
+                       drift=0.05)
+    full_check(x["Q"], x["K"], x["V"], 1000, 2, "longest cache")
+
+
 def test_llama_32k_full_trajectory():
     cfg = wl.CONFIGS[1]
     x = wl.make_layer(cfg, 0, device="cuda")
