@@ -111,6 +111,25 @@ def test_merge_matches_oracle(name, cfg, seed):
     _check_weights(cfg, Wm, X, Q, W, got["pairs"])
 
 
+def test_merge_single_token_fits_exactly():
+    """One calibration token and one query head per group (n = 1, h_q = h_kt): the merged
+    key of a pair can reproduce both heads' logits (two constraints on d entries), so eq. 13
+    is zero at eq. 15 for every pair, and S_a + S_b has rank 2.  The GPU's pair costs are zero
+    up to rounding against the pair's logit energy, and its merged projections (a forced
+    pairing, since every pairing ties) equal the oracle's eq. 15."""
+    cfg = MergeConfig("t", n=1, h_q=4, h_kt=4, d=64, d_model=64)
+    pairs = [(0, 1), (2, 3)]
+    X, Q, W, got = _run(cfg, 16, pairs_in=pairs)
+    keys = (_f64(X) @ _f64(W).T).reshape(cfg.h_kt, cfg.d)       # the token's key per head
+    logit = (_f64(Q)[0] * keys).sum(-1)                          # query head j reads head j
+    w = got["w"]
+    for a, b in itertools.combinations(range(cfg.h_kt), 2):
+        energy = logit[a] ** 2 + logit[b] ** 2
+        assert abs(w[a, b]) <= 1e-4 * energy, (a, b, w[a, b], energy)
+    assert got["pairs"] == pairs
+    _check_weights(cfg, got["W_merged"].reshape(cfg.h_kt // 2, cfg.d, -1), X, Q, W, pairs)
+
+
 def test_merge_sixteen_heads():
     """h_kt = 16 (the largest supported): 120 pair costs and the 2^16-state matching."""
     cfg = MergeConfig("t", n=96, h_q=16, h_kt=16, d=64, d_model=128)

@@ -71,6 +71,7 @@ SMALL = [
     (1, 8, 2, 2, 64, 1500, 1500, 1, 2, 0),     # N = l_kv: dense GQA
     (1, 4, 1, 2, 64, 300, 1, 1, 2, 0),         # N = 1
     (3, 4, 2, 3, 128, 17, 5, 2, 3, 2),         # l_kv shorter than one tile
+    (1, 4, 2, 2, 64, 1, 1, 1, 2, 0),           # a single cache position
     (1, 32768, 512, 1024, 64, 40, 6, 2, 2, 0),  # the largest head count, groups of 64
 ]
 
