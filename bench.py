@@ -142,7 +142,7 @@ def merge_bench(torch, reps: int, warmup: int = 2) -> dict:
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
     res = {}
-    for cfg in wl.MERGE_CONFIGS[1:]:
+    for cfg in map(wl.merge_config, wl.MERGE_BENCH):
         n, h_q, h_kt, d, dm = cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model
         X, Q, W = wl.make_merge_inputs(cfg, 1, dev)
         m = KeyMerge(n, h_q, h_kt, d, dm, device=dev)

@@ -63,6 +63,14 @@ CONFIGS = [
 ]
 
 
+def config(name: str) -> SagaConfig:
+    """The decode workload of that name."""
+    for c in CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
 def config_index(cfg: SagaConfig) -> int:
     for i, c in enumerate(CONFIGS):
         if c.name == cfg.name:
@@ -198,6 +206,16 @@ MERGE_CONFIGS = [
     MergeConfig("merge-llama32-1b-16k", n=16384, h_q=32, h_kt=8, d=64, d_model=2048),
     MergeConfig("merge-qwen25-1.5b-16k", n=16384, h_q=12, h_kt=2, d=128, d_model=1536, decay=64.0),
 ]
+# the layer shapes the key merge is benchmarked on (16384 calibration tokens)
+MERGE_BENCH = ("merge-llama32-1b-16k", "merge-qwen25-1.5b-16k")
+
+
+def merge_config(name: str) -> MergeConfig:
+    """The key-merge workload of that name."""
+    for c in MERGE_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
 
 
 def make_merge_inputs(cfg: MergeConfig, seed: int, device="cpu", planted: bool = False):

@@ -21,7 +21,8 @@ import torch
 
 from oracle import key_merge as km
 from sparse_asymmetric_head_amd.merge import KeyMerge
-from sparse_asymmetric_head_amd.workload import MERGE_CONFIGS, MergeConfig, make_merge_inputs
+from sparse_asymmetric_head_amd.workload import (MERGE_BENCH, MergeConfig, make_merge_inputs,
+                                                 merge_config)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +95,7 @@ def _check_weights(cfg, Wm, X, Q, W, pairs):
 
 
 CASES = [
-    ("llama-tiny", MERGE_CONFIGS[0], 1),
+    ("llama-tiny", merge_config("merge-tiny"), 1),
     ("llama-ragged", MergeConfig("t", n=517, h_q=32, h_kt=8, d=64, d_model=192), 2),
     ("qwen-tiny", MergeConfig("t", n=250, h_q=12, h_kt=2, d=128, d_model=256, decay=64.0), 3),
     ("uneven-groups", MergeConfig("t", n=200, h_q=10, h_kt=4, d=64, d_model=128), 4),
@@ -143,7 +144,7 @@ def test_merge_sixteen_heads():
 def test_merge_planted_pairs_are_found_exactly():
     """Identical teacher heads in pairs: the GPU finds that pairing with zero cost,
     and each merged key is the shared projection."""
-    cfg = MERGE_CONFIGS[0]
+    cfg = merge_config("merge-tiny")
     X, Q, W, got = _run(cfg, 7, planted=True)
     want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
     assert got["pairs"] == want["pairs"]
@@ -160,7 +161,7 @@ def test_merge_planted_pairs_are_found_exactly():
 def test_merge_forced_pairing():
     """A caller-chosen pairing: costs are unchanged, the total and the merged keys
     follow that pairing (given in any order)."""
-    cfg = MERGE_CONFIGS[0]
+    cfg = merge_config("merge-tiny")
     forced = [(7, 0), (2, 5), (1, 6), (4, 3)]
     X, Q, W, got = _run(cfg, 8, pairs_in=forced)
     canon = sorted((min(a, b), max(a, b)) for a, b in forced)
@@ -241,7 +242,7 @@ def test_merge_unqueried_group_costs_nothing():
 
 
 def test_merge_repeat_is_deterministic():
-    cfg = MERGE_CONFIGS[0]
+    cfg = merge_config("merge-tiny")
     X, Q, W = [t.cuda() for t in make_merge_inputs(cfg, 11, "cpu")]
     m = KeyMerge(cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model)
     m(X, Q, W)
@@ -251,7 +252,7 @@ def test_merge_repeat_is_deterministic():
     assert torch.equal(first[2], m.pairs)
 
 
-@pytest.mark.parametrize("cfg", MERGE_CONFIGS[1:], ids=[c.name for c in MERGE_CONFIGS[1:]])
+@pytest.mark.parametrize("cfg", [merge_config(n) for n in MERGE_BENCH], ids=MERGE_BENCH)
 def test_merge_full_size_properties(cfg):
     """At the benchmark sizes (16384 calibration tokens, the Llama-3.2-1B and
     Qwen2.5-1.5B layer shapes), where eq. 13 as written is out of the oracle's
@@ -281,7 +282,7 @@ def test_merge_full_size_properties(cfg):
         assert np.abs(Wm[i] - Wt[a]).max() <= RTOL * np.abs(Wt[a]).max()
 
 
-@pytest.mark.parametrize("cfg", MERGE_CONFIGS[1:], ids=[c.name for c in MERGE_CONFIGS[1:]])
+@pytest.mark.parametrize("cfg", [merge_config(n) for n in MERGE_BENCH], ids=MERGE_BENCH)
 def test_merge_full_width_prefix_matches_oracle(cfg):
     """The benchmark layer width (d_model 2048 / 1536, all heads) on a 384-token
     prefix of its calibration set: element-wise parity with the oracle."""

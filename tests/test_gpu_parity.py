@@ -55,7 +55,7 @@ def full_check(Q, K, V, N, R, tag=""):
 
 
 def test_tiny_config_full_trajectory():
-    cfg = wl.CONFIGS[0]
+    cfg = wl.config("tiny")
     x = wl.make_layer(cfg, 0, device="cuda")
     full_check(x["Q"], x["K"], x["V"], cfg.N, cfg.R, "tiny")
 
@@ -95,7 +95,7 @@ def test_longest_cache():
 
 
 def test_llama_32k_full_trajectory():
-    cfg = wl.CONFIGS[1]
+    cfg = wl.config("llama32-1b-32k")
     x = wl.make_layer(cfg, 0, device="cuda")
     flips = full_check(x["Q"], x["K"], x["V"], cfg.N, cfg.R, cfg.name)
     print(f"[parity] {cfg.name}: boundary flips within the band: {flips}", flush=True)
@@ -138,18 +138,18 @@ def sampled_check(cfg, layer, steps, rows):
 
 
 def test_llama_128k_16_layers_sampled():
-    cfg = wl.CONFIGS[2]
+    cfg = wl.config("llama32-1b-128k-16L")
     for layer in (0, 7, 15):
         sampled_check(cfg, layer, steps=[0, 16, 33, 63], rows=[0, 9, 22, 31])
 
 
 def test_qwen_128k_sampled():
-    cfg = wl.CONFIGS[3]
+    cfg = wl.config("qwen25-1.5b-128k")
     sampled_check(cfg, 0, steps=[0, 31, 32, 63], rows=[0, 13, 30, 47])
 
 
 def test_stress_batch16_sampled():
-    cfg = wl.CONFIGS[4]
+    cfg = wl.config("stress-b16-64k")
     sampled_check(cfg, 0, steps=[0, 63, 64, 127], rows=[0, 3 * 32 + 17, 15 * 32 + 31, 8 * 32 + 5])
 
 
@@ -299,7 +299,7 @@ def test_full_attention_small(case):
 
 def test_full_attention_llama_128k():
     """SAGA full attention at the 128K Llama shape against the oracle."""
-    cfg = wl.CONFIGS[2]
+    cfg = wl.config("llama32-1b-128k-16L")
     x = wl.make_layer(cfg, 0, device="cuda", steps=1)
     B, h_q, h_k, h_v, d, l_kv = cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv
     ws = torch.empty(saga.saga_full_attention_workspace_bytes(B, h_q, h_k, h_v, d, l_kv),
@@ -312,9 +312,9 @@ def test_full_attention_llama_128k():
     assert rel_err(O.cpu().numpy().astype(np.float64), ref) <= OUT_RTOL
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3])
-def test_dense_gqa_full_size(ci):
-    cfg = wl.CONFIGS[ci]
+@pytest.mark.parametrize("name", ["llama32-1b-32k", "llama32-1b-128k-16L", "qwen25-1.5b-128k"])
+def test_dense_gqa_full_size(name):
+    cfg = wl.config(name)
     x = wl.make_dense_layer(cfg, 0, device="cuda")
     print(f"[parity] dense {cfg.name} h_kv={cfg.dense_h_kv}", flush=True)
     O = _dense(x["Q"], x["K"], x["V"])

@@ -15,7 +15,7 @@ def test_configs_shapes():
 
 
 def test_deterministic_and_seeded():
-    cfg = wl.CONFIGS[0]
+    cfg = wl.config("tiny")
     a = wl.make_layer(cfg, 0)
     b = wl.make_layer(cfg, 0)
     c = wl.make_layer(cfg, 1)
@@ -28,7 +28,7 @@ def test_deterministic_and_seeded():
 
 
 def test_planted_keys_near_group_mean():
-    cfg = wl.CONFIGS[0]
+    cfg = wl.config("tiny")
     x = wl.make_layer(cfg, 0)
     q0 = x["Q"][0, 0].float()  # [h_q][d]
     qbar = q0.mean(0)
@@ -39,7 +39,7 @@ def test_planted_keys_near_group_mean():
 
 
 def test_query_drift_scale():
-    cfg = wl.CONFIGS[0]
+    cfg = wl.config("tiny")
     Q = wl.make_layer(cfg, 0)["Q"].float()
     step = (Q[1:] - Q[:-1]).std().item()
     assert 0.03 < step < 0.08
@@ -53,7 +53,7 @@ def test_heavy_tail_planted():
 
 
 def test_dense_layer_shapes():
-    cfg = wl.CONFIGS[1].with_(l_kv=256)
+    cfg = wl.config("llama32-1b-32k").with_(l_kv=256)
     x = wl.make_dense_layer(cfg, 0)
     assert x["K"].shape == (1, 8, 256, 64) and x["V"].shape == (1, 8, 256, 64)
     assert x["Q"].shape == (1, 32, 64)
