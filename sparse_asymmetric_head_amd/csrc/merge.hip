@@ -1,7 +1,7 @@
 // merge.hip -- host side of the GQA -> SAGA key-head merge (C ABI in include/saga_merge.h).
 //
 // Launch sequence on one stream:
-//   k_kproj          K = X W_K^T                                  (n/128 x h_kt*d/128 blocks)
+//   k_kproj<BM>      K = X W_K^T                                  (n/BM x h_kt*d/128 blocks)
 //   k_gram<D,1>      per-chunk second moments S_r of each group's queries (h_kt items)
 //   k_gram<D,0>      per-chunk second moments G_p of K_a - K_b         (one item per pair)
 //   k_gram_reduce    fixed-order fp64 sum over chunks
@@ -103,16 +103,29 @@ size_t pinv_lds_bytes(int d) {
     return (size_t)2 * d * (d + 4) * sizeof(float) + (size_t)2 * d * sizeof(float);
 }
 
-// The pseudoinverse kernel for d = 128 takes more than 64 KB of dynamic LDS;
-// say so once per process.
+// The d = 128 pseudoinverse and the projection's LDS rings take more than
+// 64 KB of dynamic LDS; say so once per process.
 int lds_limits_once() {
     static int status = [] {
-        const hipError_t e = hipFuncSetAttribute((const void *)k_pair_pinv<128>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)pinv_lds_bytes(128));
-        return e == hipSuccess ? (int)SAGA_OK : (int)SAGA_ERR_HIP;
+        const hipFuncAttribute at = hipFuncAttributeMaxDynamicSharedMemorySize;
+        const bool ok =
+            hipFuncSetAttribute((const void *)k_pair_pinv<128>, at, (int)pinv_lds_bytes(128)) ==
+                hipSuccess &&
+            hipFuncSetAttribute((const void *)k_kproj<128>, at, (int)proj_lds_bytes(128)) ==
+                hipSuccess &&
+            hipFuncSetAttribute((const void *)k_kproj<256>, at, (int)proj_lds_bytes(256)) ==
+                hipSuccess;
+        return ok ? (int)SAGA_OK : (int)SAGA_ERR_HIP;
     }();
     return status;
+}
+
+// Projection tile height: 256 tokens when that still gives a block per compute
+// unit (256 blocks), else 128.
+template <int BM>
+void launch_kproj(const ProjArgs &pa, hipStream_t s) {
+    hipLaunchKernelGGL(k_kproj<BM>, dim3((unsigned)ceil_div(pa.n, BM), (unsigned)(pa.cols / kPBN)),
+                       dim3(proj_threads(BM)), proj_lds_bytes(BM), s, pa);
 }
 
 template <int D>
@@ -126,8 +139,8 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     float *Pm = (float *)(ws + p.off_Pm);
 
     ProjArgs pa{(const uint16_t *)X, (const uint16_t *)W_K, K, p.n, p.ldt, p.dm, p.h_kt * D};
-    hipLaunchKernelGGL(k_kproj, dim3((unsigned)ceil_div(p.n, kPBM), (unsigned)(p.h_kt * D / kPBN)),
-                       dim3(kThreads), 0, s, pa);
+    if (ceil_div(p.n, 256) * (p.h_kt * D / kPBN) >= 256) launch_kproj<256>(pa, s);
+    else launch_kproj<128>(pa, s);
 
     GramArgs ga{};
     ga.Q = (const uint16_t *)Q;

@@ -44,74 +44,119 @@ struct ProjArgs {
     const uint16_t *X;  // [n][dm] bf16
     const uint16_t *W;  // [cols][dm] bf16 (row r*D + c = channel c of teacher key head r)
     float *Kt;          // [cols][ldt] fp32, channel-major; tokens n .. ldt-1 written as zero
-    int64_t n, ldt;     // ldt: n rounded up to kPBM
+    int64_t n, ldt;     // ldt: n rounded up to 128
     int dm;
     int cols;
 };
 
-constexpr int kPBM = 128, kPBN = 128, kPBK = 64;    // block tile (tokens x columns x k)
+constexpr int kPBM = 128, kPBN = 128, kPBK = 64;    // token padding, block columns, k-stage
 
-// LDS tile [128 rows][64 k] bf16: row = 8 chunks of 16 B, chunk c of row r stored
+// LDS tile [rows][64 k] bf16: row = 8 chunks of 16 B, chunk c of row r stored
 // at chunk position c ^ (r & 7), so the 16 rows one MFMA operand read touches
 // fall on different banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
-// K = X W^T.  256 threads = 2 x 2 waves, each wave a 64 x 64 sub-tile of 4 x 4
-// MFMA 16x16x32 tiles; X and W tiles pass through LDS, double-buffered.
-__global__ __launch_bounds__(kThreads) void k_kproj(ProjArgs a) {
-    __shared__ u32x4 As[2][kPBM * 8];
-    __shared__ u32x4 Bs[2][kPBN * 8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t t0 = (int64_t)blockIdx.x * kPBM;
-    const int n0 = blockIdx.y * kPBN;
-    const int lr = tid >> 3, lc = tid & 7;          // load mapping: row lr + 32 i, chunk lc
-    const int64_t last = a.n - 1;
+// Stages of the projection's LDS ring: 144 KB (BM = 256) or 128 KB (BM = 128).
+__host__ __device__ constexpr int proj_stages(int bm) { return bm == 256 ? 3 : 4; }
+__host__ __device__ constexpr int proj_threads(int bm) { return bm / 64 * 2 * 64; }
+__host__ __device__ constexpr size_t proj_lds_bytes(int bm) {
+    return (size_t)proj_stages(bm) * (bm + kPBN) * 8 * 16;
+}
 
-    const uint16_t *xrow[4], *wrow[4];
+// s_waitcnt vmcnt(N) (the other counters left alone), N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that leaves the vector-memory counter alone (__syncthreads
+// waits for every outstanding load, the direct LDS loads of later stages too):
+// the caller has waited for what it needs; LDS operations are complete first
+// (lgkmcnt(0)), and the compiler keeps memory accesses on their side.
+__device__ __forceinline__ void barrier_keep_loads() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// K = X W^T.  Block tile BM tokens x 128 columns, BM/64 x 2 waves of 64 x 64
+// (4 x 4 MFMA 16x16x32 tiles each).  The X and W tiles of each 64-wide k-stage
+// go through a ring of proj_stages(BM) LDS stages filled by direct global->LDS
+// loads, so two (BM 256) or three (BM 128) stages are in flight while one is
+// multiplied, with no staging registers and one barrier per stage.  Lane l of a
+// direct load lands in LDS slot l of the load's 64 slots, so the XOR swizzle of
+// the 16-byte chunks (swz) is made by the choice of each lane's source address.
+template <int BM>
+__global__ __launch_bounds__(proj_threads(BM)) void k_kproj(ProjArgs a) {
+    constexpr int NW = proj_threads(BM) / 64;      // waves
+    constexpr int S = proj_stages(BM);             // ring stages
+    constexpr int SLOTS = (BM + kPBN) * 8;         // 16-byte chunks per stage
+    constexpr int LPW = SLOTS / (64 * NW);         // direct loads per wave and stage
+    static_assert(LPW * 64 * NW == SLOTS && (BM * 8) % 64 == 0, "stage split");
+    extern __shared__ u32x4 ring[];                // [S][SLOTS]: X rows, then W rows
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t t0 = (int64_t)blockIdx.x * BM;
+    const int n0 = blockIdx.y * kPBN;
+    const int64_t last = a.n - 1;
+    const int nk = a.dm / kPBK;
+
+    // source of this lane's chunk in each of the wave's loads; rows past n read
+    // the last token (their outputs are not kept)
+    const uint16_t *src[LPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int64_t t = t0 + lr + 32 * i;
-        t = t < last ? t : last;
-        xrow[i] = a.X + t * a.dm + lc * 8;
-        wrow[i] = a.W + (int64_t)(n0 + lr + 32 * i) * a.dm + lc * 8;
+    for (int j = 0; j < LPW; ++j) {
+        const int sl = (wave * LPW + j) * 64 + lane;   // X or W for the whole wave: uniform
+        if (sl < BM * 8) {
+            const int row = sl >> 3, ch = (sl & 7) ^ (row & 7);
+            int64_t t = t0 + row;
+            t = t < last ? t : last;
+            src[j] = a.X + t * a.dm + ch * 8;
+        } else {
+            const int row = (sl - BM * 8) >> 3, ch = (sl & 7) ^ (row & 7);
+            src[j] = a.W + (int64_t)(n0 + row) * a.dm + ch * 8;
+        }
     }
+    auto issue = [&](int kt) {
+        u32x4 *dst = ring + (kt % S) * SLOTS + wave * LPW * 64;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j)
+            __builtin_amdgcn_global_load_lds((const void *)(src[j] + kt * kPBK),
+                                             (__attribute__((address_space(3))) void *)(dst + j * 64),
+                                             16, 0, 0);
+    };
     f32x4v acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xa[4], wb[4];
-    auto gload = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xa[i] = ld16(xrow[i] + kt * kPBK);
-            wb[i] = ld16(wrow[i] + kt * kPBK);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            As[buf][swz(lr + 32 * i, lc)] = xa[i];
-            Bs[buf][swz(lr + 32 * i, lc)] = wb[i];
-        }
-    };
-    const int nk = a.dm / kPBK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    for (int st = 0; st < S - 1; ++st)
+        if (st < nk) issue(st);
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+        // this wave's loads of stage kt are done once at most the later stages'
+        // loads are outstanding; the barrier then makes every wave's part visible
+        // and frees the slot of stage kt - 1 for stage kt + S - 1
+        const int later = min(S - 2, nk - 1 - kt);
+        if (later >= 2) wait_vmcnt<2 * LPW>();
+        else if (later == 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        barrier_keep_loads();
+        if (kt + S - 1 < nk) issue(kt + S - 1);
+        const u32x4 *As = ring + (kt % S) * SLOTS;
+        const u32x4 *Bs = As + BM * 8;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {               // two k-steps of 32 per tile
+        for (int s = 0; s < 2; ++s) {               // two k-steps of 32 per stage
             const int ch = s * 4 + (lane >> 4);
             bf16x8 af[4], bfr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                af[i] = as_bf16x8(As[cur][swz(wm * 64 + i * 16 + (lane & 15), ch)]);
-                bfr[i] = as_bf16x8(Bs[cur][swz(wn * 64 + i * 16 + (lane & 15), ch)]);
+                af[i] = as_bf16x8(As[swz(wm * 64 + i * 16 + (lane & 15), ch)]);
+                bfr[i] = as_bf16x8(Bs[swz(wn * 64 + i * 16 + (lane & 15), ch)]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -120,14 +165,14 @@ __global__ __launch_bounds__(kThreads) void k_kproj(ProjArgs a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
     }
     // lane holds rows (tokens) 4*(lane/16)+r, column lane%16 of each 16 x 16 tile:
-    // four consecutive tokens of one channel, one 16-byte store (zero past n)
+    // four consecutive tokens of one channel, one 16-byte store (zero past n,
+    // nothing past the padded token count ldt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+        if (t >= a.ldt) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4v v = acc[i][j];
