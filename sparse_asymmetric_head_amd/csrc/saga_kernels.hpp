@@ -382,9 +382,10 @@ constexpr int kWaveWin = 256;  // survivors staged per wave and window
 // the fifteenth of a segment are loaded by the whole wave, 64 per round);
 // groups of d/32 lanes then gather one survivor each per round, so the
 // loads stay dense.  Weights use the wave's running maximum (rescaled when a
-// later pass raises it); sums over lanes run through DPP; the one block
-// barrier comes at the end, where a thread per column rescales the eight
-// waves' partials to the row maximum and adds them in a fixed order.
+// later pass raises it); sums over lanes run through DPP and shuffles; at the
+// end two block barriers give every wave the row maximum, each wave rescales
+// its own sums to it, and a thread per column adds the eight waves' sums in a
+// fixed order.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     constexpr int DC = D / kAttendSplit;        // columns of this block
@@ -396,8 +397,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     static_assert(seg_words(1) >= 32, "128-byte record heads");
     __shared__ int wlt[kAttendWaves][kWaveWin];
     __shared__ float wls[kAttendWaves][kWaveWin];
-    __shared__ float wpart[kAttendWaves * 4][DC];
-    __shared__ float wlp[kAttendWaves * 4];
+    __shared__ float wpart[kAttendWaves][DC];
+    __shared__ float wlp[kAttendWaves];
     __shared__ float wmx[kAttendWaves];
     __shared__ int wcnt[kAttendWaves];
 
@@ -446,6 +447,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         }
         const int n = (int)hd[0][0];
         const uint32_t mk = wave_max_u32_dpp(n > 0 ? hd[0][1] : 0u);
+        const int nmax = (int)wave_max_u32_dpp((uint32_t)n);  // the wave's longest segment
         const int incl = wave_incl_scan(h == 0 ? n : 0);
         const int tot = __builtin_amdgcn_readlane(incl, 63);
         if (tot == 0) continue;  // wave-uniform
@@ -463,6 +465,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             // survivors k < fifteen from the registers: lane h takes k = h mod 2
 #pragma unroll
             for (int k = 0; k < kRecHead; ++k) {
+                if (k >= nmax) break;  // wave-uniform
                 const int e = ex + k;
                 if ((k & 1) == h && k < n && e >= w0 && e < w1) {
                     lt[e - w0] = (int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4];
@@ -512,39 +515,46 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // list reused by the next window
         }
     }
-    // lanes of one column group: sum within each 16-lane row, then the
-    // (wave, row) partials go to LDS
+    // Every wave learns the row maximum, rescales its own sums to it in
+    // registers and adds its four 16-lane rows (lanes of one column group:
+    // DPP within a row, then xor-shuffles across rows, a fixed order); one
+    // thread per column then adds the eight waves' sums in wave order.
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<LPE>(acc[i]);
     l = row_sum_mod<LPE>(l);
-    const int wr = wave * 4 + (lane >> 4);
-    if ((lane & 15) < LPE) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) wpart[wr][cl * 8 + i] = acc[i];
-        if (cl == 0) wlp[wr] = l;
-    }
     if (lane == 0) {
         wmx[wave] = m_run;
         wcnt[wave] = cnt_w;
     }
     __syncthreads();
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kAttendWaves; ++q) M = fmaxf(M, wmx[q]);
+    const float f = cnt_w > 0 ? expf(m_run - M) : 0.f;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float v = acc[i] * f;
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[i] = v;
+    }
+    l *= f;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (lane < LPE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wpart[wave][cl * 8 + i] = acc[i];
+        if (cl == 0) wlp[wave] = l;
+    }
+    __syncthreads();
     if (tid < DC) {
-        float M = -INFINITY;
+        float so = 0.f, sl = 0.f;
         int total = 0;
 #pragma unroll
         for (int q = 0; q < kAttendWaves; ++q) {
-            M = fmaxf(M, wmx[q]);
+            so += wpart[q][tid];
+            sl += wlp[q];
             total += wcnt[q];
-        }
-        float so = 0.f, sl = 0.f;
-#pragma unroll
-        for (int q = 0; q < kAttendWaves; ++q) {
-            const float f = wcnt[q] > 0 ? expf(wmx[q] - M) : 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                so += f * wpart[q * 4 + r][tid];
-                sl += f * wlp[q * 4 + r];
-            }
         }
         a.O[(int64_t)row * D + csl * DC + tid] = sl > 0.f ? so / sl : 0.f;
         if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
