@@ -1481,12 +1481,26 @@ __global__ __launch_bounds__(kThreads) void k_dense_merge(DenseMergeArgs a) {
     for (int q = 0; q < kWaves; ++q) M = fmaxf(M, smax[q]);
     const int c = threadIdx.x % D, grp = threadIdx.x / D;
     float acc = 0.f, L = 0.f;
-    for (int k = grp; k < a.n_chunk; k += NG) {
-        const float *pk = pr + (int64_t)k * (D + 4);
-        const float mk = pk[0];
-        const float f = (mk == -INFINITY) ? 0.f : exp2f(mk - M);
-        acc += f * pk[4 + c];
-        L += f * pk[1];
+    // the group's chunks grp, grp + NG, ... in order, UNR at a time with all
+    // their loads in flight
+    constexpr int UNR = 8;
+    for (int k0 = grp; k0 < a.n_chunk; k0 += NG * UNR) {
+        float mk[UNR], vk[UNR], lk[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int k = k0 + u * NG;
+            const bool ok = k < a.n_chunk;
+            const float *pk = pr + (int64_t)(ok ? k : k0) * (D + 4);
+            mk[u] = ok ? pk[0] : -INFINITY;
+            vk[u] = pk[4 + c];
+            lk[u] = pk[1];
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const float f = (mk[u] == -INFINITY) ? 0.f : exp2f(mk[u] - M);
+            acc += f * vk[u];
+            L += f * lk[u];
+        }
     }
     sm[grp][c] = acc;
     if (c == 0) sl[grp] = L;
