@@ -462,15 +462,22 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         const uint64_t big = ballot(h == 0 && n > kRecHead);
         for (int w0 = 0; w0 < tot; w0 += kWaveWin) {
             const int w1 = min(tot, w0 + kWaveWin);
-            // survivors k < fifteen from the registers: lane h takes k = h mod 2
-#pragma unroll
-            for (int k = 0; k < kRecHead; ++k) {
-                if (k >= nmax) break;  // wave-uniform
+            // survivors k < fifteen from the registers: lane h takes k = h mod 2;
+            // the upper seven only when some segment of the wave reaches them
+            // (one wave-uniform branch; a branch per survivor costs more where
+            // segments are long)
+            auto stage = [&](int k) {
                 const int e = ex + k;
                 if ((k & 1) == h && k < n && e >= w0 && e < w1) {
                     lt[e - w0] = (int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4];
                     ls[e - w0] = __uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]);
                 }
+            };
+#pragma unroll
+            for (int k = 0; k < 8; ++k) stage(k);
+            if (nmax > 8) {
+#pragma unroll
+                for (int k = 8; k < kRecHead; ++k) stage(k);
             }
             // the rest of long segments, 64 entries per wave round
             for (uint64_t bm = big; bm != 0ull; bm &= bm - 1ull) {
