@@ -130,6 +130,7 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
 
 struct DensePlan {
     int rows, gmax, nv, n_vsub;
+    int run;  // query heads per value head when every block's heads come in whole runs, else 0
     int64_t chunk_len;
     int n_chunk;
     size_t total;
@@ -190,6 +191,9 @@ int make_dense_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, Dense
     if (gmax > 16) return SAGA_ERR_UNSUPPORTED;
     p->rows = B * h_q;
     p->gmax = (int)gmax;
+    // h_v | h_q and h_k | h_v: a group's first query head, and the first query
+    // head of each subset, start a run of h_q/h_v heads on one value head
+    p->run = (p->nv > 1 && h_q % h_v == 0 && h_v % h_k == 0) ? h_q / h_v : 0;
     const int64_t pairs = (int64_t)B * h_k * p->n_vsub;
     int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetDenseBlocks), kChunkUnit) * kChunkUnit;
     const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kChunkUnit) * kChunkUnit;
@@ -344,15 +348,42 @@ int run_pivot_refresh(const Plan &p, const void *Q, const void *K, float *tau, i
 }
 
 template <int D, int GMAX, int NV>
-void launch_dense_t(const DenseArgs &a, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((k_dense<D, GMAX, NV>), dim3(blocks), dim3(kThreads), 0, s, a);
+void launch_dense_t(const DenseArgs &a, int run, int blocks, hipStream_t s) {
+    // a compile-time value-head map for runs of up to 4 query heads per
+    // value head that fit the block's head count; else the run-time lookup
+    const dim3 g(blocks), t(kThreads);
+    if constexpr (NV > 1) {
+        if (run == 1) {
+            hipLaunchKernelGGL((k_dense<D, GMAX, NV, 1>), g, t, 0, s, a);
+            return;
+        }
+        if constexpr (2 * NV <= GMAX) {
+            if (run == 2) {
+                hipLaunchKernelGGL((k_dense<D, GMAX, NV, 2>), g, t, 0, s, a);
+                return;
+            }
+        }
+        if constexpr (3 * NV <= GMAX) {
+            if (run == 3) {
+                hipLaunchKernelGGL((k_dense<D, GMAX, NV, 3>), g, t, 0, s, a);
+                return;
+            }
+        }
+        if constexpr (4 * NV <= GMAX) {
+            if (run == 4) {
+                hipLaunchKernelGGL((k_dense<D, GMAX, NV, 4>), g, t, 0, s, a);
+                return;
+            }
+        }
+    }
+    hipLaunchKernelGGL((k_dense<D, GMAX, NV, 0>), g, t, 0, s, a);
 }
 
 template <int D, int NV>
 void launch_dense_g(const DensePlan &p, const DenseArgs &a, int blocks, hipStream_t s) {
-    if (p.gmax <= 4) launch_dense_t<D, 4, NV>(a, blocks, s);
-    else if (p.gmax <= 8) launch_dense_t<D, 8, NV>(a, blocks, s);
-    else launch_dense_t<D, 16, NV>(a, blocks, s);
+    if (p.gmax <= 4) launch_dense_t<D, 4, NV>(a, p.run, blocks, s);
+    else if (p.gmax <= 8) launch_dense_t<D, 8, NV>(a, p.run, blocks, s);
+    else launch_dense_t<D, 16, NV>(a, p.run, blocks, s);
 }
 
 // Dense split-KV decode (key heads h_k, value heads h_v) and the merge of

@@ -1248,7 +1248,12 @@ struct DenseArgs {
 // P*V on the VALU (each lane owns 8 columns of a few rows of every tile, of
 // each of the subset's NV value heads; a query head adds the rows of its own
 // value head, a wave-uniform choice).  NV = 1 is dense GQA (h_k = h_v).
-template <int D, int GMAX, int NV>
+// RUN > 0: every value head serves RUN consecutive query heads and the
+// block's first query head starts such a run (h_q/h_v = RUN and h_k divides
+// h_v), so block head h uses subset value head h / RUN, known at compile
+// time; RUN = 0 looks the value head up per head at run time, one branch per
+// head and V row.
+template <int D, int GMAX, int NV, int RUN>
 __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     constexpr int KS = D / 32;
     constexpr int U = NV == 1 ? SAGA_SELECT_U * 64 / D : 1;
@@ -1305,7 +1310,7 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
 #pragma unroll
     for (int vi = 0; vi < NV; ++vi)
         Vb[vi] = a.V + ((int64_t)b * a.h_v + min(v_lo + vi, a.h_v - 1)) * a.l_kv * D;
-    if constexpr (NV > 1) {
+    if constexpr (NV > 1 && RUN == 0) {
 #pragma unroll
         for (int h = 0; h < GMAX; ++h)
             vix[h] = (j_lo + h) * a.h_v / a.h_q - v_lo;
@@ -1390,7 +1395,11 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
                     const int rr = u * 16 + vr + k * RPI;
 #pragma unroll
                     for (int h = 0; h < GMAX; ++h) {
-                        if (NV > 1 && vix[h] != vi) continue;  // uniform: another value head
+                        if constexpr (NV > 1 && RUN > 0) {
+                            if (h / RUN != vi) continue;  // resolved at compile time
+                        } else if (NV > 1 && vix[h] != vi) {
+                            continue;  // uniform: another value head
+                        }
                         const float p = p_lds[wave][rr][h];
 #pragma unroll
                         for (int i = 0; i < 8; ++i) o[h][i] += p * vf[i];

@@ -277,6 +277,8 @@ FULL = [
     (2, 6, 4, 5, 64, 1001),      # non-integer head ratios, ragged tail
     (1, 8, 2, 2, 64, 700),       # h_k = h_v: dense GQA
     (1, 8, 2, 4, 64, 1234),      # two value heads per key head
+    (1, 16, 2, 4, 64, 999),      # runs of four query heads per value head
+    (1, 12, 4, 6, 64, 800),      # h_v divides h_q but h_k does not divide h_v
 ]
 
 
