@@ -189,10 +189,10 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     };
 
     // Score, compare and stage one wave iteration (U tiles starting at t0).
-    auto process = [&](const u32x4 (&kin)[U][KS], int64_t t0) {
-        // Whole iteration inside the chunk (every iteration but possibly the
-        // last): no per-element position checks.
-        const bool inside = t0 + 16 * U <= t_end;
+    // INSIDE: the whole iteration lies inside the chunk (every iteration but
+    // possibly the last), so the compare needs no position checks.
+    auto process = [&](const u32x4 (&kin)[U][KS], int64_t t0, auto inside_tag) {
+        constexpr bool INSIDE = decltype(inside_tag)::value;
 #if SAGA_KT_LDS
         // Row r, 16-byte column c of tile u sits at slot r*CPR + (c ^ (r & 7)):
         // eight consecutive lanes of either access touch eight distinct bank
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t tr = t0 + u * 16 + lq * 4;  // position of acc[0]
-            const int rem = inside ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - tr));
+            const int rem = INSIDE ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - tr));
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
                     uint64_t m[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        pr[r] = (r < rem) && (sc[r] >= tau_l[nt]);
+                        pr[r] = INSIDE ? sc[r] >= tau_l[nt] : (r < rem) && (sc[r] >= tau_l[nt]);
                         m[r] = ballot(pr[r]);
                     }
                     if ((m[0] | m[1] | m[2] | m[3]) != 0ull) {
@@ -307,14 +307,21 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     int64_t t0 = t_begin + wave * 16 * U;
     if (t0 < t_end) {
         u32x4 ka[U][KS], kb[U][KS];
+        // a full iteration, or the chunk's partial last one
+        auto step = [&](const u32x4 (&k)[U][KS], int64_t t) {
+            if (t + 16 * U <= t_end)
+                process(k, t, std::true_type{});
+            else
+                process(k, t, std::false_type{});
+        };
         load_tiles(ka, t0);
         for (;;) {
             load_tiles(kb, t0 + kStride);   // next tiles (clamped past the end)
-            process(ka, t0);
+            step(ka, t0);
             t0 += kStride;
             if (t0 >= t_end) break;
             load_tiles(ka, t0 + kStride);
-            process(kb, t0);
+            step(kb, t0);
             t0 += kStride;
             if (t0 >= t_end) break;
         }
