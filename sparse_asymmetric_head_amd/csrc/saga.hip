@@ -282,10 +282,10 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.O = O;
     aa.counts = counts;
     if (p.d == 64)
-        hipLaunchKernelGGL(k_attend<64>, dim3(attend_grid(p.rows)), dim3(kAttendThreads), 0, s,
+        hipLaunchKernelGGL(k_attend<64>, dim3(attend_grid(p.rows, 64)), dim3(kAttendThreads), 0, s,
                            aa);
     else
-        hipLaunchKernelGGL(k_attend<128>, dim3(attend_grid(p.rows)), dim3(kAttendThreads), 0, s,
+        hipLaunchKernelGGL(k_attend<128>, dim3(attend_grid(p.rows, 128)), dim3(kAttendThreads), 0, s,
                            aa);
     return launch_status();
 }

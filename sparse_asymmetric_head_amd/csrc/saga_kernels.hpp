@@ -360,51 +360,50 @@ struct AttendArgs {
 
 constexpr int kAttendWaves = 8;
 constexpr int kAttendThreads = kAttendWaves * kWave;
-#ifndef SAGA_ATTEND_SPLIT
-#define SAGA_ATTEND_SPLIT 4  // blocks per row, each owning d/SPLIT output columns
-#endif
-constexpr int kAttendSplit = SAGA_ATTEND_SPLIT;
+constexpr int kAttendCols = 16;  // output columns per attend block: a lane pair's 2 x 16 bytes
 #ifndef SAGA_ATTEND_XCD
 #define SAGA_ATTEND_XCD 1  // the blocks of a row share an XCD (and its L2)
 #endif
 constexpr int kXcds = 8;  // workgroups are dealt round-robin over the 8 XCDs
 
-// Blocks launched for the attend kernel over `rows` rows.
-__host__ __device__ constexpr int64_t attend_grid(int64_t rows) {
-    return SAGA_ATTEND_XCD ? (rows + kXcds - 1) / kXcds * kXcds * kAttendSplit
-                           : rows * kAttendSplit;
+// Attend blocks per row: block c owns output columns [16c, 16c + 16).
+__host__ __device__ constexpr int attend_split(int d) { return d / kAttendCols; }
+
+// Blocks launched for the attend kernel over `rows` rows of head size d.
+__host__ __device__ constexpr int64_t attend_grid(int64_t rows, int d) {
+    return SAGA_ATTEND_XCD ? (rows + kXcds - 1) / kXcds * kXcds * attend_split(d)
+                           : rows * attend_split(d);
 }
 
-constexpr int kWaveWin = 256;  // survivors staged per wave and window
+constexpr int kWaveWin = 256;  // tail survivors staged per wave and window
 
-// kAttendSplit blocks per row (b, j), block c owning output columns
-// [c*D/S, (c+1)*D/S); every block of a row reads the row's records the same
-// way and gathers the same survivors in the same order, so the blocks agree
-// on the weight sum and the result is deterministic.
-// The two lanes of pair i of a wave own segment i of the pass
-// (256 segments per pass over the block): each loads one half of the
-// record's first 128 bytes and they swap halves with DPP, so both hold the
-// count, the max key and the first fifteen survivors.  A DPP scan of the
-// counts places the wave's survivors in a wave-private LDS list (entries past
-// the fifteenth of a segment are loaded by the whole wave, 64 per round);
-// groups of d/32 lanes then gather one survivor each per round, so the
-// loads stay dense.  Weights use the wave's running maximum (rescaled when a
-// later pass raises it); sums over lanes run through DPP and shuffles; at the
-// end two block barriers give every wave the row maximum, each wave rescales
-// its own sums to it, and a thread per column adds the eight waves' sums in a
-// fixed order.
+// d/16 blocks per row (b, j), block c owning output columns [16c, 16c + 16);
+// every block of a row reads the row's records the same way and gathers the
+// same survivors in the same lanes and order, so the blocks agree on the
+// weight sum and the result is deterministic.
+// The two lanes of pair i of a wave own segment i of the pass (256 segments
+// per pass over the block): each loads one half of the record's first 128
+// bytes and they swap halves with DPP, so both hold the count, the max key
+// and the first fifteen survivors.  The pair gathers those fifteen itself,
+// lane h taking columns 8h .. 8h + 8 of the block's sixteen, all loads in
+// flight at once, with no list to build first.  Entries past the fifteenth
+// of long segments go through a wave-private LDS list (a DPP scan of the
+// tail lengths places them; the whole wave loads them, 64 per round) and
+// are gathered by lane pairs, 32 per round.  Weights use the wave's running
+// maximum (rescaled when a later pass raises it); at the end two block
+// barriers give every wave the row maximum, each wave rescales its own sums
+// to it, and a thread per column adds the eight waves' sums in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
-    constexpr int DC = D / kAttendSplit;        // columns of this block
-    constexpr int LPE = DC / 8;                 // lanes per survivor (16 B each)
-    constexpr int EPI = kWave / LPE;            // survivors per wave round
+    constexpr int S = attend_split(D);
+    constexpr int EPI = kWave / 2;              // tail survivors per wave round
     constexpr int UN = 4;
     constexpr int SEGP = kAttendThreads / 2;    // segments per pass
-    static_assert(LPE >= 1 && LPE <= 8 && DC % 8 == 0, "attend column split");
+    static_assert(S * kAttendCols == D, "attend column split");
     static_assert(seg_words(1) >= 32, "128-byte record heads");
     __shared__ int wlt[kAttendWaves][kWaveWin];
     __shared__ float wls[kAttendWaves][kWaveWin];
-    __shared__ float wpart[kAttendWaves][DC];
+    __shared__ float wpart[kAttendWaves][kAttendCols];
     __shared__ float wlp[kAttendWaves];
     __shared__ float wmx[kAttendWaves];
     __shared__ int wcnt[kAttendWaves];
@@ -412,11 +411,11 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #if SAGA_ATTEND_XCD
     const int xk = blockIdx.x / kXcds;
-    const int csl = xk % kAttendSplit;
-    const int row = xk / kAttendSplit * kXcds + blockIdx.x % kXcds;
+    const int csl = xk % S;
+    const int row = xk / S * kXcds + blockIdx.x % kXcds;
     if (row >= a.B * a.h_q) return;  // whole block: padding of the last XCD round
 #else
-    const int row = blockIdx.x / kAttendSplit, csl = blockIdx.x % kAttendSplit;
+    const int row = blockIdx.x / S, csl = blockIdx.x % S;
 #endif
     const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
     const int h = lane & 1;
@@ -432,8 +431,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     load_heads(0);  // first, so the row's setup overlaps the load latency
     const int b = row / a.h_q, j = row % a.h_q;
     const int vh = j * a.h_v / a.h_q;  // j * h_v < 2^30 (h_q <= 32768)
-    const int e_in = lane / LPE, cl = lane % LPE;
-    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + csl * DC + cl * 8;
+    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + csl * kAttendCols + h * 8;
     int *lt = wlt[wave];
     float *ls = wls[wave];
 
@@ -441,7 +439,16 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     float l = 0.f, m_run = -INFINITY;
-    int cnt_w = 0;
+    int cnt = 0;
+    // one gathered half row with weight p (the weight sum counts it on lane 0 of the pair)
+    auto add = [&](const u32x4 &v, float p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += p * bf_lo(v[i]);
+            acc[2 * i + 1] += p * bf_hi(v[i]);
+        }
+        l += h == 0 ? p : 0.f;
+    };
     for (int p0 = 0; p0 < a.n_sub; p0 += SEGP) {
         const int sg = p0 + (tid >> 1);
         if (p0 > 0) load_heads(p0);
@@ -453,44 +460,52 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             hd[4 + q] = h ? own[q] : oth;
         }
         const int n = (int)hd[0][0];
-        const uint32_t mk = wave_max_u32_dpp(n > 0 ? hd[0][1] : 0u);
         const int nmax = (int)wave_max_u32_dpp((uint32_t)n);  // the wave's longest segment
-        const int incl = wave_incl_scan(h == 0 ? n : 0);
-        const int tot = __builtin_amdgcn_readlane(incl, 63);
-        if (tot == 0) continue;  // wave-uniform
-        cnt_w += tot;
-        const int ex = incl - n;  // the pair's first slot in the wave's sequence
+        if (nmax == 0) continue;  // wave-uniform
+        const uint32_t mk = wave_max_u32_dpp(n > 0 ? hd[0][1] : 0u);
+        cnt += h == 0 ? n : 0;
         const float m_new = fmaxf(m_run, fkey_inv(mk));
         const float sc = expf(m_run - m_new);  // 0 while m_run is -inf
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] *= sc;
         l *= sc;
         m_run = m_new;
-        const uint64_t big = ballot(h == 0 && n > kRecHead);
+        // The pair's first fifteen survivors, straight from the registers; the
+        // upper seven only when some segment of the wave reaches them (one
+        // wave-uniform branch).
+        u32x4 vv[kRecHead];
+        auto issue = [&](int k) {
+            if (k < n) vv[k] = ld16(Vb + (int64_t)(int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4] * D);
+        };
+        auto take = [&](int k) {
+            if (k < n) add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
+        };
+#pragma unroll
+        for (int k = 0; k < 8; ++k) issue(k);
+        if (nmax > 8) {
+#pragma unroll
+            for (int k = 8; k < kRecHead; ++k) issue(k);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) take(k);
+        if (nmax > 8) {
+#pragma unroll
+            for (int k = 8; k < kRecHead; ++k) take(k);
+        }
+        if (nmax <= kRecHead) continue;  // wave-uniform: no tails
+        // Tails of the long segments: entry k >= 15 of the pair's segment goes
+        // to list slot ex + k - 15.
+        const int nt = h == 0 ? max(0, n - kRecHead) : 0;
+        const int incl = wave_incl_scan(nt);
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        const int ex = incl - nt;
+        const uint64_t big = ballot(nt > 0);
         for (int w0 = 0; w0 < tot; w0 += kWaveWin) {
             const int w1 = min(tot, w0 + kWaveWin);
-            // survivors k < fifteen from the registers: lane h takes k = h mod 2;
-            // the upper seven only when some segment of the wave reaches them
-            // (one wave-uniform branch; a branch per survivor costs more where
-            // segments are long)
-            auto stage = [&](int k) {
-                const int e = ex + k;
-                if ((k & 1) == h && k < n && e >= w0 && e < w1) {
-                    lt[e - w0] = (int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4];
-                    ls[e - w0] = __uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]);
-                }
-            };
-#pragma unroll
-            for (int k = 0; k < 8; ++k) stage(k);
-            if (nmax > 8) {
-#pragma unroll
-                for (int k = 8; k < kRecHead; ++k) stage(k);
-            }
-            // the rest of long segments, 64 entries per wave round
             for (uint64_t bm = big; bm != 0ull; bm &= bm - 1ull) {
                 const int src = __ffsll((unsigned long long)bm) - 1;
                 const int sn = __builtin_amdgcn_readlane(n, src);
-                const int sx = __builtin_amdgcn_readlane(ex, src);
+                const int sx = __builtin_amdgcn_readlane(ex, src) - kRecHead;  // slot of entry k: sx + k
                 const int ssg = __builtin_amdgcn_readlane(sg, src);
                 const int2 *pr = (const int2 *)(rb + (int64_t)ssg * a.seg_w) + 1;
                 const int k0 = max(kRecHead, w0 - sx), k1 = min(sn, w1 - sx);
@@ -505,46 +520,40 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             for (int e0 = 0; e0 < W; e0 += EPI * UN) {
                 int tt[UN];
                 float pp[UN];
-                u32x4 vv[UN];
+                u32x4 vt[UN];
 #pragma unroll
                 for (int u = 0; u < UN; ++u) {
-                    const int ei = e0 + u * EPI + e_in;
+                    const int ei = e0 + u * EPI + (lane >> 1);
                     tt[u] = ei < W ? lt[ei] : -1;
                     pp[u] = ei < W ? ls[ei] : 0.f;
                 }
 #pragma unroll
                 for (int u = 0; u < UN; ++u)
-                    vv[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
+                    vt[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int u = 0; u < UN; ++u) {
-                    const float p = tt[u] >= 0 ? expf(pp[u] - m_run) : 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[2 * i] += p * bf_lo(vv[u][i]);
-                        acc[2 * i + 1] += p * bf_hi(vv[u][i]);
-                    }
-                    l += (cl == 0) ? p : 0.f;
-                }
+                for (int u = 0; u < UN; ++u)
+                    if (tt[u] >= 0) add(vt[u], expf(pp[u] - m_run));
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // list reused by the next window
         }
     }
     // Every wave learns the row maximum, rescales its own sums to it in
-    // registers and adds its four 16-lane rows (lanes of one column group:
-    // DPP within a row, then xor-shuffles across rows, a fixed order); one
-    // thread per column then adds the eight waves' sums in wave order.
+    // registers and adds its lanes of each column (DPP within 16-lane rows,
+    // then xor-shuffles across rows, a fixed order); one thread per column
+    // then adds the eight waves' sums in wave order.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<LPE>(acc[i]);
-    l = row_sum_mod<LPE>(l);
+    for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<2>(acc[i]);
+    l = row_sum_mod<2>(l);
+    cnt = wave_sum_i32(cnt);
     if (lane == 0) {
         wmx[wave] = m_run;
-        wcnt[wave] = cnt_w;
+        wcnt[wave] = cnt;
     }
     __syncthreads();
     float M = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kAttendWaves; ++q) M = fmaxf(M, wmx[q]);
-    const float f = cnt_w > 0 ? expf(m_run - M) : 0.f;  // wave-uniform
+    const float f = cnt > 0 ? expf(m_run - M) : 0.f;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float v = acc[i] * f;
@@ -555,13 +564,13 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     l *= f;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (lane < LPE) {
+    if (lane < 2) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wpart[wave][cl * 8 + i] = acc[i];
-        if (cl == 0) wlp[wave] = l;
+        for (int i = 0; i < 8; ++i) wpart[wave][h * 8 + i] = acc[i];
+        if (h == 0) wlp[wave] = l;
     }
     __syncthreads();
-    if (tid < DC) {
+    if (tid < kAttendCols) {
         float so = 0.f, sl = 0.f;
         int total = 0;
 #pragma unroll
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             sl += wlp[q];
             total += wcnt[q];
         }
-        a.O[(int64_t)row * D + csl * DC + tid] = sl > 0.f ? so / sl : 0.f;
+        a.O[(int64_t)row * D + csl * kAttendCols + tid] = sl > 0.f ? so / sl : 0.f;
         if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
     }
 }
