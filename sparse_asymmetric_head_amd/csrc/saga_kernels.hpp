@@ -14,10 +14,11 @@
 //                        heads of the group, compare with tau, compact the
 //                        survivors through LDS into per-(row, segment)
 //                        records.                         [HBM-bound, hot]
-//   k_attend             per row (a few column blocks): read the segment
-//                        records, wave-local survivor lists in LDS, softmax
-//                        weights, gather of the survivors' V rows, fp32
-//                        accumulation, O.
+//   k_attend             per row (d/16 column blocks): read the segment
+//                        records, gather the survivors' V rows (the first
+//                        fifteen of a segment straight from the record head,
+//                        the rest through a wave-local list in LDS), softmax
+//                        weights, fp32 accumulation, O.
 // Refresh (every R steps) instead runs:
 //   k_select<.., true>   same score pass, writes fp32 A
 //   k_hist / k_select1 / k_collect / k_select_final   exact radix select
