@@ -209,6 +209,31 @@ bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                       ? n : 256;
+    }
+    return cus[dev];
+}
+
+template <int D>
+void launch_attend(const AttendArgs &aa, int64_t grid, bool direct15, bool spread, hipStream_t s) {
+    const dim3 g((unsigned)grid), t(kAttendThreads);
+    if (direct15) {
+        if (spread) hipLaunchKernelGGL((k_attend<D, 15, true>), g, t, 0, s, aa);
+        else hipLaunchKernelGGL((k_attend<D, 15, false>), g, t, 0, s, aa);
+    } else {
+        if (spread) hipLaunchKernelGGL((k_attend<D, 8, true>), g, t, 0, s, aa);
+        else hipLaunchKernelGGL((k_attend<D, 8, false>), g, t, 0, s, aa);
+    }
+}
+
 template <int D, int NT, bool MAT>
 void launch_select_t(const SelectArgs &a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((k_select<D, NT, MAT>), dim3(blocks), dim3(kThreads), 0, s, a);
@@ -281,12 +306,13 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.ld_kv = p.ld_kv;
     aa.O = O;
     aa.counts = counts;
+    const int64_t grid = attend_grid(p.rows, p.d);
+    const bool direct15 = grid <= device_cus();
+    const bool spread = p.N > (int64_t)kRecHead * p.n_sub;
     if (p.d == 64)
-        hipLaunchKernelGGL(k_attend<64>, dim3(attend_grid(p.rows, 64)), dim3(kAttendThreads), 0, s,
-                           aa);
+        launch_attend<64>(aa, grid, direct15, spread, s);
     else
-        hipLaunchKernelGGL(k_attend<128>, dim3(attend_grid(p.rows, 128)), dim3(kAttendThreads), 0, s,
-                           aa);
+        launch_attend<128>(aa, grid, direct15, spread, s);
     return launch_status();
 }
 

@@ -377,30 +377,40 @@ __host__ __device__ constexpr int64_t attend_grid(int64_t rows, int d) {
 }
 
 constexpr int kWaveWin = 256;  // tail survivors staged per wave and window
+// Attend launch choices, made per launch by the host:
+// DIRECT  survivors per segment gathered straight from the record head: 15
+//         (every one the head holds) when one block per CU covers the grid;
+//         8 where blocks must share CUs (103 instead of 136 VGPRs, so two
+//         8-wave blocks fit on a CU).
+// SPREAD  deal a pass's segments round-robin over the eight waves, for rows
+//         whose segments average more than fifteen survivors (few, long
+//         segments would otherwise leave most waves idle).
 
 // d/16 blocks per row (b, j), block c owning output columns [16c, 16c + 16);
 // every block of a row reads the row's records the same way and gathers the
 // same survivors in the same lanes and order, so the blocks agree on the
 // weight sum and the result is deterministic.
-// The two lanes of pair i of a wave own segment i of the pass (256 segments
-// per pass over the block): each loads one half of the record's first 128
+// The two lanes of a pair own one segment of the pass (256 segments per pass
+// over the block; pair i of the block, or with SPREAD pair i of wave w
+// takes segment 8i + w): each loads one half of the record's first 128
 // bytes and they swap halves with DPP, so both hold the count, the max key
-// and the first fifteen survivors.  The pair gathers those fifteen itself,
+// and the first fifteen survivors.  The pair gathers the first DIRECT itself,
 // lane h taking columns 8h .. 8h + 8 of the block's sixteen, all loads in
-// flight at once, with no list to build first.  Entries past the fifteenth
-// of long segments go through a wave-private LDS list (a DPP scan of the
-// tail lengths places them; the whole wave loads them, 64 per round) and
-// are gathered by lane pairs, 32 per round.  Weights use the wave's running
+// flight at once, with no list to build first.  Entries past those go
+// through a wave-private LDS list (a DPP scan of the tail lengths places
+// them; the whole wave loads them, 64 per round) and are gathered by lane
+// pairs, 32 per round.  Weights use the wave's running
 // maximum (rescaled when a later pass raises it); at the end two block
 // barriers give every wave the row maximum, each wave rescales its own sums
 // to it, and a thread per column adds the eight waves' sums in a fixed order.
-template <int D>
+template <int D, int DIRECT, bool SPREAD>
 __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     constexpr int S = attend_split(D);
     constexpr int EPI = kWave / 2;              // tail survivors per wave round
     constexpr int UN = 4;
     constexpr int SEGP = kAttendThreads / 2;    // segments per pass
     static_assert(S * kAttendCols == D, "attend column split");
+    static_assert(DIRECT >= 1 && DIRECT <= kRecHead, "direct survivors come from the record head");
     static_assert(seg_words(1) >= 32, "128-byte record heads");
     __shared__ int wlt[kAttendWaves][kWaveWin];
     __shared__ float wls[kAttendWaves][kWaveWin];
@@ -422,8 +432,12 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     const int h = lane & 1;
     // The two lanes of a pair load the halves of their segment's 128-byte head.
     u32x4 own[4];
+    // Pair lp of wave w owns segment p0 + 8 lp + w of the pass starting at p0:
+    // segments are dealt round-robin over the waves, so rows with few
+    // segments still keep every wave busy.
+    const int seg_in_pass = SPREAD ? (lane >> 1) * kAttendWaves + wave : tid >> 1;
     auto load_heads = [&](int p0) {
-        const int sg = p0 + (tid >> 1);
+        const int sg = p0 + seg_in_pass;
         const int32_t *rs = rb + (int64_t)sg * a.seg_w;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         l += h == 0 ? p : 0.f;
     };
     for (int p0 = 0; p0 < a.n_sub; p0 += SEGP) {
-        const int sg = p0 + (tid >> 1);
+        const int sg = p0 + seg_in_pass;
         if (p0 > 0) load_heads(p0);
         u32x4 hd[8];
 #pragma unroll
@@ -471,32 +485,31 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         for (int i = 0; i < 8; ++i) acc[i] *= sc;
         l *= sc;
         m_run = m_new;
-        // The pair's first fifteen survivors, straight from the registers; the
-        // upper seven only when some segment of the wave reaches them (one
+        // The pair's first DIRECT survivors, straight from the registers (past
+        // the eighth only when some segment of the wave reaches them: one
         // wave-uniform branch).
-        u32x4 vv[kRecHead];
-        auto issue = [&](int k) {
+        u32x4 vv[DIRECT];
+        constexpr int K8 = DIRECT < 8 ? DIRECT : 8;
+#pragma unroll
+        for (int k = 0; k < K8; ++k)
             if (k < n) vv[k] = ld16(Vb + (int64_t)(int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4] * D);
-        };
-        auto take = [&](int k) {
+        if (DIRECT > 8 && nmax > 8) {
+#pragma unroll
+            for (int k = K8; k < DIRECT; ++k)
+                if (k < n) vv[k] = ld16(Vb + (int64_t)(int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4] * D);
+        }
+#pragma unroll
+        for (int k = 0; k < K8; ++k)
             if (k < n) add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
-        };
+        if (DIRECT > 8 && nmax > 8) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) issue(k);
-        if (nmax > 8) {
-#pragma unroll
-            for (int k = 8; k < kRecHead; ++k) issue(k);
+            for (int k = K8; k < DIRECT; ++k)
+                if (k < n) add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) take(k);
-        if (nmax > 8) {
-#pragma unroll
-            for (int k = 8; k < kRecHead; ++k) take(k);
-        }
-        if (nmax <= kRecHead) continue;  // wave-uniform: no tails
-        // Tails of the long segments: entry k >= 15 of the pair's segment goes
-        // to list slot ex + k - 15.
-        const int nt = h == 0 ? max(0, n - kRecHead) : 0;
+        if (nmax <= DIRECT) continue;  // wave-uniform: no tails
+        // Tails of the longer segments: entry k >= DIRECT of the pair's segment
+        // goes to list slot ex + k - DIRECT.
+        const int nt = h == 0 ? max(0, n - DIRECT) : 0;
         const int incl = wave_incl_scan(nt);
         const int tot = __builtin_amdgcn_readlane(incl, 63);
         const int ex = incl - nt;
@@ -506,10 +519,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             for (uint64_t bm = big; bm != 0ull; bm &= bm - 1ull) {
                 const int src = __ffsll((unsigned long long)bm) - 1;
                 const int sn = __builtin_amdgcn_readlane(n, src);
-                const int sx = __builtin_amdgcn_readlane(ex, src) - kRecHead;  // slot of entry k: sx + k
+                const int sx = __builtin_amdgcn_readlane(ex, src) - DIRECT;  // slot of entry k: sx + k
                 const int ssg = __builtin_amdgcn_readlane(sg, src);
                 const int2 *pr = (const int2 *)(rb + (int64_t)ssg * a.seg_w) + 1;
-                const int k0 = max(kRecHead, w0 - sx), k1 = min(sn, w1 - sx);
+                const int k0 = max(DIRECT, w0 - sx), k1 = min(sn, w1 - sx);
                 for (int k = k0 + lane; k < k1; k += kWave) {
                     const int2 v = pr[k];
                     lt[sx + k - w0] = v.x;

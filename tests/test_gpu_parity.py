@@ -73,6 +73,8 @@ SMALL = [
     (3, 4, 2, 3, 128, 17, 5, 2, 3, 2),         # l_kv shorter than one tile
     (1, 4, 2, 2, 64, 1, 1, 1, 2, 0),           # a single cache position
     (1, 32768, 512, 1024, 64, 40, 6, 2, 2, 0),  # the largest head count, groups of 64
+    (4, 32, 4, 16, 64, 2000, 600, 2, 3, 16),   # many rows, few long segments (attend spreads them)
+    (1, 8, 2, 4, 128, 1200, 900, 2, 3, 8),     # d = 128, few rows, long segments
 ]
 
 
