@@ -2,6 +2,7 @@
 // MI355X (gfx950).  Validates arguments, lays out the caller's workspace,
 // and enqueues the kernels of saga_kernels.hpp on the caller's stream.
 // Declarations and the contract of every entry point: include/saga.h.
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -210,20 +211,25 @@ bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 int launch_status() { return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
 
 // Compute units of the current device (cached per device; 256 on MI355X).
+// Callers on several host threads may fill the cache at once; they store
+// the same value.
 int device_cus() {
-    static int cus[64];
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int n = 0;
-        cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
-                       ? n : 256;
+        c = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                ? n : 256;
+        cus[dev].store(c, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return c;
 }
 
 template <int D>
 void launch_attend(const AttendArgs &aa, int64_t grid, bool direct15, bool spread, hipStream_t s) {
+    // direct15: all fifteen head survivors in flight (one block per CU); else eight at a time
     const dim3 g((unsigned)grid), t(kAttendThreads);
     if (direct15) {
         if (spread) hipLaunchKernelGGL((k_attend<D, 15, true>), g, t, 0, s, aa);
