@@ -40,6 +40,7 @@ struct Plan {
     int B, h_q, h_k, h_v, d;
     int64_t l_kv, N;
     int rows, gmax, nt;
+    int u;  // k_select tiles per wave iteration (a record group is 16 u rows)
     int64_t chunk_len;
     int n_chunk, n_sub;
     int64_t sub_cap;
@@ -66,13 +67,27 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
     return SAGA_OK;
 }
 
+// Chunk granularity of the short-cache plan: one 16-row tile per wave
+// iteration of the 4 waves.
+constexpr int64_t kShortUnit = kWaves * 16;
+
+// Short cache: chunks of the streaming unit would give fewer than
+// kTargetSelectBlocks blocks, so the select pass takes one tile per wave
+// iteration and 64-row chunk units instead (monotone in l_kv: the short
+// plan's chunks are never longer than 256 rows, the streaming plan's never
+// shorter).
+bool short_plan(int64_t pairs, int64_t l_kv) {
+    return pairs * ceil_div(l_kv, kChunkUnit) < kTargetSelectBlocks;
+}
+
 // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
 // pairs, and at most kMaxSub/kWaves chunks per row (non-decreasing in l_kv).
 int64_t chunk_len_for(int64_t pairs, int64_t l_kv) {
-    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), kChunkUnit) * kChunkUnit;
-    const int64_t cl_min = ceil_div(ceil_div(l_kv, kMaxSub / kWaves), kChunkUnit) * kChunkUnit;
+    const int64_t unit = short_plan(pairs, l_kv) ? kShortUnit : kChunkUnit;
+    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetSelectBlocks), unit) * unit;
+    const int64_t cl_min = ceil_div(ceil_div(l_kv, kMaxSub / kWaves), unit) * unit;
     if (cl < cl_min) cl = cl_min;
-    if (cl < kChunkUnit) cl = kChunkUnit;
+    if (cl < unit) cl = unit;
     return cl;
 }
 
@@ -97,7 +112,8 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->n_sub = p->n_chunk * kWaves;
     p->sub_cap = cl / kWaves;
-    p->grp = 1024 * SAGA_SELECT_U / d;
+    p->u = short_plan(pairs, l_kv) ? 1 : (d == 64 ? select_tiles<64>() : select_tiles<128>());
+    p->grp = 16 * p->u;
     p->ld_a = ceil_div(l_kv, 64) * 64;
     p->hist_bpr = (int)ceil_div(l_kv, kHistBlock);
 
@@ -241,21 +257,24 @@ void launch_attend(const AttendArgs &aa, int64_t grid, bool direct15, bool sprea
 }
 
 template <int D, int NT, bool MAT>
-void launch_select_t(const SelectArgs &a, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((k_select<D, NT, MAT>), dim3(blocks), dim3(kThreads), 0, s, a);
+void launch_select_t(const SelectArgs &a, int u, int blocks, hipStream_t s) {
+    if (u == 1)
+        hipLaunchKernelGGL((k_select<D, NT, MAT, 1>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_select<D, NT, MAT, select_tiles<D>()>), dim3(blocks), dim3(kThreads), 0, s, a);
 }
 
 template <bool MAT>
 void launch_select(const Plan &p, const SelectArgs &a, hipStream_t s) {
     const int blocks = p.B * p.h_k * p.n_chunk;
     if (p.d == 64) {
-        if (p.nt == 1) launch_select_t<64, 1, MAT>(a, blocks, s);
-        else if (p.nt == 2) launch_select_t<64, 2, MAT>(a, blocks, s);
-        else launch_select_t<64, 4, MAT>(a, blocks, s);
+        if (p.nt == 1) launch_select_t<64, 1, MAT>(a, p.u, blocks, s);
+        else if (p.nt == 2) launch_select_t<64, 2, MAT>(a, p.u, blocks, s);
+        else launch_select_t<64, 4, MAT>(a, p.u, blocks, s);
     } else {
-        if (p.nt == 1) launch_select_t<128, 1, MAT>(a, blocks, s);
-        else if (p.nt == 2) launch_select_t<128, 2, MAT>(a, blocks, s);
-        else launch_select_t<128, 4, MAT>(a, blocks, s);
+        if (p.nt == 1) launch_select_t<128, 1, MAT>(a, p.u, blocks, s);
+        else if (p.nt == 2) launch_select_t<128, 2, MAT>(a, p.u, blocks, s);
+        else launch_select_t<128, 4, MAT>(a, p.u, blocks, s);
     }
 }
 

@@ -43,6 +43,10 @@ namespace saga {
 #ifndef SAGA_SELECT_U
 #define SAGA_SELECT_U 4  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
 #endif
+// k_select's tiles per wave iteration: the streaming choice, or one tile
+// where 256-row chunks would leave compute units idle (short caches).
+template <int D>
+constexpr int select_tiles() { return SAGA_SELECT_U * 64 / D; }
 #ifndef SAGA_KT_LDS
 #define SAGA_KT_LDS 1  // k_select: contiguous key loads, moved into the MFMA layout through LDS
 #endif
@@ -120,7 +124,7 @@ struct SelectArgs {
 // tile, then row, then lane), staged in LDS and flushed to the wave's
 // segment record of that head.  The record order of the positions is the
 // bijection record_order_key below.
-template <int D, int NT, bool MATERIALIZE>
+template <int D, int NT, bool MATERIALIZE, int U>
 __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     // First d-index of the 8 elements lane quarter lq supplies at MFMA
     // k-step s; the query operand uses the same map, so any permutation of
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
         return lq * (D / 4) + s * 8;     // a lane reads D/2 contiguous bytes of its row
 #endif
     };
-    constexpr int KS = D / 32;             // MFMA k-steps per row
-    constexpr int U = SAGA_SELECT_U * 64 / D;  // tiles per wave iteration
+    constexpr int KS = D / 32;             // MFMA k-steps per row (U: tiles per wave iteration)
+    static_assert(U >= 1, "tiles per wave iteration");
     constexpr int QW = D / 4;              // elements of a row per lane quarter
     constexpr int CPR = D / 8;             // 16-byte columns per cache row
     constexpr int RPL = 64 / CPR;          // rows per contiguous wave load
