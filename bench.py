@@ -30,7 +30,7 @@ METRIC = "µs per decode-attention step and achieved HBM GB/s at 128K ctx, 1 MI3
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_select_traffic_llama32-1b-128k-16L.json")
-DOMINANT = "saga::k_select<64, 1, false>"
+DOMINANT = "saga::k_select<64, 1, false, 4>"
 
 
 # The sources the decode-step kernels are built from (the key-merge sources,
