@@ -71,13 +71,14 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
 // iteration of the 4 waves.
 constexpr int64_t kShortUnit = kWaves * 16;
 
-// Short cache: chunks of the streaming unit would give fewer than
-// kTargetSelectBlocks blocks, so the select pass takes one tile per wave
-// iteration and 64-row chunk units instead (monotone in l_kv: the short
-// plan's chunks are never longer than 256 rows, the streaming plan's never
-// shorter).
+// Short cache: the streaming plan would give each wave a single iteration
+// (chunks of one 256-row unit), so the select pass takes one tile per wave
+// iteration and 64-row chunk units instead -- shorter iterations, and up to
+// kTargetSelectBlocks blocks where 256-row chunks would leave compute units
+// idle.  Monotone in l_kv: the short plan's chunks are never longer than 256
+// rows, the streaming plan's never shorter.
 bool short_plan(int64_t pairs, int64_t l_kv) {
-    return pairs * ceil_div(l_kv, kChunkUnit) < kTargetSelectBlocks;
+    return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= kChunkUnit;
 }
 
 // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
