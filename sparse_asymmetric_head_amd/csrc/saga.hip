@@ -81,6 +81,15 @@ bool short_plan(int64_t pairs, int64_t l_kv) {
     return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= kChunkUnit;
 }
 
+// k_select tiles per wave iteration: one on the short plan; two where the
+// streaming chunks would hold two four-tile iterations per wave (32K at the
+// Llama shape); else the streaming choice (4 at d 64, 2 at d 128).
+int select_u(int64_t pairs, int64_t l_kv, int d) {
+    if (short_plan(pairs, l_kv)) return 1;
+    const int u = d == 64 ? select_tiles<64>() : select_tiles<128>();
+    return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= 2 * kChunkUnit && u > 2 ? 2 : u;
+}
+
 // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
 // pairs, and at most kMaxSub/kWaves chunks per row (non-decreasing in l_kv).
 int64_t chunk_len_for(int64_t pairs, int64_t l_kv) {
@@ -113,7 +122,7 @@ int make_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N, 
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->n_sub = p->n_chunk * kWaves;
     p->sub_cap = cl / kWaves;
-    p->u = short_plan(pairs, l_kv) ? 1 : (d == 64 ? select_tiles<64>() : select_tiles<128>());
+    p->u = select_u(pairs, l_kv, d);
     p->grp = 16 * p->u;
     p->ld_a = ceil_div(l_kv, 64) * 64;
     p->hist_bpr = (int)ceil_div(l_kv, kHistBlock);
@@ -261,6 +270,8 @@ template <int D, int NT, bool MAT>
 void launch_select_t(const SelectArgs &a, int u, int blocks, hipStream_t s) {
     if (u == 1)
         hipLaunchKernelGGL((k_select<D, NT, MAT, 1>), dim3(blocks), dim3(kThreads), 0, s, a);
+    else if (u == 2)
+        hipLaunchKernelGGL((k_select<D, NT, MAT, 2>), dim3(blocks), dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((k_select<D, NT, MAT, select_tiles<D>()>), dim3(blocks), dim3(kThreads), 0, s, a);
 }

@@ -91,10 +91,12 @@ def test_workspace_layout_consistent(L, shape):
     assert lay.bytes == nbytes
     assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
     assert lay.n_seg == 4 * lay.n_chunk and lay.seg_cap * 4 == lay.chunk_len
-    # record groups: the streaming tile count (4 at d 64, 2 at d 128) of 16-row tiles, or one
-    # tile when the streaming plan's chunks would be a single 256-row unit (short caches)
-    short = -(-(B * h_k * l_kv) // 256) <= 256
-    assert lay.seg_group == (16 if short else 64 * 64 // d)
+    # record groups of 16-row tiles: one tile when the streaming plan's chunks would be a single
+    # 256-row unit (short caches), at most two when they would be two units, else the streaming
+    # tile count (4 at d 64, 2 at d 128)
+    per = -(-(B * h_k * l_kv) // 256)
+    u = 1 if per <= 256 else min(2, 4 * 64 // d) if per <= 512 else 4 * 64 // d
+    assert lay.seg_group == 16 * u
     assert lay.chunk_len % (4 * lay.seg_group) == 0
     assert lay.n_seg <= 1024
     assert lay.scores_ld >= l_kv and lay.scores_ld % 4 == 0
