@@ -207,7 +207,10 @@ typedef struct saga_ws_layout {
     int64_t n_chunk;       /* blocks per key-head row: ceil(l_kv / chunk_len) */
     int64_t n_seg;         /* segments per row (n_chunk * 4) */
     int64_t seg_cap;       /* positions covered by one segment (chunk_len / 4) */
-    int64_t seg_group;     /* rows per group of a segment (16 * 4 * 64 / d) */
+    int64_t seg_group;     /* rows per group of a segment: 16 times the select pass's
+                              tiles per wave iteration -- 16 when ceil(B*h_k*l_kv / 256)
+                              <= 256, else 32 when it is <= 512, else 16 * 4 * 64 / d
+                              (never more than 16 * 4 * 64 / d) */
 } saga_ws_layout;
 
 /* Fill *out for this shape.  Returns SAGA_OK or a negative status. */
