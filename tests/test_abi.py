@@ -268,3 +268,27 @@ def test_merge_validates_before_launch(L):
     assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
     bad = list(args); bad[8] = pin(0, 1, 2, 3, 4, 5, 6, 8)       # head 8 does not exist
     assert f(*bad) == saga.SAGA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunking_monotone_over_lengths(L, d):
+    """The select plan switches its chunk unit (64 rows with one tile per wave iteration on
+    short caches, 256 rows otherwise). A workspace sized for a cache's capacity serves every
+    shorter length only if the chunk length never decreases as the cache grows, and every
+    length must keep the record layout's invariants."""
+    from sparse_asymmetric_head_amd import saga
+
+    for B, h_k in [(1, 1), (1, 4), (4, 1), (2, 8), (16, 2), (1, 64)]:
+        h_q = h_v = 2 * h_k
+        prev = 0
+        for l_kv in sorted({int(1.19 ** i) for i in range(1, 90)} | {16384, 16385, 32768, 65536}):
+            if l_kv * d * 2 >= 1 << 31:
+                break
+            lay = saga.saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, 1)
+            assert lay.chunk_len >= prev, (B, h_k, l_kv)
+            prev = lay.chunk_len
+            assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
+            assert lay.n_seg == 4 * lay.n_chunk <= 1024
+            assert lay.seg_group in (16, 32, 64 * 64 // d) and lay.seg_group <= 64 * 64 // d
+            assert lay.chunk_len % (4 * lay.seg_group) == 0
+            assert lay.seg_cap * 4 == lay.chunk_len
