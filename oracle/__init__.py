@@ -13,7 +13,8 @@ Source of every definition: "More Value per Key: Asymmetric Sparse Attention
 for Faster LLM Decoding" (picx.dev summary): eqs. 2-4 (scores, softmax, PV),
 eq. 6 (top-N indices), Methodology > Atop-N Attention items 1-2 and eq. 7
 (threshold compare, periodic exact refresh, sparse softmax-PV), SAGA
-Architecture (separate key and value head counts).
+Architecture (separate key and value head counts); the growing cache of the
+decode loop from Introduction > Background (cached keys and values reused).
 """
 from __future__ import annotations
 
@@ -60,6 +61,10 @@ def load(path: str | None = None):
     lib.sao_trajectory.argtypes = [_u16p, _u16p, _u16p, i32, i32, i32, i32, i32, i32, i64, i64,
                                    i32, _f64p, _f64p, _i64p, ctypes.c_void_p]
     lib.sao_trajectory.restype = i32
+    lib.sao_trajectory_growing.argtypes = [_u16p, _u16p, _u16p, i32, i32, i32, i32, i32, i32,
+                                           i64, i64, i64, i32, _f64p, _f64p, _i64p,
+                                           ctypes.c_void_p]
+    lib.sao_trajectory_growing.restype = i32
     lib.sao_given_mask.argtypes = [_u16p, _u16p, _u16p, i32, i32, i32, i32, i32, i64, _u8p,
                                    _f64p, _i64p]
     lib.sao_given_mask.restype = i32
@@ -158,6 +163,30 @@ def trajectory(Q, K, V, h_k: int, h_v: int, N: int, R: int, want_mask: bool = Fa
                             mask.ctypes.data if mask is not None else None)
     if rc != 0:
         raise ValueError("oracle trajectory rejected its arguments")
+    return {"O": O, "tau": tau, "count": cnt, "mask": mask}
+
+
+def trajectory_growing(Q, K, V, h_k: int, h_v: int, l0: int, N: int, R: int,
+                       want_mask: bool = False, lib=None):
+    """Run T Atop-N decode steps over a growing cache: step t appends the row
+    at position l0 + t and attends over the first l0 + t + 1 rows.
+
+    Q: [T][B][h_q][d]; K: [B][h_k][cap][d], V: [B][h_v][cap][d] (bf16 bits),
+    rows 0 .. l0 + T - 1 used.  Returns dict(O, tau, count, mask [T][B][h_q][cap]
+    or None) as trajectory()."""
+    lib = lib or load()
+    Q, K, V = _u16(Q), _u16(K), _u16(V)
+    T, B, h_q, d = Q.shape
+    cap = K.shape[2]
+    assert K.shape == (B, h_k, cap, d) and V.shape == (B, h_v, cap, d)
+    O = np.empty((T, B, h_q, d), np.float64)
+    tau = np.empty((T, B, h_q), np.float64)
+    cnt = np.empty((T, B, h_q), np.int64)
+    mask = np.empty((T, B, h_q, cap), np.uint8) if want_mask else None
+    rc = lib.sao_trajectory_growing(Q, K, V, T, B, h_q, h_k, h_v, d, cap, int(l0), int(N), int(R),
+                                    O, tau, cnt, mask.ctypes.data if mask is not None else None)
+    if rc != 0:
+        raise ValueError("oracle growing trajectory rejected its arguments")
     return {"O": O, "tau": tau, "count": cnt, "mask": mask}
 
 

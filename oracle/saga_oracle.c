@@ -228,6 +228,72 @@ int sao_trajectory(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int 
 }
 
 /*
+ * A whole Atop-N decode trajectory over a GROWING cache: the decode loop's
+ * key/value cache (Introduction > Background: keys and values of earlier
+ * tokens are cached and reused) receives the current token's key and value
+ * rows before the step attends, so step t attends over the first
+ *     len_t = l0 + t + 1
+ * cache rows, the newest being the current token's.  The threshold follows
+ * Atop-N items 1-2 exactly as in sao_trajectory: at t mod R == 0 it is the
+ * exact N-th largest of this step's len_t scores; at every other step the
+ * threshold of the last refresh is reused, and the rows appended since then
+ * (the new keys) are compared with it like every other position.
+ *   Q    [T][B][h_q][d]          bf16 query of every step
+ *   K    [B][h_k][cap][d], V [B][h_v][cap][d]  bf16; rows 0 .. l0+T-1 used
+ *   O    [T][B][h_q][d]          out, double
+ *   tau  [T][B][h_q]             out, the threshold in force at each step
+ *   count[T][B][h_q]             out, |S|
+ *   mask [T][B][h_q][cap]        out, nullable; positions >= len_t are 0
+ * Requires 0 <= l0, l0 + T <= cap and N <= l0 + 1 (the first step's length).
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int sao_trajectory_growing(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int T, int B,
+                           int h_q, int h_k, int h_v, int d, int64_t cap, int64_t l0, int64_t N,
+                           int R, double *O, double *tau, int64_t *count, uint8_t *mask_out)
+{
+    if (T < 1 || B < 1 || h_q < 1 || h_k < 1 || h_v < 1 || h_k > h_q || h_v > h_q || d < 1 ||
+        cap < 1 || l0 < 0 || l0 + T > cap || N < 1 || N > l0 + 1 || R < 1)
+        return -1;
+    int rows = B * h_q;
+    double *tau_cur = (double *)malloc((size_t)rows * sizeof *tau_cur);
+    if (!tau_cur) return -1;
+    int fail = 0;
+    for (int t = 0; t < T; ++t) {
+        const int64_t len = l0 + t + 1; /* the token of step t sits at row l0 + t */
+        const int refresh_step = t % R == 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+        for (int r = 0; r < rows; ++r) {
+            int b = r / h_q, j = r % h_q;
+            int g = key_head_of(j, h_q, h_k), v = value_head_of(j, h_q, h_v);
+            double *a = (double *)malloc((size_t)len * sizeof *a);
+            uint8_t *mk = (uint8_t *)malloc((size_t)len);
+            if (!a || !mk) {
+                free(a);
+                free(mk);
+                fail |= 1;
+                continue;
+            }
+            const uint16_t *q = Q + (((int64_t)t * B + b) * h_q + j) * d;
+            sao_scores_row(q, K + ((int64_t)b * h_k + g) * cap * d, d, len, a);
+            if (refresh_step) tau_cur[r] = sao_nth_largest(a, len, N);
+            int64_t idx = (int64_t)t * rows + r;
+            tau[idx] = tau_cur[r];
+            sao_select_row(a, len, tau_cur[r], mk);
+            count[idx] = sao_attend_row(a, mk, V + ((int64_t)b * h_v + v) * cap * d, d, len,
+                                        O + idx * d);
+            if (mask_out) {
+                memset(mask_out + idx * cap, 0, (size_t)cap);
+                memcpy(mask_out + idx * cap, mk, (size_t)len);
+            }
+            free(a);
+            free(mk);
+        }
+    }
+    free(tau_cur);
+    return fail ? -1 : 0;
+}
+
+/*
  * One decode step with a selection supplied from outside ("given-mask"
  * mode): O = softmax(A[S]) V[S] with S = mask, eq. 7.  Lets an output be
  * checked independently of which entries sit right at the threshold.

@@ -296,6 +296,102 @@ def pin_brute_force_tiny(lib, seed=9):
         np.testing.assert_allclose(tr["O"][0, 0, 0], want, rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- growing cache
+# The decode loop appends each token's key and value rows to the cache before
+# the step attends (Introduction > Background: cached keys and values are
+# reused); the threshold of the last refresh is reused for every position,
+# the new ones included (Atop-N item 2).
+
+
+def growing_case(rng, B, h_q, h_k, h_v, d, cap, T):
+    return rand_case(rng, B, h_q, h_k, h_v, d, cap, T=T)
+
+
+def pin_growing_brute_force(lib, seed=10):
+    """Brute force on tiny inputs, written from the definition in numpy: step t
+    scores the first l0 + t + 1 rows (matrix product in fp64), refreshes tau by a
+    full sort at t mod R == 0, otherwise keeps the last refresh's tau, selects
+    A >= tau and takes the softmax-weighted value rows."""
+    rng = np.random.default_rng(seed)
+    for (B, h_q, h_k, h_v, d, cap, l0, T, N, R) in [(2, 4, 2, 3, 8, 40, 20, 12, 5, 4),
+                                                   (1, 6, 3, 6, 16, 30, 4, 9, 5, 3)]:
+        Q, K, V = growing_case(rng, B, h_q, h_k, h_v, d, cap, T)
+        tr = oracle.trajectory_growing(Q, K, V, h_k, h_v, l0, N, R, want_mask=True, lib=lib)
+        Qw, Kw, Vw = widen(Q), widen(K), widen(V)
+        tau = np.zeros((B, h_q))
+        for t in range(T):
+            n = l0 + t + 1
+            for b in range(B):
+                for j in range(h_q):
+                    g, v = (j * h_k) // h_q, (j * h_v) // h_q
+                    a = Kw[b, g, :n] @ Qw[t, b, j] / math.sqrt(d)
+                    if t % R == 0:
+                        tau[b, j] = np.sort(a)[::-1][N - 1]
+                    sel = a >= tau[b, j]
+                    o = np.zeros(d)  # an empty selection gives O = 0 (the reading for S empty)
+                    if sel.any():
+                        w = np.exp(a[sel] - a[sel].max())
+                        o = (w[:, None] * Vw[b, v, :n][sel]).sum(0) / w.sum()
+                    assert abs(tr["tau"][t, b, j] - tau[b, j]) <= 1e-12 * max(1, abs(tau[b, j]))
+                    assert np.array_equal(tr["mask"][t, b, j, :n].astype(bool), sel), (t, b, j)
+                    assert not tr["mask"][t, b, j, n:].any()
+                    assert tr["count"][t, b, j] == sel.sum()
+                    np.testing.assert_allclose(tr["O"][t, b, j], o, rtol=1e-12, atol=1e-12)
+
+
+def pin_growing_new_keys_against_stale_tau(lib):
+    """Closed-form counts: with a constant query and one refresh (R > T), each
+    appended key joins S exactly when its score reaches the stale tau, so
+    count_t = N + (appended keys so far above tau), and tau never changes.  The
+    appended keys alternate between k = 4 q (far above every old score) and
+    k = -q (far below); the last hot key is made dominant (k = 8 q), so the
+    output equals its value row to within exp(-16).  (Step 0 refreshes over its
+    own prefix, which already holds the first appended key.)"""
+    rng = np.random.default_rng(11)
+    d, l0, T, N = 16, 50, 8, 4
+    cap = l0 + T
+    q = np.sign(rng.standard_normal(d))                      # +-1 entries, |q|^2 = d
+    Kf = rng.standard_normal((1, 1, cap, d)) * 0.25          # old scores |a| <~ 1
+    for t in range(T):
+        Kf[0, 0, l0 + t] = (4.0 * q if t % 2 == 0 else -q)
+    Kf[0, 0, l0 + T - 2] = 8.0 * q                           # the last hot key dominates
+    Vf = rng.standard_normal((1, 1, cap, d))
+    Qf = np.broadcast_to(q, (T, 1, 1, d)).copy()
+    tr = oracle.trajectory_growing(bf16(Qf), bf16(Kf), bf16(Vf), 1, 1, l0, N, R=T + 1,
+                                   want_mask=True, lib=lib)
+    hot = 0  # hot keys appended after the refresh at t = 0 (whose own key is among its top N)
+    for t in range(T):
+        hot += (t % 2 == 0 and t > 0)
+        assert tr["tau"][t, 0, 0] == tr["tau"][0, 0, 0]
+        assert tr["count"][t, 0, 0] == N + hot, (t, tr["count"][t, 0, 0])
+        assert tr["mask"][t, 0, 0, l0 + t] == (t % 2 == 0)
+    # scores of the two hot keys: 8d/4 = 32 and 4d/4 = 16 (exact in bf16), others <~ 1
+    np.testing.assert_allclose(tr["O"][T - 1, 0, 0], widen(bf16(Vf))[0, 0, l0 + T - 2],
+                               rtol=0, atol=1e-6)
+
+
+def pin_growing_refresh_every_step_is_topn(lib, seed=12):
+    """R = 1: every step is the exact top-N of its own prefix (numpy argsort on
+    tie-free scores), and the step equals a static trajectory over that prefix."""
+    rng = np.random.default_rng(seed)
+    B, h_q, h_k, h_v, d, cap, l0, T, N = 1, 4, 2, 2, 16, 64, 40, 10, 7
+    Q, K, V = growing_case(rng, B, h_q, h_k, h_v, d, cap, T)
+    tr = oracle.trajectory_growing(Q, K, V, h_k, h_v, l0, N, 1, want_mask=True, lib=lib)
+    Qw, Kw = widen(Q), widen(K)
+    for t in range(T):
+        n = l0 + t + 1
+        st = oracle.trajectory(Q[t:t + 1], np.ascontiguousarray(K[:, :, :n]),
+                               np.ascontiguousarray(V[:, :, :n]), h_k, h_v, N, 1, want_mask=True,
+                               lib=lib)
+        np.testing.assert_array_equal(st["mask"][0], tr["mask"][t][..., :n])
+        np.testing.assert_allclose(st["O"][0], tr["O"][t], rtol=1e-14, atol=1e-14)
+        for j in range(h_q):
+            g = (j * h_k) // h_q
+            a = Kw[0, g, :n] @ Qw[t, 0, j]
+            want = set(np.argsort(-a, kind="stable")[:N].tolist())
+            assert set(np.nonzero(tr["mask"][t, 0, j])[0].tolist()) == want, (t, j)
+
+
 ALL_PINS = [
     pin_scores_one_hot,
     pin_scores_sum_of_products,
@@ -311,4 +407,7 @@ ALL_PINS = [
     pin_empty_selection,
     pin_given_mask_consistent,
     pin_brute_force_tiny,
+    pin_growing_brute_force,
+    pin_growing_new_keys_against_stale_tau,
+    pin_growing_refresh_every_step_is_topn,
 ]

@@ -30,6 +30,19 @@ MUTATIONS = {
                         "const uint16_t *v = Vhead + ((t + 1) % l_kv) * (int64_t)d;"),
     "stale_tau_every_step": ("if (refresh) tau_cur[r] = sao_nth_largest(a, l_kv, N);",
                              "if (t == 0) tau_cur[r] = sao_nth_largest(a, l_kv, N);"),
+    # the growing-cache trajectory
+    "growing_excludes_new_key": ("const int64_t len = l0 + t + 1;",
+                                 "const int64_t len = l0 + t + (t > 0 ? 0 : 1);"),
+    "growing_key_head_stride": ("sao_scores_row(q, K + ((int64_t)b * h_k + g) * cap * d, d, len, a);",
+                                "sao_scores_row(q, K + ((int64_t)b * h_k + g) * len * d, d, len, a);"),
+    "growing_value_head_stride": ("count[idx] = sao_attend_row(a, mk, V + ((int64_t)b * h_v + v) * cap * d, d, len,",
+                                  "count[idx] = sao_attend_row(a, mk, V + ((int64_t)b * h_v + v) * len * d, d, len,"),
+    "growing_refresh_phase": ("const int refresh_step = t % R == 0;",
+                              "const int refresh_step = t % R == R - 1 || t == 0;"),
+    "growing_never_refreshes": ("if (refresh_step) tau_cur[r] = sao_nth_largest(a, len, N);",
+                                "if (t == 0) tau_cur[r] = sao_nth_largest(a, len, N);"),
+    "growing_refresh_over_old_rows": ("if (refresh_step) tau_cur[r] = sao_nth_largest(a, len, N);",
+                                      "if (refresh_step) tau_cur[r] = sao_nth_largest(a, l0 + 1, N);"),
 }
 
 
