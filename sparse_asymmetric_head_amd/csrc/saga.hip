@@ -306,6 +306,8 @@ SelectArgs select_args(const Plan &p, const void *Q, const void *K, const float 
     a.n_sub = p.n_sub;
     a.sub_cap = p.sub_cap;
     a.seg_w = p.seg_w;
+    a.hist = (uint32_t *)(ws + p.off_hist);
+    a.state = (uint32_t *)(ws + p.off_state);
     return a;
 }
 
@@ -337,6 +339,7 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.seg = (const int32_t *)(ws + p.off_seg);
     aa.n_sub = p.n_sub;
     aa.seg_w = p.seg_w;
+    aa.sub_cap = (int)p.sub_cap;
     aa.V = (const uint16_t *)V;
     aa.B = p.B, aa.h_q = p.h_q, aa.h_v = p.h_v;
     aa.l_kv = p.l_kv;

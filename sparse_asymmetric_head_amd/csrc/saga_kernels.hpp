@@ -106,6 +106,8 @@ struct SelectArgs {
     int32_t *seg;        // [rows][n_sub][seg_w] records
     int n_sub;
     int64_t sub_cap, seg_w;
+    uint32_t *hist;      // [rows][kHistBins] radix histograms (materialize mode: cleared here)
+    uint32_t *state;     // [rows][4] radix state                (materialize mode: cleared here)
 };
 
 // One workgroup = (batch b, key head g, chunk of cache positions).  Each wave
@@ -153,6 +155,19 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     const int j_lo = group_lo(g, a.h_q, a.h_k), j_hi = group_lo(g + 1, a.h_q, a.h_k);
     const int64_t t_begin = (int64_t)chunk * a.chunk_len;
     const int64_t t_end = min(a.l_kv, t_begin + a.chunk_len);
+    if constexpr (MATERIALIZE) {
+        // The radix select that follows needs zeroed histograms and state for
+        // this group's rows (contiguous: rows b*h_q + j_lo .. j_hi); the
+        // group's blocks clear them between them, so no earlier call has to
+        // leave them at zero.
+        const int64_t r0 = (int64_t)b * a.h_q + j_lo, nr = j_hi - j_lo;
+        uint32_t *hz = a.hist + r0 * kHistBins, *sz = a.state + r0 * 4;
+        for (int64_t i = (int64_t)chunk * kThreads + threadIdx.x; i < nr * (kHistBins + 4);
+             i += (int64_t)a.n_chunk * kThreads) {
+            if (i < nr * kHistBins) hz[i] = 0u;
+            else sz[i - nr * kHistBins] = 0u;
+        }
+    }
 
     bf16x8 qop[NT][KS];
     float tau_l[NT];
@@ -356,6 +371,7 @@ struct AttendArgs {
     const int32_t *seg;  // [rows][n_sub][seg_w] records
     int n_sub;
     int64_t seg_w;
+    int sub_cap;         // positions per segment: a record never lists more
     const uint16_t *V;   // bf16 [B][h_v][ld_kv][D], rows < l_kv valid
     int B, h_q, h_v;
     int64_t l_kv, ld_kv;
@@ -453,6 +469,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + csl * kAttendCols + h * 8;
     int *lt = wlt[wave];
     float *ls = wls[wave];
+    const uint32_t lkv_last = (uint32_t)(a.l_kv - 1);  // positions are unsigned-compared with it
 
     float acc[8];
 #pragma unroll
@@ -478,7 +495,10 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
             hd[q] = h ? oth : own[q];
             hd[4 + q] = h ? own[q] : oth;
         }
-        const int n = (int)hd[0][0];
+        // A record holds at most sub_cap survivors, all inside the cache; a
+        // workspace whose last select was for another shape may hold anything,
+        // so the count is clamped and positions outside [0, l_kv) are skipped.
+        const int n = min(max((int)hd[0][0], 0), a.sub_cap);
         const int nmax = (int)wave_max_u32_dpp((uint32_t)n);  // the wave's longest segment
         if (nmax == 0) continue;  // wave-uniform
         const uint32_t mk = wave_max_u32_dpp(n > 0 ? hd[0][1] : 0u);
@@ -494,21 +514,28 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         // wave-uniform branch).
         u32x4 vv[DIRECT];
         constexpr int K8 = DIRECT < 8 ? DIRECT : 8;
+        // position of head entry k, clamped into the cache for the load; an
+        // entry outside it is loaded from the last row and given no weight
+        auto tpos = [&](int k) { return hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4]; };
+        auto tload = [&](int k) { return (int64_t)min(tpos(k), lkv_last) * D; };
+        auto inside = [&](int k) { return tpos(k) <= lkv_last; };
 #pragma unroll
         for (int k = 0; k < K8; ++k)
-            if (k < n) vv[k] = ld16(Vb + (int64_t)(int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4] * D);
+            if (k < n) vv[k] = ld16(Vb + tload(k));
         if (DIRECT > 8 && nmax > 8) {
 #pragma unroll
             for (int k = K8; k < DIRECT; ++k)
-                if (k < n) vv[k] = ld16(Vb + (int64_t)(int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4] * D);
+                if (k < n) vv[k] = ld16(Vb + tload(k));
         }
 #pragma unroll
         for (int k = 0; k < K8; ++k)
-            if (k < n) add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
+            if (k < n && inside(k))
+                add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
         if (DIRECT > 8 && nmax > 8) {
 #pragma unroll
             for (int k = K8; k < DIRECT; ++k)
-                if (k < n) add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
+                if (k < n && inside(k))
+                    add(vv[k], expf(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]) - m_run));
         }
         if (nmax <= DIRECT) continue;  // wave-uniform: no tails
         // Tails of the longer segments: entry k >= DIRECT of the pair's segment
@@ -547,10 +574,11 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
                 }
 #pragma unroll
                 for (int u = 0; u < UN; ++u)
-                    vt[u] = tt[u] >= 0 ? ld16(Vb + (int64_t)tt[u] * D) : u32x4{0u, 0u, 0u, 0u};
+                    vt[u] = (uint32_t)tt[u] <= lkv_last ? ld16(Vb + (int64_t)tt[u] * D)
+                                                        : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                 for (int u = 0; u < UN; ++u)
-                    if (tt[u] >= 0) add(vt[u], expf(pp[u] - m_run));
+                    if ((uint32_t)tt[u] <= lkv_last) add(vt[u], expf(pp[u] - m_run));
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // list reused by the next window
         }
@@ -610,8 +638,8 @@ struct RadixArgs {
     int rows;
     int bpr;          // blocks per row for the histogram/collect passes
     int64_t blk_len;  // positions per block
-    uint32_t *hist;   // [rows][2048] (zero on entry, zero on exit)
-    uint32_t *state;  // [rows][4]: prefix, rank within bucket, bucket size, fill counter
+    uint32_t *hist;   // [rows][2048] (cleared by the materialising score pass)
+    uint32_t *state;  // [rows][4]: prefix, rank within bucket, bucket size, fill counter (cleared alike)
     uint32_t *cand;   // [rows][l_kv]
     float *tau;       // [rows]
 };
@@ -688,10 +716,8 @@ __global__ __launch_bounds__(kThreads) void k_select1(RadixArgs a) {
     __shared__ uint32_t above;
     const int row = blockIdx.x;
     uint32_t *hg = a.hist + (int64_t)row * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) {
-        h[i] = hg[i];
-        hg[i] = 0u;  // leave the histogram cleared for the next refresh
-    }
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = hg[i];
+    if (threadIdx.x == 0) sel_bin = 0, above = 0u;  // (rank N always falls in a bin)
     __syncthreads();
     find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
     if (threadIdx.x == 0) {
@@ -733,8 +759,12 @@ __global__ __launch_bounds__(kThreads) void k_collect(RadixArgs a) {
     __syncthreads();
     if (threadIdx.x == 0) base = nk ? atomicAdd(fill, nk) : 0u;
     __syncthreads();
+    // the row's bucket never holds more than l_kv keys; the clamp only keeps
+    // a corrupted fill counter inside the row
+    const uint32_t room = base < (uint64_t)a.l_kv ? (uint32_t)(a.l_kv - base) : 0u;
+    const uint32_t nw = nk < room ? nk : room;
     uint32_t *cr = a.cand + (int64_t)row * a.l_kv + base;
-    for (uint32_t i = threadIdx.x; i < nk; i += kThreads) cr[i] = keys[i];
+    for (uint32_t i = threadIdx.x; i < nw; i += kThreads) cr[i] = keys[i];
 }
 
 // Finish the select on the bucket's keys: digits 20..10 then 9..0.
@@ -745,10 +775,12 @@ __global__ __launch_bounds__(kThreads) void k_select_final(RadixArgs a) {
     __shared__ uint32_t above;
     const int row = blockIdx.x;
     uint32_t *st = a.state + (int64_t)row * 4;
-    const uint32_t prefix = st[0], k = st[1], n = st[2];
+    const uint32_t prefix = st[0], k = st[1];
+    const uint32_t n = st[2] < (uint64_t)a.l_kv ? st[2] : (uint32_t)a.l_kv;  // (never more)
     const uint32_t *cr = a.cand + (int64_t)row * a.l_kv;
 
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
+    if (threadIdx.x == 0) sel_bin = 0, above = 0u;
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < n; i += kThreads) atomicAdd(&h[(cr[i] >> 10) & 2047u], 1u);
     __syncthreads();
@@ -766,7 +798,6 @@ __global__ __launch_bounds__(kThreads) void k_select_final(RadixArgs a) {
     if (threadIdx.x == 0) {
         const uint32_t key = (prefix << 21) | (d1 << 10) | (uint32_t)sel_bin;
         a.tau[row] = fkey_inv(key);
-        st[3] = 0u;  // fill counter back to zero
     }
 }
 

@@ -187,11 +187,35 @@ def _dims(Q, K, V=None):
     return B, h_q, d
 
 
+def _arr(t, dtype, shape, name, optional=False):
+    """Check a per-row tensor the library reads or writes (tau, O, counts, pivot):
+    the C ABI trusts its size, so a short or mistyped buffer is refused here."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _ws(ws):
+    if ws is None:
+        raise ValueError("a workspace is required (alloc_workspace)")
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise TypeError("the workspace must be a contiguous 1-D uint8 device tensor")
+
+
 # ----------------------------------------------------------------- entry points
 
 def saga_refresh_threshold(Q, K, N: int, tau, ws, stream=None) -> None:
     B, h_q, d = _dims(Q, K)
     h_k, l_kv = K.shape[1], K.shape[2]
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _ws(ws)
     _check(lib().saga_refresh_threshold(_ptr(Q), _ptr(K), B, h_q, h_k, d, l_kv, int(N),
                                         _ptr(tau), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_refresh_threshold")
@@ -201,8 +225,10 @@ def saga_decode_step(Q, K, V, N: int, tau, refresh: bool, O, counts=None, ws=Non
                      stream=None) -> None:
     B, h_q, d = _dims(Q, K, V)
     h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
-    if ws is None:
-        raise ValueError("a workspace is required (alloc_workspace)")
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _arr(counts, torch.int32, (B, h_q), "counts", optional=True)
+    _ws(ws)
     _check(lib().saga_decode_step(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv, int(N),
                                   _ptr(tau), 1 if refresh else 0, _ptr(O), _ptr(counts),
                                   _ptr(ws), ws.numel(), _stream(stream)),
@@ -215,8 +241,11 @@ def saga_decode_step_pivot(Q, K, V, N: int, tau, pivot, refresh: int, O, counts=
     refresh from the pivot; pivot is an int32 [B][h_q][N] tensor."""
     B, h_q, d = _dims(Q, K, V)
     h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
-    if ws is None:
-        raise ValueError("a workspace is required (alloc_workspace)")
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _arr(pivot, torch.int32, (B, h_q, int(N)), "pivot", optional=int(refresh) == 0)
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _arr(counts, torch.int32, (B, h_q), "counts", optional=True)
+    _ws(ws)
     _check(lib().saga_decode_step_pivot(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
                                         int(N), _ptr(tau), _ptr(pivot), int(refresh), _ptr(O),
                                         _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
@@ -226,6 +255,8 @@ def saga_decode_step_pivot(Q, K, V, N: int, tau, pivot, refresh: int, O, counts=
 def saga_select(Q, K, h_v: int, N: int, tau, refresh: bool, ws, stream=None) -> None:
     B, h_q, d = _dims(Q, K)
     h_k, l_kv = K.shape[1], K.shape[2]
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _ws(ws)
     _check(lib().saga_select(_ptr(Q), _ptr(K), B, h_q, h_k, int(h_v), d, l_kv, int(N), _ptr(tau),
                              1 if refresh else 0, _ptr(ws), ws.numel(), _stream(stream)),
            "saga_select")
@@ -235,6 +266,9 @@ def saga_attend(V, B: int, h_q: int, h_k: int, N: int, O, counts, ws, stream=Non
     if V.dtype != torch.bfloat16 or V.dim() != 4 or not V.is_contiguous():
         raise TypeError("V must be contiguous bfloat16 [B][h_v][l_kv][d]")
     h_v, l_kv, d = V.shape[1], V.shape[2], V.shape[3]
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _arr(counts, torch.int32, (B, h_q), "counts", optional=True)
+    _ws(ws)
     _check(lib().saga_attend(_ptr(V), int(B), int(h_q), int(h_k), h_v, d, l_kv, int(N), _ptr(O),
                              _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_attend")
@@ -243,12 +277,17 @@ def saga_attend(V, B: int, h_q: int, h_k: int, N: int, O, counts, ws, stream=Non
 def saga_dense_gqa_baseline(Q, K, V, O, ws, stream=None) -> None:
     B, h_q, d = _dims(Q, K, V)
     h_kv, l_kv = K.shape[1], K.shape[2]
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _ws(ws)
     _check(lib().saga_dense_gqa_baseline(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_kv, d, l_kv,
                                          _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_dense_gqa_baseline")
 
 
 def saga_selection_mask(ws, B, h_q, h_k, h_v, d, l_kv, N, mask, stream=None) -> None:
+    _ws(ws)
+    if mask.dtype != torch.uint8 or mask.numel() < B * h_q * l_kv or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8 tensor of B*h_q*l_kv bytes")
     _check(lib().saga_selection_mask(_ptr(ws), ws.numel(), B, h_q, h_k, h_v, d, l_kv, int(N),
                                      _ptr(mask), _stream(stream)),
            "saga_selection_mask")
@@ -263,6 +302,8 @@ def saga_full_attention(Q, K, V, O, ws, stream=None) -> None:
     head floor(j*h_v/h_q); Q [B][h_q][d], K [B][h_k][l_kv][d], V [B][h_v][l_kv][d]."""
     B, h_q, d = _dims(Q, K, V)
     h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _ws(ws)
     _check(lib().saga_full_attention(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
                                      _ptr(O), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_full_attention")
@@ -279,6 +320,10 @@ def saga_append_kv(K, V, k_new, v_new, pos: int, stream=None) -> None:
     for t in (K, V, k_new, v_new):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise TypeError("caches and new rows must be contiguous bfloat16")
+    if tuple(V.shape) != (B, h_v, cap, d) or tuple(k_new.shape) != (B, h_k, d) or \
+            tuple(v_new.shape) != (B, h_v, d):
+        raise ValueError("k_new must be [B][h_k][d] and v_new [B][h_v][d] for caches "
+                         "[B][h][cap][d]")
     _check(lib().saga_append_kv(_ptr(K), _ptr(V), _ptr(k_new), _ptr(v_new), B, h_k, h_v, d, cap,
                                 int(pos), _stream(stream)), "saga_append_kv")
 
@@ -289,8 +334,11 @@ def saga_decode_step_cache(Q, K, V, length: int, N: int, tau, pivot, refresh: in
     K.shape[2] rows per head."""
     B, h_q, d = _dims(Q, K, V)
     h_k, cap, h_v = K.shape[1], K.shape[2], V.shape[1]
-    if ws is None:
-        raise ValueError("a workspace is required (alloc_workspace)")
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _arr(pivot, torch.int32, (B, h_q, int(N)), "pivot", optional=int(refresh) == 0)
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _arr(counts, torch.int32, (B, h_q), "counts", optional=True)
+    _ws(ws)
     _check(lib().saga_decode_step_cache(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, cap,
                                         int(length), int(N), _ptr(tau), _ptr(pivot), int(refresh),
                                         _ptr(O), _ptr(counts), _ptr(ws), ws.numel(),
