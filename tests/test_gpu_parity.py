@@ -572,20 +572,29 @@ CACHE_CASES = [
     (1, 8, 2, 4, 64, 5000, 12, 64, 4),
     (1, 8, 2, 4, 64, 32760, 12, 128, 3),   # the chunking changes at 32768 positions
     (2, 12, 1, 4, 128, 3001, 9, 50, 4),
+    (1, 32, 4, 16, 64, 32762, 10, 256, 4),  # Llama shape across the 32K select-plan change
 ]
 
 
 @pytest.mark.parametrize("case", CACHE_CASES, ids=[str(c) for c in CACHE_CASES])
-def test_growing_context_matches_contiguous(case):
-    """KV append + decode over a growing prefix of caches with spare room: each
-    step equals the contiguous path on a copy of the prefix (tau, counts and O
-    bit for bit; the cache path refreshes from the pivot), so the new key is
-    compared with the stale tau like every other position."""
+def test_growing_context_matches_oracle(case):
+    """KV append + decode over a growing prefix of caches with spare room, every
+    step against the oracle's growing-cache trajectory (step t appends row
+    l0 + t and attends over l0 + t + 1 rows; the new key meets the stale tau):
+    on refresh steps tau bit-identical to a CPU sort of the GPU's fp32 scores
+    of the prefix, selections within the band, counts exact, outputs within
+    2e-3 of the oracle on the GPU's selection and of its own trajectory where
+    the selections agree.  Each step also equals the contiguous path on a copy
+    of the prefix bit for bit (the cache path refreshes from the pivot)."""
     B, h_q, h_k, h_v, d, l0, T, N, R = case
     cap = l0 + T
+    print(f"[parity] growing B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l0={l0} T={T} N={N} R={R}",
+          flush=True)
     x = wl.make_random(B, h_q, h_k, h_v, d, cap, seed=cap % 1013, device="cuda", steps=T,
                        planted=16)
     Kf, Vf, Q = x["K"], x["V"], x["Q"]
+    Qh, Kh, Vh = bits(Q), bits(Kf), bits(Vf)
+    ref_tr = oracle.trajectory_growing(Qh, Kh, Vh, h_k, h_v, l0, N, R, want_mask=True)
     K = torch.zeros_like(Kf)
     V = torch.zeros_like(Vf)
     K[:, :, :l0] = Kf[:, :, :l0]
@@ -609,8 +618,157 @@ def test_growing_context_matches_contiguous(case):
         assert torch.equal(tau_c.view(torch.int32), tau_r.view(torch.int32)), f"tau at step {t}"
         assert torch.equal(c_c, c_r), f"counts at step {t}"
         assert torch.equal(O_c, O_r), f"outputs at step {t}"
+        # against the oracle's growing trajectory
+        shape = (B, h_q, h_k, h_v, d, length)
+        m = read_mask(ws_c, shape, N)
+        A = oracle.scores(Qh[t], np.ascontiguousarray(Kh[:, :, :length]), h_k)
+        tc = tau_c.cpu().numpy()
+        if ref:
+            S = read_scores(ws_r, shape, N).reshape(B, h_q, length)
+            for b in range(B):
+                for j in range(h_q):
+                    check_tau_bits(S[b, j], tc[b, j], N, f"growing t={t} b={b} j={j}")
+        for b in range(B):
+            for j in range(h_q):
+                check_selection(m[b, j], A[b, j], ref_tr["tau"][t, b, j], f"growing t={t} b={b} j={j}")
+        cc = c_c.cpu().numpy()
+        assert np.array_equal(cc, m.sum(-1)), f"counts t={t}"
+        Og, cg = oracle.given_mask(Qh[t], np.ascontiguousarray(Kh[:, :, :length]),
+                                   np.ascontiguousarray(Vh[:, :, :length]), h_k, h_v, m)
+        assert np.array_equal(cg, cc)
+        Oc = O_c.cpu().numpy().astype(np.float64)
+        assert rel_err(Oc, Og) <= OUT_RTOL, f"growing output t={t}: {rel_err(Oc, Og)}"
+        agree = (m == ref_tr["mask"][t][..., :length]).all(-1)
+        if agree.any():
+            assert rel_err(Oc[agree], ref_tr["O"][t][agree]) <= OUT_RTOL
     assert torch.equal(K, Kf) and torch.equal(V, Vf)
-    m = read_mask(ws_r, (B, h_q, h_k, h_v, d, cap), N)
-    Og, cg = oracle.given_mask(bits(Q[T - 1]), bits(Kf), bits(Vf), h_k, h_v, m)
-    assert np.array_equal(cg, c_c.cpu().numpy())
-    assert rel_err(O_c.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
+
+
+# ------------------------------------------------------------------ the timed refresh path
+
+def pivot_sampled_check(cfg, layer, steps, rows):
+    """The refresh the benchmark times (saga_decode_step_pivot: an exact refresh
+    recording the pivot at step 0, refreshes from the pivot at the later
+    multiples of R, compares in between), in the benchmark's launch
+    configuration, against (a) the full refresh of saga_decode_step bit for
+    bit at every step (tau, counts, O; selections at the sampled steps) and
+    (b) the oracle at the sampled rows and steps: tau bit-identical to a CPU
+    sort of the GPU's fp32 scores, selection within the band, outputs within
+    2e-3 of the oracle on the GPU's selection."""
+    x = wl.make_layer(cfg, layer, device="cuda")
+    Q, K, V = x["Q"], x["K"], x["V"]
+    T, B, h_q, d = Q.shape
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    N, R = cfg.N, cfg.R
+    print(f"[parity] pivot {cfg.name} layer={layer} steps={steps} rows={rows}", flush=True)
+    shape = (B, h_q, h_k, h_v, d, l_kv)
+    nb = saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N)
+    ws_a, ws_b = saga.alloc_workspace(nb), saga.alloc_workspace(nb)
+    tau_a = torch.zeros(B, h_q, device="cuda")
+    tau_b = torch.zeros(B, h_q, device="cuda")
+    piv = torch.full((B, h_q, N), -1, dtype=torch.int32, device="cuda")
+    O_a = torch.empty(B, h_q, d, device="cuda")
+    O_b = torch.empty_like(O_a)
+    c_a = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+    c_b = torch.empty_like(c_a)
+    Qh = bits(Q)
+    Kr = {row: bits(K[row // h_q, ((row % h_q) * h_k) // h_q])[None, None] for row in rows}
+    Vr = {row: bits(V[row // h_q, ((row % h_q) * h_v) // h_q]) for row in rows}
+    modes = set()
+    for t in range(T):
+        ref = t % R == 0
+        mode = 0 if not ref else (1 if t == 0 else 2)
+        modes.add(mode)
+        saga.saga_decode_step(Q[t], K, V, N, tau_a, ref, O_a, c_a, ws_a)
+        saga.saga_decode_step_pivot(Q[t], K, V, N, tau_b, piv, mode, O_b, c_b, ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(tau_a.view(torch.int32), tau_b.view(torch.int32)), f"tau t={t}"
+        assert torch.equal(c_a, c_b), f"counts t={t}"
+        assert torch.equal(O_a, O_b), f"outputs t={t}"
+        if t not in steps:
+            continue
+        m_b = read_mask(ws_b, shape, N)
+        assert np.array_equal(m_b, read_mask(ws_a, shape, N)), f"selection t={t}"
+        S = read_scores(ws_a, shape, N) if ref else None
+        tb, cb = tau_b.cpu().numpy(), c_b.cpu().numpy()
+        Ob = O_b.cpu().numpy().astype(np.float64)
+        for row in rows:
+            b, j = divmod(row, h_q)
+            tr = R * (t // R)
+            a_tr = oracle.scores(Qh[tr, b, j][None, None], Kr[row], 1)[0, 0]
+            tau_ref = oracle.nth_largest(a_tr, N)
+            a_t = oracle.scores(Qh[t, b, j][None, None], Kr[row], 1)[0, 0] if t != tr else a_tr
+            if ref:
+                assert np.abs(S[row] - a_t).max() <= 1e-5 * max(1.0, np.abs(a_t).max())
+                check_tau_bits(S[row], tb[b, j], N, f"pivot {cfg.name} t={t} row={row}")
+            check_selection(m_b[b, j], a_t, tau_ref, f"pivot {cfg.name} t={t} row={row}")
+            assert cb[b, j] == m_b[b, j].sum()
+            o_ref, c_ref = oracle.attend_row(a_t, m_b[b, j], Vr[row])
+            assert c_ref == cb[b, j]
+            err = rel_err(Ob[b, j][None], o_ref[None])
+            assert err <= OUT_RTOL, f"pivot {cfg.name} t={t} row={row}: {err}"
+    assert modes == {0, 1, 2}
+    del x, Q, K, V, ws_a, ws_b
+    torch.cuda.empty_cache()
+
+
+def test_pivot_refresh_llama_128k_16_layers_sampled():
+    cfg = wl.config("llama32-1b-128k-16L")
+    for layer in (0, 7, 15):
+        pivot_sampled_check(cfg, layer, steps=[0, 16, 33, 48, 63], rows=[0, 9, 22, 31])
+
+
+def test_pivot_refresh_qwen_128k_sampled():
+    cfg = wl.config("qwen25-1.5b-128k")
+    pivot_sampled_check(cfg, 0, steps=[0, 31, 32, 63], rows=[0, 13, 30, 47])
+
+
+def test_pivot_refresh_stress_batch16_sampled():
+    cfg = wl.config("stress-b16-64k")
+    pivot_sampled_check(cfg, 0, steps=[0, 63, 64, 127],
+                        rows=[0, 3 * 32 + 17, 15 * 32 + 31, 8 * 32 + 5])
+
+
+# ------------------------------------------------------------------ workspace robustness
+
+def test_attend_on_fresh_workspace_is_empty():
+    """saga_attend on a freshly initialised workspace (every record empty) gives
+    O = 0 and counts = 0."""
+    B, h_q, h_k, h_v, d, l_kv, N = 2, 8, 2, 4, 64, 5000, 40
+    x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=3, device="cuda")
+    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
+    O = torch.full((B, h_q, d), float("nan"), device="cuda")
+    cnt = torch.full((B, h_q), -1, dtype=torch.int32, device="cuda")
+    saga.saga_attend(x["V"], B, h_q, h_k, N, O, cnt, ws)
+    torch.cuda.synchronize()
+    assert (cnt == 0).all() and (O == 0).all()
+
+
+def test_workspace_reused_for_larger_batch_refreshes_exactly():
+    """One workspace (sized for the larger shape, initialised once) serves a
+    refresh at B = 1 and then at B = 4, whose radix histograms and state sit
+    where the first call's records were: tau stays bit-identical to a CPU sort
+    of the GPU's own scores, and the selection matches the oracle."""
+    h_q, h_k, h_v, d, l_kv, N = 12, 2, 4, 128, 9000, 70
+    big = saga.saga_workspace_bytes(4, h_q, h_k, h_v, d, l_kv, N)
+    ws = saga.alloc_workspace(big)
+    for B in (1, 4, 2):
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=40 + B, device="cuda", planted=16)
+        Q, K, V = x["Q"][0], x["K"], x["V"]
+        tau = torch.zeros(B, h_q, device="cuda")
+        O = torch.empty(B, h_q, d, device="cuda")
+        cnt = torch.empty(B, h_q, dtype=torch.int32, device="cuda")
+        saga.saga_decode_step(Q, K, V, N, tau, True, O, cnt, ws)
+        torch.cuda.synchronize()
+        shape = (B, h_q, h_k, h_v, d, l_kv)
+        S = read_scores(ws, shape, N).reshape(B, h_q, l_kv)
+        m = read_mask(ws, shape, N)
+        A = oracle.scores(bits(Q), bits(K), h_k)
+        tc = tau.cpu().numpy()
+        for b in range(B):
+            for j in range(h_q):
+                check_tau_bits(S[b, j], tc[b, j], N, f"B={B} b={b} j={j}")
+                check_selection(m[b, j], A[b, j], oracle.nth_largest(A[b, j], N), f"B={B}")
+        Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
+        assert np.array_equal(cg, cnt.cpu().numpy())
+        assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
