@@ -28,9 +28,16 @@ import time
 
 METRIC = "µs per decode-attention step and achieved HBM GB/s at 128K ctx, 1 MI355X"
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache: caches larger than this stream from HBM
+ROTATE_K_BYTES = 1 << 30  # single-layer workloads rotate over >= 1 GiB of key caches
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_select_traffic_llama32-1b-128k-16L.json")
-DOMINANT = "saga::k_select<64, 1, false, 4>"
+PROFILES = os.path.join(ROOT, "profiles")
+DOMINANT = "saga::k_select"  # the streaming score/compare/compact kernel (any instantiation)
+
+
+def traffic_file(workload: str) -> str:
+    """Counter summary of one workload (name, with any size overrides)."""
+    return os.path.join(PROFILES, "traffic_" + workload.replace(" ", "_").replace("=", "") + ".json")
 
 
 # The sources the decode-step kernels are built from (the key-merge sources,
@@ -51,36 +58,54 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, out: str) -> dict:
+def _kernel_key(name: str) -> str:
+    """rocprofv3's kernel name without the return type and argument list."""
+    n = name.replace("void ", "", 1)
+    return n[:n.index("(")] if "(" in n else n
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, out: str, workload: str,
+                  shape: dict, dominant: str | None = None) -> dict:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
-    `bench.py --calibrate-copy MIB` into HBM bytes per launch of the dominant kernel,
-    each counter scaled by what it reads for the calibration copy of known size."""
+    `bench.py --calibrate-copy MIB` into HBM bytes per launch of every library kernel,
+    each counter scaled by what it reads for the calibration copy of known size.  The
+    summary names the workload and shape it was taken on and the kernel sources' hash;
+    `measured_traffic` reports it only for that same workload, shape and code."""
     import csv
     import statistics
 
     def per_kernel(path):
         vals = {}
         for r in csv.DictReader(open(path)):
-            vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(
-                float(r["Counter_Value"]))
+            vals.setdefault(_kernel_key(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         return vals
 
     known_kib = copy_mib * 1024.0
-    res = {}
+    kernels: dict = {}
+    scales = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         v = per_kernel(path)
-        copy = [x for (k, g), xs in v.items() if "copyBuffer" in k for x in xs
-                if x > 0.25 * known_kib]
-        dom = [x for (k, g), xs in v.items() if k.replace("void ", "", 1).startswith(DOMINANT)
-               for x in xs]
-        if not copy or not dom:
-            raise SystemExit(f"{path}: calibration copy or {DOMINANT} not found")
+        copy = [x for k, xs in v.items() if "copyBuffer" in k for x in xs if x > 0.25 * known_kib]
+        if not copy:
+            raise SystemExit(f"{path}: calibration copy not found")
         factor = known_kib / statistics.median(copy)
-        res[name] = {"counter_kib_per_launch": statistics.median(dom), "launches": len(dom),
-                     "copy_counter_kib": statistics.median(copy), "scale": round(factor, 4)}
-    traffic = sum(r["counter_kib_per_launch"] * r["scale"] for r in res.values()) * 1024.0
-    summary = {"kernel": DOMINANT, "workload": "llama32-1b-128k-16L",
-               "traffic_bytes_per_launch": round(traffic), "counters": res,
+        scales[name] = {"copy_counter_kib": statistics.median(copy), "scale": round(factor, 4)}
+        for k, xs in v.items():
+            if not k.startswith("saga::"):
+                continue
+            e = kernels.setdefault(k, {})
+            e[name] = {"counter_kib_per_launch": statistics.median(xs), "launches": len(xs)}
+    for k, e in kernels.items():
+        e["bytes_per_launch"] = round(sum(
+            e[c]["counter_kib_per_launch"] * scales[c]["scale"] for c in e if c in scales) * 1024.0)
+    dom = dominant or max((k for k in kernels if k.startswith(DOMINANT)),
+                          key=lambda k: kernels[k].get("FETCH_SIZE", {}).get("launches", 0),
+                          default=None)
+    if dom is None:
+        raise SystemExit(f"{fetch_csv}: no {DOMINANT} launches found")
+    summary = {"workload": workload, "shape": shape, "dominant": dom,
+               "traffic_bytes_per_launch": kernels[dom]["bytes_per_launch"],
+               "kernels": kernels, "scales": scales,
                "calibration": f"__amd_rocclr_copyBuffer of {copy_mib} MiB (torch D2D copy)",
                "kernel_source_sha256": kernel_source_hash()}
     with open(out, "w") as f:
@@ -89,16 +114,18 @@ def summarize_pmc(fetch_csv: str, write_csv: str, copy_mib: int, out: str) -> di
     return summary
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
-    or None when the kernel sources changed since it was taken."""
+def measured_traffic(workload: str, shape: dict, path: str | None = None):
+    """The committed counter summary of this workload, or None when there is none,
+    or it was taken on another shape or on other kernel sources."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path or traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return t.get("traffic_bytes_per_launch")
+    if t.get("workload") != workload or t.get("shape") != shape:
+        return None
+    return t
 
 
 def log(msg: str) -> None:
@@ -125,7 +152,10 @@ def parse():
                     help="time only the GQA -> SAGA key merge and print its JSON")
     ap.add_argument("--merge-reps", type=int, default=20)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the dominant kernel's counter traffic summary and exit")
+                    help="write the workload's per-kernel counter traffic summary and exit")
+    ap.add_argument("--caches", type=int, default=0,
+                    help="independent seeded caches per pass (default: the workload's layers, "
+                         "or for a one-layer workload enough caches for 1 GiB of keys)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 4 plain device-to-device copies of MIB MiB (a reference "
                          "kernel of known traffic for hardware counter runs)")
@@ -175,17 +205,55 @@ def merge_bench(torch, reps: int, warmup: int = 2) -> dict:
     return res
 
 
+def resolve_workload(args):
+    """(cfg, config index, workload name with its overrides, caches per pass, shape)."""
+    from sparse_asymmetric_head_amd import workload as wl
+
+    cfg = next((c for c in wl.CONFIGS if c.name == args.config), None)
+    if cfg is None:
+        return None
+    ci = wl.config_index(cfg)
+    over = {k: v for k, v in (("l_kv", args.l_kv), ("R", args.R), ("N", args.N)) if v > 0}
+    if over:  # the same seeded recipe at another size or refresh period (a sweep point)
+        cfg = cfg.with_(**over)
+    k_bytes = cfg.B * cfg.h_k * cfg.l_kv * cfg.d * 2
+    caches = rotation_caches(cfg.layers, k_bytes, args.caches)
+    name = cfg.name + "".join(f" {k}={v}" for k, v in over.items())
+    if caches != cfg.layers:
+        name += f" caches={caches}"
+    shape = {"B": cfg.B, "h_q": cfg.h_q, "h_k": cfg.h_k, "h_v": cfg.h_v, "d": cfg.d,
+             "l_kv": cfg.l_kv, "N": cfg.N, "R": cfg.R, "caches": caches}
+    return cfg, ci, name, caches, shape
+
+
+def rotation_caches(layers: int, k_bytes: int, forced: int = 0) -> int:
+    """Independent caches one timed pass runs over: a multi-layer workload runs its
+    layers; a one-layer workload rotates over enough seeded caches that a pass reads at
+    least 1 GiB of keys, so no step finds its cache in the 256 MB Infinity Cache."""
+    if forced > 0:
+        return forced
+    if layers > 1:
+        return layers
+    return max(1, min(1024, -(-ROTATE_K_BYTES // k_bytes)))
+
+
 def main() -> int:
     args = parse()
-    if args.summarize_pmc:
-        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
-                                       args.calibrate_copy or 256, TRAFFIC_FILE)))
-        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the SAGA decode step here runs on a single "
               "MI355X with no collectives; run with --gpus 1.", file=sys.stderr)
         return 2
+    res = None if args.merge_only else resolve_workload(args)
+    if res is None and not args.merge_only:
+        print(f"unknown config {args.config}", file=sys.stderr)
+        return 2
+    if args.summarize_pmc:
+        cfg, ci, wname, L, shape = res
+        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                                       args.calibrate_copy or 256, traffic_file(wname), wname,
+                                       shape)))
+        return 0
 
     import torch
 
@@ -199,16 +267,12 @@ def main() -> int:
     if args.merge_only:
         print(json.dumps({"gqa_to_saga_merge": merge_bench(torch, args.merge_reps)}), flush=True)
         return 0
-    cfg = next((c for c in wl.CONFIGS if c.name == args.config), None)
-    if cfg is None:
-        print(f"unknown config {args.config}", file=sys.stderr)
-        return 2
-    ci = wl.config_index(cfg)
-    over = {k: v for k, v in (("l_kv", args.l_kv), ("R", args.R), ("N", args.N)) if v > 0}
-    if over:  # the same seeded recipe at another size or refresh period (a sweep point)
-        cfg = cfg.with_(**over)
-    B, h_q, h_k, h_v, d, l_kv, N, R, T, L = (cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv,
-                                              cfg.N, cfg.R, cfg.steps, cfg.layers)
+    cfg, ci, wname, L, shape = res
+    B, h_q, h_k, h_v, d, l_kv, N, R, T = (cfg.B, cfg.h_q, cfg.h_k, cfg.h_v, cfg.d, cfg.l_kv,
+                                           cfg.N, cfg.R, cfg.steps)
+    # a pass runs every cache once (one decode token through all layers, or one
+    # layer-step on each rotated cache); a workload step is cfg.layers of them
+    steps_per_pass = L / cfg.layers
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy > 0:
@@ -222,8 +286,8 @@ def main() -> int:
         log(f"calibration: 4 copies of {args.calibrate_copy} MiB "
             f"({n} bytes read and {n} written per copy)")
         del src, dst
-    log(f"workload {cfg.name}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv} N={N} "
-        f"R={R} layers={L}")
+    log(f"workload {wname}: B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv} N={N} "
+        f"R={R} layers={cfg.layers} caches per pass={L}")
 
     # ------------------------------------------------------------ inputs
     layers = [wl.make_layer(cfg, l, device=dev, cfg_index=ci) for l in range(L)]
@@ -297,9 +361,13 @@ def main() -> int:
             step(t)
             evs[i + 1].record(stream)
         stream.synchronize()
-        step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
-    ms_per_step = max(gpu_ms, wall_ms) / args.steps
-    us_per_step = ms_per_step * 1e3
+        # per workload step: a pass runs steps_per_pass of them (one, unless a
+        # one-layer workload rotates over several caches)
+        step_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / steps_per_pass
+                   for i in range(args.steps)]
+    pass_us = max(gpu_ms, wall_ms) / args.steps * 1e3
+    us_per_step = pass_us / steps_per_pass
+    ms_per_step = us_per_step / 1e3
     ref_us = [u for i, u in enumerate(step_us) if (args.warmup + i) % R == 0]
     non_us = [u for i, u in enumerate(step_us) if (args.warmup + i) % R != 0]
 
@@ -311,7 +379,8 @@ def main() -> int:
                 "non_refresh_p50": pct(non_us, 0.5),
                 "refresh_p50": pct(ref_us, 0.5), "refresh_steps": len(ref_us)}
     per_step = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in per_step.items()}
-    log(f"timed {args.steps} steps: {us_per_step:.1f} us/step (events {gpu_ms:.3f} ms, "
+    log(f"timed {args.steps} passes of {steps_per_pass:g} steps: {us_per_step:.1f} us/step "
+        f"(events {gpu_ms:.3f} ms, "
         f"wall {wall_ms:.3f} ms); per step p10/p50/p90 {per_step['p10']}/{per_step['p50']}/"
         f"{per_step['p90']} us, non-refresh p50 {per_step['non_refresh_p50']}, refresh p50 "
         f"{per_step['refresh_p50']}")
@@ -389,7 +458,7 @@ def main() -> int:
     o_bytes = B * h_q * d * 4
     v_bytes = B * h_q * mean_count * d * 2
     select_alg = k_bytes + q_bytes + tau_bytes
-    step_alg = L * (k_bytes + q_bytes + tau_bytes + o_bytes + v_bytes)
+    pass_alg = L * (k_bytes + q_bytes + tau_bytes + o_bytes + v_bytes)
     achieved = select_alg / (sel_us * 1e-6)
     log(f"select kernel {sel_us:.2f} us/launch -> {achieved / 1e9:.0f} GB/s")
 
@@ -427,8 +496,8 @@ def main() -> int:
             e1.record(stream)
             stream.synchronize()
             w1 = time.perf_counter()
-        full_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3
-        full_bytes = L * (B * (h_k + h_v) * l_kv * d * 2 + q_bytes + o_bytes)
+        full_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3 / steps_per_pass
+        full_bytes = cfg.layers * (B * (h_k + h_v) * l_kv * d * 2 + q_bytes + o_bytes)
         full = {"us_per_step": round(full_us, 2),
                 "hbm_gbps": round(full_bytes / (full_us * 1e-6) / 1e9, 1),
                 "speedup_saga_sparse_vs_full": round(full_us / us_per_step, 3)}
@@ -471,8 +540,8 @@ def main() -> int:
             e1.record(stream)
             stream.synchronize()
             w1 = time.perf_counter()
-        dense_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3
-        dense_bytes = L * (2 * B * hk * l_kv * d * 2 + q_bytes + o_bytes)
+        dense_us = max(e0.elapsed_time(e1), (w1 - w0) * 1e3) / args.steps * 1e3 / steps_per_pass
+        dense_bytes = cfg.layers * (2 * B * hk * l_kv * d * 2 + q_bytes + o_bytes)
         dense = {"h_kv": hk, "us_per_step": round(dense_us, 2),
                  "hbm_gbps": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
                  "speedup_saga_vs_dense": round(dense_us / us_per_step, 3)}
@@ -508,7 +577,7 @@ def main() -> int:
         t_ref = t_one / S
         # the full trajectory holds n_ref refresh steps and n_norm non-refresh ones
         t_norm = max((t_all / S - n_ref * t_ref) / n_norm, 0.0) if n_norm else 0.0
-        cpu_us = L * (t_ref + (R - 1) * t_norm) / R * 1e6
+        cpu_us = cfg.layers * (t_ref + (R - 1) * t_norm) / R * 1e6
         # the same oracle on one core: one layer's refresh step and one plain step
         cores = oracle.num_threads(lib)
         oracle.set_num_threads(1, lib)
@@ -522,7 +591,7 @@ def main() -> int:
         c2 = time.perf_counter()
         oracle.set_num_threads(cores, lib)
         one_ref, one_norm = c1 - c0, max((c2 - c1) - (c1 - c0), 0.0)
-        one_us = L * (one_ref + (R - 1) * one_norm) / R * 1e6
+        one_us = cfg.layers * (one_ref + (R - 1) * one_norm) / R * 1e6
         cpu_model = ""
         try:
             with open("/proc/cpuinfo") as f:
@@ -534,17 +603,18 @@ def main() -> int:
                "kind": "oracle",
                "single_core_value": round(one_us, 1),
                "host": {"cpu_model": cpu_model, "logical_cpus": os.cpu_count()},
-               "sample": (f"{S} of {L} layers x {steps + 1} oracle layer-steps each (one refresh "
+               "sample": (f"{S} of {L} caches x {steps + 1} oracle layer-steps each (one refresh "
                           f"step alone, then {steps} steps with {n_ref} refreshes, at multiples "
                           f"of {R}) of "
-                          f"{cfg.name}; per-layer costs amortised over R={R} and scaled to {L} "
-                          f"layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
+                          f"{cfg.name}; per-layer costs amortised over R={R} and scaled to "
+                          f"{cfg.layers} layers (refresh {t_ref:.3f} s, non-refresh {t_norm:.3f} s per "
                           f"layer-step, {t_one + t_all:.1f} s of oracle time); single_core_value "
                           f"from layer 0's refresh step and one plain step on one thread "
                           f"(refresh {one_ref:.3f} s, non-refresh {one_norm:.3f} s), scaled alike")}
         log(f"cpu oracle: {cpu_us / 1e3:.1f} ms/step on {cpu['cores']} threads, "
             f"{one_us / 1e3:.1f} ms/step on one ({cpu_model})")
 
+    traffic = measured_traffic(wname, shape)
     merge = None
     if not args.no_merge:
         merge = merge_bench(torch, args.merge_reps)
@@ -554,7 +624,7 @@ def main() -> int:
         "value": round(us_per_step, 2),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": round(args.steps * steps_per_pass),
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": False,
@@ -562,21 +632,31 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name + "".join(f" {k}={v}" for k, v in over.items()),
+        "config": {"workload": wname,
                    "B": B, "h_q": h_q, "h_k": h_k, "h_v": h_v, "d": d,
-                   "l_kv": l_kv, "N": N, "R": R, "layers": L, "global_batch": B,
+                   "l_kv": l_kv, "N": N, "R": R, "layers": cfg.layers, "global_batch": B,
                    "seq_len": l_kv, "parallelism": "single-gpu"},
-        "hbm_gbps": round(step_alg / (us_per_step * 1e-6) / 1e9, 1),
-        "us_per_layer_step": round(us_per_step / L, 3),
+        # every pass reads L independent caches; beyond the 256 MB Infinity Cache none
+        # of them is still on chip when its turn comes again
+        "rotation": {"caches_per_pass": L, "passes": args.steps,
+                     "k_bytes_per_pass": L * k_bytes,
+                     "kv_bytes_resident": L * B * (h_k + h_v) * l_kv * d * 2,
+                     "cold": L * B * (h_k + h_v) * l_kv * d * 2 > MALL_BYTES},
+        "hbm_gbps": round(pass_alg / (pass_us * 1e-6) / 1e9, 1),
+        "us_per_layer_step": round(pass_us / L, 3),
         "mean_survivors_per_row": round(mean_count, 1),
         "roofline": {"bound": "hbm", "kernel": "k_select (score + compare + compact)",
                      "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
-                     "traffic": measured_traffic(), "traffic_unit": "HBM bytes per launch",
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "traffic_unit": "HBM bytes per launch",
+                     "traffic_source": os.path.relpath(traffic_file(wname), ROOT) if traffic else None,
                      "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg,
                      "probe_read_gbps": round(probe_gbps, 1),
                      "frac_of_probe": round(achieved / 1e9 / probe_gbps, 4)},
         "per_step_us": per_step,
+        "kernel_traffic": ({k: v["bytes_per_launch"] for k, v in traffic["kernels"].items()}
+                           if traffic else None),
         "dense_gqa": dense,
         "saga_full_attention": full,
         "gqa_to_saga_merge": merge,
