@@ -191,6 +191,26 @@ int saga_full_attention(const void *Q, const void *K, const void *V, int B, int 
                         int h_v, int d, int64_t l_kv, float *O, void *ws, size_t ws_bytes,
                         void *hip_stream);
 
+/*
+ * saga_decode_step_pivot without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static array inside
+ * the library, one per GPU, of SAGA_STATIC_WORKSPACE_BYTES bytes (128 MiB),
+ * held from the library's first use on that GPU until the process ends; this
+ * entry point itself allocates nothing.  Shapes whose workspace
+ * (saga_workspace_bytes) exceeds it return SAGA_ERR_WORKSPACE and enqueue
+ * nothing; the 128K-context Llama-3.2-1B shape needs 65 MiB, the batch-4
+ * Qwen2.5-1.5B shape 97 MiB.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (several streams or host threads)
+ * race and must be serialised by the caller.  Results equal
+ * saga_decode_step_pivot's bit for bit.  The array's device address is looked
+ * up once per device, on the first call made with that device current.
+ */
+#define SAGA_STATIC_WORKSPACE_BYTES (128u << 20)
+int saga_decode_step_noalloc(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                             int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
+                             int refresh, float *O, int32_t *counts, void *hip_stream);
+
 /* Where the last call left its intermediate results inside the workspace
  * (byte offsets from ws), for inspection and testing. */
 typedef struct saga_ws_layout {

@@ -3,6 +3,7 @@
 // and enqueues the kernels of saga_kernels.hpp on the caller's stream.
 // Declarations and the contract of every entry point: include/saga.h.
 #include <atomic>
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -670,6 +671,56 @@ int saga_decode_step_cache(const void *Q, const void *K, const void *V, int B, i
     int st = make_plan(B, h_q, h_k, h_v, d, len, N, &p, cap);
     if (st != SAGA_OK) return st;
     return decode_pivot(p, Q, K, V, tau, pivot, refresh, O, counts, ws, ws_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free entry point's workspace: one array per GPU, held from the
+// library's first use on that GPU until the process ends.  Host code must never
+// pass `scratch` itself to a kernel or a copy (in host code the name is a
+// host-side stand-in, not the device address): the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in scratch_dev[].
+constexpr size_t kScratchBytes = size_t(SAGA_STATIC_WORKSPACE_BYTES);
+static_assert(kScratchBytes % kAlign == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices];
+
+// The current device's scratch address (looked up on its first call there).
+int scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SAGA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return SAGA_ERR_HIP;
+        }
+        scratch_dev[dev] = ptr;
+    }
+    *out = scratch_dev[dev];
+    return SAGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int saga_decode_step_noalloc(const void *Q, const void *K, const void *V, int B, int h_q, int h_k,
+                             int h_v, int d, int64_t l_kv, int64_t N, float *tau, int32_t *pivot,
+                             int refresh, float *O, int32_t *counts, void *hip_stream) {
+    Plan p;
+    int st = make_plan(B, h_q, h_k, h_v, d, l_kv, N, &p);
+    if (st != SAGA_OK) return st;
+    if (p.total > kScratchBytes) return SAGA_ERR_WORKSPACE;  // beyond the static workspace
+    void *ws = nullptr;
+    if ((st = scratch_ptr(&ws)) != SAGA_OK) return st;
+    return decode_pivot(p, Q, K, V, tau, pivot, refresh, O, counts, ws, kScratchBytes, hip_stream);
 }
 
 int saga_append_kv(void *K, void *V, const void *k_new, const void *v_new, int B, int h_k,

@@ -29,7 +29,9 @@ EXPORTS = (
     "saga_attend", "saga_read_probe", "saga_decode_step_pivot", "saga_full_attention",
     "saga_full_attention_workspace_bytes", "saga_cache_workspace_bytes", "saga_append_kv",
     "saga_decode_step_cache", "saga_merge_workspace_bytes", "saga_merge_key_heads",
+    "saga_decode_step_noalloc",
 )
+STATIC_WORKSPACE_BYTES = 128 << 20  # SAGA_STATIC_WORKSPACE_BYTES
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
 
 
@@ -107,6 +109,9 @@ def lib(path: str | None = None):
     L.saga_decode_step_cache.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, i64, vp,
                                          vp, i32, vp, vp, vp, sz, vp]
     L.saga_decode_step_cache.restype = i32
+    L.saga_decode_step_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, vp,
+                                           vp, i32, vp, vp, vp]
+    L.saga_decode_step_noalloc.restype = i32
     L.saga_read_probe.argtypes = [vp, i64, vp, vp]
     L.saga_read_probe.restype = i32
     L.saga_merge_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
@@ -250,6 +255,22 @@ def saga_decode_step_pivot(Q, K, V, N: int, tau, pivot, refresh: int, O, counts=
                                         int(N), _ptr(tau), _ptr(pivot), int(refresh), _ptr(O),
                                         _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)),
            "saga_decode_step_pivot")
+
+
+def saga_decode_step_noalloc(Q, K, V, N: int, tau, pivot, refresh: int, O, counts=None,
+                             stream=None) -> None:
+    """saga_decode_step_pivot on the library's static per-GPU workspace (no workspace
+    argument; the call allocates nothing).  Calls on one GPU must not overlap."""
+    B, h_q, d = _dims(Q, K, V)
+    h_k, l_kv, h_v = K.shape[1], K.shape[2], V.shape[1]
+    _arr(tau, torch.float32, (B, h_q), "tau")
+    _arr(pivot, torch.int32, (B, h_q, int(N)), "pivot", optional=int(refresh) == 0)
+    _arr(O, torch.float32, (B, h_q, d), "O")
+    _arr(counts, torch.int32, (B, h_q), "counts", optional=True)
+    _check(lib().saga_decode_step_noalloc(_ptr(Q), _ptr(K), _ptr(V), B, h_q, h_k, h_v, d, l_kv,
+                                          int(N), _ptr(tau), _ptr(pivot), int(refresh), _ptr(O),
+                                          _ptr(counts), _stream(stream)),
+           "saga_decode_step_noalloc")
 
 
 def saga_select(Q, K, h_v: int, N: int, tau, refresh: bool, ws, stream=None) -> None:
