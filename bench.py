@@ -144,6 +144,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--no-read-sweep", action="store_true",
+                    help="skip the search for the fastest cold read of the caches")
     ap.add_argument("--cpu-sample-layers", type=int, default=16)
     ap.add_argument("--kernel-timing-steps", type=int, default=8)
     ap.add_argument("--no-merge", action="store_true",
@@ -452,6 +454,45 @@ def main() -> int:
     probe_gbps = B * h_k * l_kv * d * 2 / (probe_us * 1e-6) / 1e9
     log(f"read probe over the same caches: {probe_us:.2f} us/launch -> {probe_gbps:.0f} GB/s")
 
+    # The fastest cold read of the same caches among the library's probe shapes
+    # (workgroups x waves x loads in flight per lane, contiguous ranges or
+    # interleaved runs): the best read pattern this GPU offers for this buffer size.
+    best_read = None
+    if not args.no_read_sweep:
+        for blocks in (256, 512, 1024):
+            for waves, loads in ((4, 4), (4, 8), (4, 16), (8, 4), (8, 8)):
+                for chunked in (True, False):
+                    def shape_pass():
+                        for _ in range(inner):
+                            for l in range(L):
+                                saga.saga_read_probe_shape(Ks[l], sink, blocks, waves, loads,
+                                                           chunked, stream)
+                    with torch.cuda.stream(stream):
+                        shape_pass()
+                        stream.synchronize()
+                        sg = None
+                        if not args.no_graph:
+                            sg = torch.cuda.CUDAGraph()
+                            with torch.cuda.graph(sg, stream=stream):
+                                shape_pass()
+                        run_s = sg.replay if sg is not None else shape_pass
+                        run_s()
+                        stream.synchronize()
+                        k0.record(stream)
+                        for _ in range(reps):
+                            run_s()
+                        k1.record(stream)
+                        stream.synchronize()
+                    us = k0.elapsed_time(k1) * 1e3 / (reps * L * inner)
+                    if best_read is None or us < best_read["us"]:
+                        best_read = {"us": round(us, 3), "blocks": blocks, "waves": waves,
+                                     "loads_per_lane": loads,
+                                     "pattern": "contiguous ranges" if chunked else "interleaved runs"}
+        best_read["gbps"] = round(B * h_k * l_kv * d * 2 / (best_read["us"] * 1e-6) / 1e9, 1)
+        log(f"best cold read of the same caches: {best_read['us']:.2f} us/launch -> "
+            f"{best_read['gbps']:.0f} GB/s ({best_read['blocks']} x {best_read['waves']} waves x "
+            f"{best_read['loads_per_lane']} loads, {best_read['pattern']})")
+
     k_bytes = B * h_k * l_kv * d * 2
     q_bytes = B * h_q * d * 2
     tau_bytes = B * h_q * 4
@@ -653,7 +694,10 @@ def main() -> int:
                      "traffic_source": os.path.relpath(traffic_file(wname), ROOT) if traffic else None,
                      "kernel_us": round(sel_us, 3), "bytes_per_launch": select_alg,
                      "probe_read_gbps": round(probe_gbps, 1),
-                     "frac_of_probe": round(achieved / 1e9 / probe_gbps, 4)},
+                     "frac_of_probe": round(achieved / 1e9 / probe_gbps, 4),
+                     "best_read": best_read,
+                     "frac_of_best_read": (round(achieved / 1e9 / best_read["gbps"], 4)
+                                           if best_read else None)},
         "per_step_us": per_step,
         "kernel_traffic": ({k: v["bytes_per_launch"] for k, v in traffic["kernels"].items()}
                            if traffic else None),

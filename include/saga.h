@@ -259,6 +259,20 @@ int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k
 #define SAGA_PROBE_SINK_WORDS 256
 int saga_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *hip_stream);
 
+/*
+ * Measurement utility, not part of the method: the same plain read with a
+ * chosen launch shape, for finding the fastest cold read of a buffer on this
+ * GPU.  blocks (1..65536) workgroups of `waves` waves (4 or 8), `loads`
+ * 16-byte non-temporal loads in flight per lane (4, 8 or 16 with 4 waves; 4
+ * or 8 with 8 waves, else SAGA_ERR_UNSUPPORTED).  chunked != 0: workgroup i
+ * reads the i-th of `blocks` contiguous ranges; chunked == 0: the workgroups
+ * take consecutive runs of waves*64*loads items in turn.  Workgroup i XORs
+ * the words it read into sink[i % SAGA_PROBE_SINK_WORDS] (so the XOR of the
+ * whole sink, cleared beforehand, is the XOR of every word of the buffer).
+ */
+int saga_read_probe_shape(const void *buf, int64_t bytes, int blocks, int waves, int loads,
+                          int chunked, uint32_t *sink, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

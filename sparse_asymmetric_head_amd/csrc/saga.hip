@@ -778,6 +778,43 @@ int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k
     return launch_status();
 }
 
+}  // extern "C"
+
+namespace {
+
+template <int W, int U>
+void launch_probe_shape(const void *buf, int64_t n16, int blocks, bool chunked, uint32_t *sink,
+                        hipStream_t s) {
+    const int64_t per = ceil_div(n16, blocks);
+    if (chunked)
+        hipLaunchKernelGGL((k_read_probe_shape<W, U, true>), dim3(blocks), dim3(W * kWave), 0, s,
+                           (const u32x4 *)buf, n16, per, sink, SAGA_PROBE_SINK_WORDS);
+    else
+        hipLaunchKernelGGL((k_read_probe_shape<W, U, false>), dim3(blocks), dim3(W * kWave), 0, s,
+                           (const u32x4 *)buf, n16, per, sink, SAGA_PROBE_SINK_WORDS);
+}
+
+}  // namespace
+
+extern "C" {
+
+int saga_read_probe_shape(const void *buf, int64_t bytes, int blocks, int waves, int loads,
+                          int chunked, uint32_t *sink, void *hip_stream) {
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes <= 0 || bytes % 16 != 0)
+        return SAGA_ERR_INVALID_ARG;
+    if (blocks < 1 || blocks > 65536) return SAGA_ERR_INVALID_ARG;
+    const int64_t n16 = bytes / 16;
+    hipStream_t s = (hipStream_t)hip_stream;
+    const bool ch = chunked != 0;
+    if (waves == 4 && loads == 4) launch_probe_shape<4, 4>(buf, n16, blocks, ch, sink, s);
+    else if (waves == 4 && loads == 8) launch_probe_shape<4, 8>(buf, n16, blocks, ch, sink, s);
+    else if (waves == 4 && loads == 16) launch_probe_shape<4, 16>(buf, n16, blocks, ch, sink, s);
+    else if (waves == 8 && loads == 4) launch_probe_shape<8, 4>(buf, n16, blocks, ch, sink, s);
+    else if (waves == 8 && loads == 8) launch_probe_shape<8, 8>(buf, n16, blocks, ch, sink, s);
+    else return SAGA_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
 int saga_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *hip_stream) {
     if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes <= 0 || bytes % 16 != 0)
         return SAGA_ERR_INVALID_ARG;

@@ -1295,6 +1295,38 @@ __global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4 *p, int64_t
     }
 }
 
+// Plain streaming read with a chosen launch shape (the search for the best
+// cold-read pattern): WAVES waves per workgroup, UNR 16-byte non-temporal
+// loads in flight per lane.  CHUNKED: workgroup i reads the contiguous range
+// [i*per, (i+1)*per) of 16-byte items, its lanes consecutive; else the
+// workgroups take consecutive runs of WAVES*64*UNR items in turn (grid-
+// strided).  Items past the end are clamped to the last item and masked.
+// Each workgroup folds the words it read with XOR into
+// sink[blockIdx.x % SAGA_PROBE_SINK_WORDS] (atomically).
+template <int WAVES, int UNR, bool CHUNKED>
+__global__ __launch_bounds__(WAVES * kWave) void k_read_probe_shape(const u32x4 *p, int64_t n16,
+                                                                   int64_t per, uint32_t *sink,
+                                                                   int sink_words) {
+    constexpr int T = WAVES * kWave;
+    uint32_t acc = 0u;
+    const int64_t beg = CHUNKED ? (int64_t)blockIdx.x * per : (int64_t)blockIdx.x * T * UNR;
+    const int64_t end = CHUNKED ? min(n16, beg + per) : n16;
+    const int64_t stride = CHUNKED ? (int64_t)T * UNR : (int64_t)gridDim.x * T * UNR;
+    for (int64_t i = beg + threadIdx.x; i < end; i += stride) {
+        u32x4 v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int64_t k = i + (int64_t)u * T;
+            v[u] = ld16_stream(p + (k < end ? k : end - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+            if (i + (int64_t)u * T < end) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & 63) == 0) atomicXor(sink + blockIdx.x % sink_words, acc);
+}
+
 // ------------------------------------------------------------------ dense
 
 struct DenseArgs {

@@ -29,7 +29,7 @@ EXPORTS = (
     "saga_attend", "saga_read_probe", "saga_decode_step_pivot", "saga_full_attention",
     "saga_full_attention_workspace_bytes", "saga_cache_workspace_bytes", "saga_append_kv",
     "saga_decode_step_cache", "saga_merge_workspace_bytes", "saga_merge_key_heads",
-    "saga_decode_step_noalloc",
+    "saga_decode_step_noalloc", "saga_read_probe_shape",
 )
 STATIC_WORKSPACE_BYTES = 128 << 20  # SAGA_STATIC_WORKSPACE_BYTES
 PROBE_SINK_WORDS = 256  # SAGA_PROBE_SINK_WORDS
@@ -112,6 +112,8 @@ def lib(path: str | None = None):
     L.saga_decode_step_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i64, vp,
                                            vp, i32, vp, vp, vp]
     L.saga_decode_step_noalloc.restype = i32
+    L.saga_read_probe_shape.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp]
+    L.saga_read_probe_shape.restype = i32
     L.saga_read_probe.argtypes = [vp, i64, vp, vp]
     L.saga_read_probe.restype = i32
     L.saga_merge_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
@@ -372,6 +374,16 @@ def saga_read_probe(buf, sink, stream=None) -> None:
     assert sink.numel() >= PROBE_SINK_WORDS and sink.element_size() == 4
     _check(lib().saga_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                  _stream(stream)), "saga_read_probe")
+
+
+def saga_read_probe_shape(buf, sink, blocks: int, waves: int, loads: int, chunked: bool,
+                          stream=None) -> None:
+    """Measurement utility: the plain read with a chosen launch shape; sink (32-bit,
+    PROBE_SINK_WORDS entries, cleared first) receives XOR folds (XOR of all = XOR of buf)."""
+    assert sink.numel() >= PROBE_SINK_WORDS and sink.element_size() == 4
+    _check(lib().saga_read_probe_shape(_ptr(buf), buf.numel() * buf.element_size(), int(blocks),
+                                       int(waves), int(loads), 1 if chunked else 0, _ptr(sink),
+                                       _stream(stream)), "saga_read_probe_shape")
 
 
 # ----------------------------------------------------------------- conveniences

@@ -476,6 +476,24 @@ def test_read_probe_checksum():
         assert got == want, nbytes
 
 
+@pytest.mark.parametrize("shape", [(256, 4, 8, True), (512, 4, 4, False), (1024, 4, 16, True),
+                                   (256, 8, 8, False), (3, 8, 4, True)])
+def test_read_probe_shape_checksum(shape):
+    """The shaped read probe reads every 16-byte item exactly once in every
+    launch shape: the XOR of the sink equals the XOR of the buffer's words."""
+    blocks, waves, loads, chunked = shape
+    g = torch.Generator().manual_seed(6)
+    for nbytes in (16, 4096 + 48, (8 << 20) + 16 * 7):
+        host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), generator=g,
+                             dtype=torch.int64).to(torch.int32)
+        sink = torch.zeros(saga.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        saga.saga_read_probe_shape(host.cuda(), sink, blocks, waves, loads, chunked)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+        assert got == want, (shape, nbytes)
+
+
 def ws_layout(B, h_q, h_k, h_v, d, l_kv, N):
     return saga.saga_workspace_layout(B, h_q, h_k, h_v, d, l_kv, N)
 
