@@ -5,12 +5,13 @@
 //   k_gram<D,1>      per-chunk second moments S_r of each group's queries (h_kt items)
 //   k_gram<D,0>      per-chunk second moments G_p of K_a - K_b         (one item per pair)
 //   k_gram_reduce    fixed-order fp64 sum over chunks
-//   k_pair_pinv<D>   (S_a + S_b)^+ by a rank-revealing Cholesky        (one block per pair)
+//   k_pair_inv<D>    S^-1 by blocked sweeps when S = S_a + S_b is comfortably full rank
+//   k_pair_pinv<D>   S^+ by pivoted Cholesky for the other pairs            (one block per pair)
 //   k_pair_maps<D>   P_a = S_a S^+, P_b = S_b S^+               (pairs x tile groups)
 //   k_pair_cost<D>   partial eq. 13 costs                          (pairs x tile groups)
 //   k_match          pair costs from the partials, then the minimum-weight perfect
 //                    matching                                          (one block)
-//   k_merged_weight  eq. 15 in the weight layout     (h_kt/2 x d/8 x d_model/256 blocks)
+//   k_merged_weight  eq. 15 in the weight layout     (h_kt/2 x d/16 x d_model/64 blocks)
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -40,7 +41,8 @@ struct MergePlan {
     int h_q, h_kt, d, dm, P, items, nq, nd;
     int64_t ct_q, ct_d;   // tokens per Gram block: query items, key-difference items
     int64_t ldt;          // token stride of the channel-major keys (n rounded up to 128)
-    size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_cost, off_rank, off_dp, off_choice, bytes;
+    size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_cost, off_rank, off_dp, off_choice,
+        bytes;
 };
 
 int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan *p) {
@@ -59,12 +61,12 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     p->items = h_kt + p->P;
     // Samples per Gram block, per launch (measured on both layer shapes): about
     // kGramBlockBudget / d blocks -- a d x d partial costs d^2 words to write and
-    // reduce -- with at least 8 d samples per query block; key-difference blocks
+    // reduce -- with at least 4 d samples per query block; key-difference blocks
     // take at least 16 d samples unless that leaves fewer than kMinGramBlocks
     // blocks, and then at least 4 d.
     const int64_t g_max = ceil_div(h_q, h_kt);
     const int64_t target = kGramBlockBudget / d;
-    const int64_t s_q = std::max<int64_t>(8 * d, ceil_div(n * h_q, target));
+    const int64_t s_q = std::max<int64_t>(4 * d, ceil_div(n * h_q, target));
     int64_t s_d = std::max<int64_t>(16 * d, ceil_div(n * p->P, target));
     if (p->P * ceil_div(n, s_d) < kMinGramBlocks)
         s_d = std::max<int64_t>(4 * d, ceil_div(n * p->P, kMinGramBlocks));
@@ -99,9 +101,12 @@ void pair_table(int h_kt, uint8_t *pa, uint8_t *pb) {
         }
 }
 
+// dynamic LDS of k_pair_pinv (two padded d x d matrices and two pivot rows) and
+// of k_pair_inv
 size_t pinv_lds_bytes(int d) {
-    return (size_t)2 * d * (d + 4) * sizeof(float) + (size_t)2 * d * sizeof(float);
+    return ((size_t)2 * d * (d + 4) + (size_t)2 * d) * sizeof(float);
 }
+size_t inv_lds_bytes(int d) { return (size_t)blocked_lds_floats(d) * sizeof(float); }
 
 // The d = 128 pseudoinverse and the projection's LDS rings take more than
 // 64 KB of dynamic LDS; say so once per process.
@@ -110,6 +115,8 @@ int lds_limits_once() {
         const hipFuncAttribute at = hipFuncAttributeMaxDynamicSharedMemorySize;
         const bool ok =
             hipFuncSetAttribute((const void *)k_pair_pinv<128>, at, (int)pinv_lds_bytes(128)) ==
+                hipSuccess &&
+            hipFuncSetAttribute((const void *)k_pair_inv<128>, at, (int)inv_lds_bytes(128)) ==
                 hipSuccess &&
             hipFuncSetAttribute((const void *)k_kproj<128>, at, (int)proj_lds_bytes(128)) ==
                 hipSuccess &&
@@ -171,6 +178,8 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
     ia.rank = (int *)(ws + p.off_rank);
     ia.h_kt = p.h_kt;
     pair_table(p.h_kt, ia.pa, ia.pb);
+    hipLaunchKernelGGL(k_pair_inv<D>, dim3((unsigned)p.P), dim3(pinv_threads(D)), inv_lds_bytes(D), s,
+                       ia);
     hipLaunchKernelGGL(k_pair_pinv<D>, dim3((unsigned)p.P), dim3(pinv_threads(D)), pinv_lds_bytes(D), s,
                        ia);
 
@@ -220,8 +229,7 @@ int run_merge(const MergePlan &p, const void *X, const void *Q, const void *W_K,
 
     WeightArgs wa{(const uint16_t *)W_K, Pm, pairs, W_merged, p.dm, p.h_kt};
     hipLaunchKernelGGL(k_merged_weight<D>,
-                       dim3((unsigned)(p.h_kt / 2), (unsigned)(D / kWCh),
-                            (unsigned)ceil_div(p.dm, kThreads)),
+                       dim3((unsigned)(p.h_kt / 2), (unsigned)(D / kWC), (unsigned)(p.dm / kWX)),
                        dim3(kThreads), 0, s, wa);
     return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP;
 }

@@ -199,11 +199,12 @@ struct GramArgs {
 
 // Tile groups of a Gram block: the (D/16)(D/16+1)/2 tiles I <= J of one item's
 // second moment are dealt round-robin to gram_groups blocks (blockIdx.z) that
-// read the same samples, so that a d = 128 block holds a half (queries) or a
-// quarter (key differences, whose double-buffered fp32 loads take the other
-// half of the registers) of the accumulators.
+// read the same samples.  A query block holds all of them (d = 128: 144
+// accumulator registers of the 512 a lane has at one wave per SIMD); a d = 128
+// key-difference block holds a quarter, since its double-buffered fp32 loads
+// and bf16 splits take most of the rest (measured: a half is slower).
 __host__ __device__ constexpr int gram_groups(int D, bool is_q) {
-    return D >= 128 ? (is_q ? 2 : 4) : 1;
+    return D >= 128 ? (is_q ? 1 : 4) : 1;
 }
 
 constexpr int kGramStep = 32;   // samples per MFMA 16x16x32 k-step
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void k_gram_reduce(ReduceArgs a) {
     const float *p = a.part + base + e;
     double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
     int c = 0;
+#pragma unroll 4                       // 16 loads in flight
     for (; c + 4 <= nc; c += 4) {
         s0 += (double)p[(int64_t)(c + 0) * a.dd];
         s1 += (double)p[(int64_t)(c + 1) * a.dd];
@@ -442,6 +444,304 @@ struct PinvArgs {
     int h_kt;
     uint8_t pa[kMaxPairs], pb[kMaxPairs];
 };
+
+// Threads of a pseudoinverse block: each thread of the pivoted path holds 16
+// entries (one register vector) of the D x D working matrix, so a step's update
+// is short and the block's waves split it evenly (d = 64: 256 threads, d = 128:
+// 1024); the blocked path uses the same count.
+__host__ __device__ constexpr int pinv_threads(int D) { return D * D / 16; }
+
+// ---- fast path: S^-1 for a comfortably full-rank S by blocked sweeps
+//
+// The symmetric sweep of a block b of rows/columns (the SWEEP operator on a
+// block) maps, with B = A_bb^-1,
+//     A_ij -> A_ij - A_ib B A_bj   (i, j outside b),
+//     A_bj -> B A_bj,  A_ib -> A_ib B,  A_bb -> -B,
+// and sweeping every block in turn leaves -A^-1 (the pivoted path below sweeps
+// one row at a time in pivot order).  Here a block is one 16 x 16 tile, in
+// natural order, without pivoting.  The matrix stays in registers as 16 x 16
+// tiles in the MFMA output layout; one wave inverts each diagonal tile by 16
+// scalar sweeps with cross-lane moves only (no LDS, no barrier), the panel
+// product B A_bj and the rank-16 update run on fp32 MFMA, and the update of
+// the next tile row goes first, so the next diagonal inversion overlaps the
+// rest of the update (three barriers per block).
+// The result is used only when the pivoted rule would also find full rank:
+// the largest diagonal of every Schur complement of S is at least
+// lambda_min(S) >= 1 / trace(S^-1), so if 1 / trace(S^-1) clears the rank cut
+// (kPivotRtol * max_i S_ii) by kFastMargin, S^+ = S^-1.  Otherwise (or on a
+// non-positive tile pivot) the block starts over on the pivoted path.
+constexpr float kFastMargin = 4.0f;
+
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
+// x of lane K of each 16-lane row, to every lane of that row (DPP row_newbcast)
+template <int K>
+__device__ __forceinline__ float row_newbcast(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xF, 0xF, false));
+}
+
+// x of 16-lane row G, to the same lane of all four rows: the row-pair swap gives
+// rows (0, 0, 2, 2) and (1, 1, 3, 3), the half swap of one of those gives
+// (y0, y1, y0, y1) and (y2, y3, y2, y3)
+template <int G>
+__device__ __forceinline__ float rows_bcast(float x) {
+    const unsigned u = __float_as_uint(x);
+    const u32x2v h = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned y = (G & 1) ? h[1] : h[0];
+    const u32x2v f = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float((G & 2) ? f[1] : f[0]);
+}
+
+// A symmetric 16 x 16 tile in one wave: lane l holds row r = l % 16, columns
+// 4 cq .. 4 cq + 3 with cq = l / 16, in w[0..3].  One sweep on pivot K: row K
+// for the lane's own columns comes from lane K of its 16-lane row, column K at
+// row r from 16-lane row K / 4 (same lane position), the pivot by readlane.
+template <int K>
+__device__ __forceinline__ void tile_sweep(float (&w)[4], int r, int cq, bool &ok) {
+    constexpr int KQ = K >> 2, KV = K & 3;
+    const float pk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[KV]), K + 16 * KQ));
+    float rk[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rk[v] = row_newbcast<K>(w[v]);  // A(K, 4 cq + v)
+    const float cr = rows_bcast<KQ>(w[KV]);                      // A(r, K)
+    ok = ok && pk > 0.f && pk < INFINITY;                        // wave-uniform
+    const float ip = __builtin_amdgcn_rcpf(pk);                 // 1 ulp
+    const bool rowk = r == K;
+    const float g = rowk ? 0.f : cr * ip;
+    const float sc = rowk ? ip : 1.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) w[v] = fmaf(-g, rk[v], w[v] * sc);
+    const float colk = rowk ? -ip : cr * ip;
+    w[KV] = (cq == KQ) ? colk : w[KV];
+}
+template <int K>
+struct TileSweeps {
+    static __device__ __forceinline__ void run(float (&w)[4], int r, int cq, bool &ok) {
+        tile_sweep<K>(w, r, cq, ok);
+        TileSweeps<K + 1>::run(w, r, cq, ok);
+    }
+};
+template <>
+struct TileSweeps<16> {
+    static __device__ __forceinline__ void run(float (&)[4], int, int, bool &) {}
+};
+
+// LDS floats of the blocked path: two tile rows, two panel products, two B,
+// a private 16 x 16 tile per wave, S_a + S_b
+__host__ __device__ constexpr int blocked_lds_floats(int D) {
+    return 4 * 16 * (D + 16) + 2 * 16 * 20 + (D * D / 16 / 64) * 256 + D * (D + 4);
+}
+
+// S^-1 of pair p by blocked sweeps; true (block-uniform) when it is S^+ and has
+// been written, false when the pair needs the pivoted path.
+template <int D>
+__device__ __forceinline__ bool pair_inv_blocked(const PinvArgs &a, int p, float *sm) {
+    constexpr int TH = pinv_threads(D);
+    constexpr int NW = TH / 64;          // waves (4 or 16); wave 0 only inverts diagonal tiles
+    constexpr int NTW = NW - 1;          // waves holding tiles
+    constexpr int NB = D / 16;           // tiles per row
+    constexpr int NT = (NB * NB + NTW - 1) / NTW;  // tile slots per wave (6 or 5)
+    constexpr int LP = D + 16;           // row stride of a tile row: 16 x 4 MFMA reads hit 64 banks
+    constexpr int LB = 20;               // row stride of B
+    float *const pan = sm;               // [2][16][LP] tile row b before the sweep of block b
+    float *const pmb = sm + 2 * 16 * LP; // [2][16][LP] B times that row
+    float *const bmb = sm + 4 * 16 * LP; // [2][16][LB] B = (diagonal tile)^-1
+    float *const own = bmb + 2 * 16 * LB;  // [NW][16][16] a wave's private copy of one B A_bj
+    constexpr int LL = D + 4;
+    float *const ls = own + NW * 256;    // [D][LL] S_a + S_b
+    __shared__ float red[NW], redm[NW];
+    __shared__ int bad;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: tile indices, LDS slots
+    const int li = lane & 15, lk = lane >> 4;  // MFMA operand / output lane roles
+    const float *Sa = a.SG + (int64_t)a.pa[p] * D * D;
+    const float *Sb = a.SG + (int64_t)a.pb[p] * D * D;
+    // slot q of wave w >= 1 holds tile t = (w - 1) + NTW q (if t < NB^2), tile
+    // (t / NB, t % NB); lane holds rows 4 lk + u of column li of it (the MFMA
+    // output layout)
+    auto tile_of = [&](int q) { return wave == 0 ? NB * NB : (wave - 1) + NTW * q; };
+    // S_a + S_b through LDS (coalesced 16-byte loads), then the symmetric part
+    // of the wave's tiles
+#pragma unroll
+    for (int i = 0; i < D * D / 4 / TH; ++i) {
+        const int e = 4 * (tid + TH * i), r = e / D, c = e % D;
+        const float4 x = *(const float4 *)(Sa + e), y = *(const float4 *)(Sb + e);
+        *(float4 *)(ls + r * LL + c) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+    }
+    __syncthreads();
+    f32x4v C[NT];
+    float dmx = 0.f;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = tile_of(q);
+        if (t >= NB * NB) continue;
+        const int r0 = (t / NB) * 16, c0 = (t % NB) * 16;
+        const float4 tt = *(const float4 *)(ls + (c0 + li) * LL + r0 + 4 * lk);  // S(c, r)
+        const float tr4[4] = {tt.x, tt.y, tt.z, tt.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 4 * lk + u, c = c0 + li;
+            C[q][u] = 0.5f * (ls[r * LL + c] + tr4[u]);
+            if (r == c) dmx = fmaxf(dmx, C[q][u]);
+        }
+    }
+    auto publish = [&](int q, float *P) {
+        const int tj = tile_of(q) % NB;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) P[(4 * lk + u) * LP + tj * 16 + li] = C[q][u];
+    };
+    // B A_sj (16 x 16) from the tile row P and B
+    auto panel_tile = [&](const float *P, const float *Bm, int j) {
+        f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4)
+            acc = mfma4(Bm[li * LB + k0 + lk], P[(k0 + lk) * LP + j * 16 + li], acc);
+        return acc;
+    };
+    // the sweep of block s on the wave's tiles outside tile row `skip`
+    auto sweep_block = [&](int s, int skip) {
+        const float *P = pan + (s & 1) * 16 * LP;
+        const float *M = pmb + (s & 1) * 16 * LP;
+        const float *Bm = bmb + (s & 1) * 16 * LB;
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int t = tile_of(q), ti = t / NB, tj = t % NB;
+            if (t >= NB * NB || ti == skip) continue;
+            const bool ib = ti == s, jb = tj == s;
+            if (ib && jb) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) C[q][u] = -Bm[(4 * lk + u) * LB + li];
+            } else if (ib) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) C[q][u] = M[(4 * lk + u) * LP + tj * 16 + li];
+            } else if (jb) {           // A_is B = (B A_si)^T
+                const float4 v = *(const float4 *)(M + li * LP + ti * 16 + 4 * lk);
+                C[q][0] = v.x;
+                C[q][1] = v.y;
+                C[q][2] = v.z;
+                C[q][3] = v.w;
+            } else {                   // A_ij - A_is (B A_sj), A_is = A_si^T
+                f32x4v acc = C[q];
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    acc = mfma4(-P[(k0 + lk) * LP + ti * 16 + li], M[(k0 + lk) * LP + tj * 16 + li], acc);
+                C[q] = acc;
+            }
+        }
+    };
+
+    // (a DPP reduction: the lane-shuffle one keeps its lane addresses live
+    // across the loop and spills them)
+    dmx = fkey_inv(wave_max_u32_dpp(fkey(dmx)));
+    if (lane == 0) redm[wave] = dmx;   // read at the end
+    if (tid == 0) bad = 0;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = tile_of(q);
+        if (t < NB) publish(q, pan);
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int b = 0; b < NB; ++b) {
+        const float *P = pan + (b & 1) * 16 * LP;
+        float *M = pmb + (b & 1) * 16 * LP;
+        float *Bm = bmb + (b & 1) * 16 * LB;
+        // 1. wave 0 inverts the diagonal tile; the others finish the sweep of
+        //    block b - 1 on their tiles outside row b (row b went first)
+        if (wave == 0) {
+            const int r = lane & 15, cq = lane >> 4;
+            const float4 x = *(const float4 *)(P + r * LP + b * 16 + 4 * cq);
+            float w[4] = {x.x, x.y, x.z, x.w};
+            bool ok = true;
+            TileSweeps<0>::run(w, r, cq, ok);
+            *(float4 *)(Bm + r * LB + 4 * cq) = make_float4(-w[0], -w[1], -w[2], -w[3]);
+            if (!ok && lane == 0) bad = 1;
+        } else if (b > 0) {
+            sweep_block(b - 1, b);
+        }
+        __syncthreads();
+        // 2. B A_bj for every j != b, and the sweep of block b on tile row b + 1,
+        //    published for the next block.  The holder of tile (b+1, j) forms
+        //    the B A_bj it needs itself (j = b+1 for j = b), writes it to the
+        //    shared panel product (or, for j = b, to its private copy) and reads
+        //    it back in the operand layout.
+        if (b + 1 < NB) {
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+                const int t = tile_of(q), ti = t / NB, tj = t % NB;
+                if (t >= NB * NB || ti != b + 1) continue;
+                const int jp = tj == b ? b + 1 : tj;
+                const f32x4v pm = panel_tile(P, Bm, jp);
+                float *const dst = tj == b ? own + wave * 256 : M + jp * 16;
+                const int ld = tj == b ? 16 : LP;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dst[(4 * lk + u) * ld + li] = pm[u];
+                if (tj == b) {         // A_(b+1)b B = (B A_b(b+1))^T
+                    const float4 v = *(const float4 *)(dst + li * ld + 4 * lk);
+                    C[q][0] = v.x;
+                    C[q][1] = v.y;
+                    C[q][2] = v.z;
+                    C[q][3] = v.w;
+                } else {
+                    f32x4v acc = C[q];
+#pragma unroll
+                    for (int k0 = 0; k0 < 16; k0 += 4)
+                        acc = mfma4(-P[(k0 + lk) * LP + ti * 16 + li], dst[(k0 + lk) * ld + li], acc);
+                    C[q] = acc;
+                }
+                publish(q, pan + ((b + 1) & 1) * 16 * LP);
+            }
+        } else {
+            for (int j = wave; j < NB; j += NW) {
+                if (j == b) continue;
+                const f32x4v pm = panel_tile(P, Bm, j);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) M[(4 * lk + u) * LP + j * 16 + li] = pm[u];
+            }
+        }
+        __syncthreads();
+    }
+    sweep_block(NB - 1, NB);
+
+    // C = -S^-1: trace(S^-1) = -sum of the diagonal
+    float tr = 0.f;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = tile_of(q), ti = t / NB, tj = t % NB;
+        if (t >= NB * NB) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (ti == tj && 4 * lk + u == li) tr -= C[q][u];
+    }
+    tr = wave_sum(tr);
+    if (lane == 0) red[wave] = tr;
+    __syncthreads();                   // also: every read of the LDS above is done
+    tr = 0.f;
+    dmx = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        tr += red[w];
+        dmx = fmaxf(dmx, redm[w]);
+    }
+    const bool use = !bad && tr > 0.f && tr < INFINITY &&
+                     1.f / tr >= kFastMargin * kPivotRtol * dmx;  // block-uniform
+    if (!use) {
+        if (tid == 0) a.rank[p] = 0;   // the pivoted kernel takes this pair
+        return false;
+    }
+    float *out = a.Sp + (int64_t)p * D * D;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        const int t = tile_of(q), ti = t / NB, tj = t % NB;
+        if (t >= NB * NB) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) out[(ti * 16 + 4 * lk + u) * D + tj * 16 + li] = -C[q][u];
+    }
+    if (tid == 0) a.rank[p] = D;
+    return true;
+}
 
 // C tile (i0, j0) of a product of two LDS matrices (row stride LD), MFMA 16x16x4:
 // C[i][j] = sum_k X(i, k) Y(k, j) with X(i, k) = XT ? X[k][i] : X[i][k] and
@@ -480,11 +780,6 @@ __device__ __forceinline__ void vput(vec16 &v0, vec16 &v1, vec16 &v2, vec16 &v3,
     else v3[m & 15] = x;
 }
 
-// Threads of a pseudoinverse block: each thread holds 16 entries (one register
-// vector) of the D x D working matrix, so a step's update is short and the
-// block's waves split it evenly (d = 64: 256 threads, d = 128: 1024).
-__host__ __device__ constexpr int pinv_threads(int D) { return D * D / 16; }
-
 // Moore-Penrose pseudoinverse of S = S_a + S_b, one block per pair.  A full-rank
 // S is inverted directly by D pivoted symmetric sweeps; otherwise:
 //  1. diagonally pivoted Cholesky, S ~ L L^T with L's rows in the original
@@ -505,7 +800,7 @@ __host__ __device__ constexpr int pinv_threads(int D) { return D * D / 16; }
 // diagonal (lane e holds entries e, e + 64) for the pivot search, so a step
 // costs one barrier.
 template <int D>
-__global__ __launch_bounds__(pinv_threads(D)) void k_pair_pinv(PinvArgs a) {
+__device__ __forceinline__ void pair_pinv_pivoted(const PinvArgs &a, int p, float *sm) {
     constexpr int TH = pinv_threads(D);
     constexpr int NW = TH / 64;        // waves
     constexpr int LD = D + 4;          // 16-byte rows; 16 x 4 MFMA operand reads hit 64 banks
@@ -513,14 +808,13 @@ __global__ __launch_bounds__(pinv_threads(D)) void k_pair_pinv(PinvArgs a) {
     constexpr int R = D * D / TH;     // rows per thread (16: one register vector)
     constexpr int EPL = D / 64;        // diagonal entries per lane
     constexpr int NT = NB * NB / NW;   // output tiles per wave
-    extern __shared__ float sm[];
     float *Lt = sm;                    // [D][LD] row k = column k of L; later Y (row-major)
     float *Mb = sm + D * LD;           // [D][LD] M, later M^-1
     float *cb = Mb + D * LD;           // [2][D] published pivot row of the sweep
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar
     const int c = tid % D;
-    const int d0 = (tid / D) * R;      // wave-uniform
-    const int p = blockIdx.x;
+    const int d0 = __builtin_amdgcn_readfirstlane((tid / D) * R);  // wave-uniform
     const float *Sa = a.SG + (int64_t)a.pa[p] * D * D;
     const float *Sb = a.SG + (int64_t)a.pb[p] * D * D;
 
@@ -727,6 +1021,25 @@ __global__ __launch_bounds__(pinv_threads(D)) void k_pair_pinv(PinvArgs a) {
 #undef APUT
 }
 
+// S^-1 per pair by blocked sweeps, one block per pair: rank[p] = d when S is
+// comfortably full rank (S^+ = S^-1 written), else rank[p] = 0.
+template <int D>
+__global__ __launch_bounds__(pinv_threads(D)) void k_pair_inv(PinvArgs a) {
+    extern __shared__ float sm[];
+    pair_inv_blocked<D>(a, blockIdx.x, sm);
+}
+
+// (S_a + S_b)^+ by the pivoted path for the pairs k_pair_inv left (rank[p] = 0).
+// Two kernels rather than one with both paths: together the paths spill, and a
+// kernel with scratch memory starts its waves several microseconds later
+// (measured), which would slow the common full-rank case.
+template <int D>
+__global__ __launch_bounds__(pinv_threads(D)) void k_pair_pinv(PinvArgs a) {
+    extern __shared__ float sm[];
+    if (a.rank[blockIdx.x] == D) return;  // block-uniform: k_pair_inv inverted it
+    pair_pinv_pivoted<D>(a, blockIdx.x, sm);
+}
+
 // ------------------------------------------------ 4. pair loss and merge maps
 
 struct LossArgs {
@@ -890,44 +1203,53 @@ struct WeightArgs {
     int dm, h_kt;
 };
 
-constexpr int kWCh = 8;   // output channels per thread
+constexpr int kWX = 64;   // output columns x per block (d_model is a multiple of 64)
+constexpr int kWC = 16;   // merged channels per block
 
 // out row i*D + c, column x = sum_e W[a*D+e][x] P_a[e][c] + W[b*D+e][x] P_b[e][c]
 // (eq. 15 in the weight layout: merged head i = pair (a, b) = pairs[i]).  Block
-// (i, channel group, column range): the group's columns of P_a and P_b sit in LDS,
-// each thread owns one column x of the output and kWCh channels.
+// (i, kWC channels, kWX columns): the two heads' weight rows over the block's
+// columns and the channels' columns of P_a and P_b are staged in LDS with
+// 16-byte loads; thread (x, channel quad) accumulates four channels of column x.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_merged_weight(WeightArgs a) {
-    __shared__ float Pa[D][kWCh], Pb[D][kWCh];
+    static_assert(kThreads == kWX * kWC / 4, "one thread per column and channel quad");
+    __shared__ uint16_t wsl[2][D][kWX];
+    __shared__ float psl[2][D][kWC];
     const int tid = threadIdx.x;
-    const int hi = blockIdx.x, c0 = blockIdx.y * kWCh;
+    const int hi = blockIdx.x, c0 = blockIdx.y * kWC, x0 = blockIdx.z * kWX;
     const int ia = a.pairs[2 * hi], ib = a.pairs[2 * hi + 1];
     if (ia < 0 || ib <= ia || ib >= a.h_kt) return;      // uniform per block
     const int p = ia * (2 * a.h_kt - ia - 1) / 2 + (ib - ia - 1);
     const float *src = a.Pm + (int64_t)p * 2 * D * D;
-    for (int e = tid; e < D * kWCh; e += kThreads) {
-        const int r = e / kWCh, c = e % kWCh;
-        Pa[r][c] = src[r * D + c0 + c];
-        Pb[r][c] = src[D * D + r * D + c0 + c];
+    constexpr int W8 = kWX / 8;                           // 16-byte pieces of a staged row
+    for (int e = tid; e < 2 * D * W8; e += kThreads) {
+        const int h = e / (D * W8), r = (e / W8) % D, k8 = e % W8;
+        const uint16_t *g = a.W + ((int64_t)(h ? ib : ia) * D + r) * a.dm + x0 + 8 * k8;
+        *(u32x4 *)&wsl[h][r][8 * k8] = ld16(g);
+    }
+    constexpr int P4 = kWC / 4;
+    for (int e = tid; e < 2 * D * P4; e += kThreads) {
+        const int h = e / (D * P4), r = (e / P4) % D, c4 = e % P4;
+        *(float4 *)&psl[h][r][4 * c4] = *(const float4 *)(src + h * D * D + r * D + c0 + 4 * c4);
     }
     __syncthreads();
-    const int x = blockIdx.z * kThreads + tid;
-    if (x >= a.dm) return;
-    float acc[kWCh];
-#pragma unroll
-    for (int c = 0; c < kWCh; ++c) acc[c] = 0.f;
-    const uint16_t *wa = a.W + (int64_t)ia * D * a.dm + x;
-    const uint16_t *wb = a.W + (int64_t)ib * D * a.dm + x;
-#pragma unroll 4
+    const int x = tid % kWX, cq = tid / kWX;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int e = 0; e < D; ++e) {
-        const float va = __uint_as_float((uint32_t)wa[(int64_t)e * a.dm] << 16);
-        const float vb = __uint_as_float((uint32_t)wb[(int64_t)e * a.dm] << 16);
-#pragma unroll
-        for (int c = 0; c < kWCh; ++c) acc[c] += va * Pa[e][c] + vb * Pb[e][c];
+        const float va = __uint_as_float((uint32_t)wsl[0][e][x] << 16);
+        const float vb = __uint_as_float((uint32_t)wsl[1][e][x] << 16);
+        const float4 pa = *(const float4 *)&psl[0][e][4 * cq];
+        const float4 pb = *(const float4 *)&psl[1][e][4 * cq];
+        acc[0] += va * pa.x + vb * pb.x;
+        acc[1] += va * pa.y + vb * pb.y;
+        acc[2] += va * pa.z + vb * pb.z;
+        acc[3] += va * pa.w + vb * pb.w;
     }
-    float *o = a.out + (int64_t)(hi * D + c0) * a.dm + x;
+    float *o = a.out + (int64_t)(hi * D + c0 + 4 * cq) * a.dm + x0 + x;
 #pragma unroll
-    for (int c = 0; c < kWCh; ++c) o[(int64_t)c * a.dm] = acc[c];
+    for (int c = 0; c < 4; ++c) o[(int64_t)c * a.dm] = acc[c];
 }
 
 }  // namespace merge

@@ -181,16 +181,18 @@ def _blind(channels):
     return f
 
 
-def test_merge_exact_null_space():
-    """Queries never read channels 40..63 (exact zeros): S_a + S_b is singular, so
-    the pseudoinverse, not an inverse, decides the merge, and the merged keys are
-    exactly zero on those channels."""
-    cfg = MergeConfig("t", n=300, h_q=8, h_kt=4, d=64, d_model=128)
-    X, Q, W, got = _run(cfg, 9, mutate=_blind(40))
+@pytest.mark.parametrize("d,keep", [(64, 40), (128, 100)])
+def test_merge_exact_null_space(d, keep):
+    """Queries never read channels keep..d-1 (exact zeros): S_a + S_b is singular, so
+    the pseudoinverse, not an inverse, decides the merge (the blocked inverse must
+    hand every pair to the rank-revealing path), and the merged keys are exactly
+    zero on those channels."""
+    cfg = MergeConfig("t", n=300, h_q=8, h_kt=4, d=d, d_model=128)
+    X, Q, W, got = _run(cfg, 9, mutate=_blind(keep))
     want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
     Wm = _check(cfg, got, want)
     _check_weights(cfg, Wm, X, Q, W, got["pairs"])
-    assert np.all(Wm[:, 40:, :] == 0.0)
+    assert np.all(Wm[:, keep:, :] == 0.0)
 
 
 def test_merge_pseudoinverse_cutoff():
