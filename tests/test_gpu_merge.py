@@ -227,6 +227,38 @@ def test_merge_pseudoinverse_cutoff():
         assert np.abs(Wm[i] - r).max() <= RTOL * np.abs(r).max()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_merge_ill_conditioned_full_rank(d):
+    """Queries with 3/8 of their directions (a random subspace) scaled by 0.03: every
+    S_a + S_b is full rank under the kernel's rule (its smallest eigenvalue, a lower
+    bound of every pivot, is far above 2^-14 of the largest diagonal), but
+    1 / trace(S^-1) is below four times that cut, so the blocked inverse hands every
+    pair to the pivoted kernel, whose full-rank branch must give the plain inverse
+    (the oracle's eigenvalue cut keeps every direction as well)."""
+    cfg = MergeConfig("t", n=400, h_q=8, h_kt=4, d=d, d_model=128)
+    g = torch.Generator().manual_seed(21)
+    R, _ = torch.linalg.qr(torch.randn(d, d, generator=g, dtype=torch.float64))
+    keep = 5 * d // 8
+
+    def squeeze(X, Q, W):
+        Qs = torch.randn(Q.shape, generator=g, dtype=torch.float64)
+        Qs[:, :, keep:] *= 0.03
+        return X, (Qs @ R).to(torch.bfloat16).contiguous(), W
+
+    X, Q, W, got = _run(cfg, 10, mutate=squeeze)
+    Qn = _f64(Q)
+    cut = 2.0 ** -14
+    for a, b in itertools.combinations(range(cfg.h_kt), 2):
+        S = km.second_moment(Qn, a, cfg.h_kt) + km.second_moment(Qn, b, cfg.h_kt)
+        lam = np.linalg.eigvalsh(S)
+        dmx = np.diag(S).max()
+        assert lam.min() > 8 * cut * dmx, "not comfortably full rank under the pivoted rule"
+        assert 1.0 / np.sum(1.0 / lam) < 4 * cut * dmx, "the blocked inverse would accept it"
+    want = _oracle(X, Q, W, cfg.h_kt, cfg.d)
+    Wm = _check(cfg, got, want)
+    _check_weights(cfg, Wm, X, Q, W, got["pairs"])
+
+
 def test_merge_unqueried_group_costs_nothing():
     """A teacher head none of whose query heads ever fires merges with any head for free."""
     cfg = MergeConfig("t", n=128, h_q=16, h_kt=4, d=64, d_model=128)
