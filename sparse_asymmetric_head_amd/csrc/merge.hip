@@ -63,13 +63,14 @@ int make_merge_plan(int64_t n, int h_q, int h_kt, int d, int d_model, MergePlan 
     // kGramBlockBudget / d blocks -- a d x d partial costs d^2 words to write and
     // reduce -- with at least 4 d samples per query block; key-difference blocks
     // take at least 16 d samples unless that leaves fewer than kMinGramBlocks
-    // blocks, and then at least 4 d.
+    // blocks, and then at least 256 (4 d at d = 64; 2 d at d = 128, whose tile
+    // groups split a chunk four ways).
     const int64_t g_max = ceil_div(h_q, h_kt);
     const int64_t target = kGramBlockBudget / d;
     const int64_t s_q = std::max<int64_t>(4 * d, ceil_div(n * h_q, target));
     int64_t s_d = std::max<int64_t>(16 * d, ceil_div(n * p->P, target));
     if (p->P * ceil_div(n, s_d) < kMinGramBlocks)
-        s_d = std::max<int64_t>(4 * d, ceil_div(n * p->P, kMinGramBlocks));
+        s_d = std::max<int64_t>(256, ceil_div(n * p->P, kMinGramBlocks));
     p->ct_q = ceil_div(s_q, g_max);
     p->ct_d = ceil_div(s_d, kPBM) * kPBM;   // four waves x whole 32-token MFMA steps
     p->ldt = ceil_div(n, kPBM) * kPBM;
