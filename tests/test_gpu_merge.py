@@ -317,6 +317,40 @@ def test_merge_full_size_properties(cfg):
 
 
 @pytest.mark.parametrize("cfg", [merge_config(n) for n in MERGE_BENCH], ids=MERGE_BENCH)
+def test_merge_full_size_costs_match_gram_reference(cfg):
+    """Pair costs at the benchmark sizes (16384 calibration tokens, the launch
+    configuration the benchmark times, with the largest projection tiles):
+    eq. 13 at the eq. 15 merge M, rewritten per group r without n x n logits as
+    the sum over its query heads of ||Q^j E_r^T||_F^2 = <Q^j^T Q^j, E_r^T E_r>,
+    E_r = X W_K^r - X M (so <S_r, E_r^T E_r> with the oracle's S_r), and
+    X M = (X W_K^a S_a + X W_K^b S_b)(S_a + S_b)^+ by eq. 15; fp64 on the CPU from
+    the oracle's second moments and pseudoinverse.  Element-wise within 2e-3."""
+    X, Q, W = make_merge_inputs(cfg, 13, "cpu")
+    print(f"[merge] full-size costs {cfg}", flush=True)
+    m = KeyMerge(cfg.n, cfg.h_q, cfg.h_kt, cfg.d, cfg.d_model)
+    m(X.cuda(), Q.cuda(), W.cuda())
+    torch.cuda.synchronize()
+    w = m.pair_loss.cpu().numpy()
+    h_kt, d = cfg.h_kt, cfg.d
+    Xn, Qn, Wn = _f64(X), _f64(Q), _f64(W)
+    K = Xn @ Wn.T                                 # [n][h_kt d]: keys of every teacher head
+    S = [km.second_moment(Qn, r, h_kt) for r in range(h_kt)]
+    want = np.zeros((h_kt, h_kt))
+    for a, b in itertools.combinations(range(h_kt), 2):
+        Ka, Kb = K[:, a * d:(a + 1) * d], K[:, b * d:(b + 1) * d]
+        KM = (Ka @ S[a] + Kb @ S[b]) @ km.pinv_psd(S[a] + S[b])
+        cost = 0.0
+        for r, Kr in ((a, Ka), (b, Kb)):
+            E = Kr - KM
+            cost += float(np.sum(S[r] * (E.T @ E)))
+        want[a, b] = want[b, a] = cost
+    assert np.all(np.isfinite(w)) and np.array_equal(w, w.T)
+    scale = np.abs(want).max()
+    err = np.abs(w - want) / (np.abs(want) + 1e-6 * scale)
+    assert err.max() <= RTOL, (err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+@pytest.mark.parametrize("cfg", [merge_config(n) for n in MERGE_BENCH], ids=MERGE_BENCH)
 def test_merge_full_width_prefix_matches_oracle(cfg):
     """The benchmark layer width (d_model 2048 / 1536, all heads) on a 384-token
     prefix of its calibration set: element-wise parity with the oracle."""
