@@ -23,7 +23,10 @@
  *     that diagonal falls to 2^-14 times the largest diagonal entry of S; at
  *     full rank S^+ = S^-1, else with S = L L^T at that rank (pivoted
  *     Cholesky) S^+ = L (L^T L)^-2 L^T (fp32 arithmetic; a spectrum with no
- *     gap near that level makes the result depend on rounding);
+ *     gap near that level makes the result depend on rounding).  S^-1 is
+ *     first formed without pivoting and kept when 1/trace(S^-1) is at least
+ *     4 times that cut (every pivot then clears it); otherwise the pair takes
+ *     the pivoted path;
  *   - equal-cost pairings: the one whose lowest head takes the lowest
  *     partner wins, recursively;
  *   - merged head i serves the query heads of teacher groups pairs[i][0]
@@ -45,8 +48,9 @@
  * Arithmetic: keys X W_K^T from bf16 products accumulated in fp32; second
  * moments of the queries from exact bf16 products, of the fp32 key
  * differences from a bf16 high/low split (about 2^-16 relative), both summed
- * in fp32 per block and fp64 across blocks; the pseudoinverse (pivoted
- * Cholesky, symmetric sweeps inverting L^T L) and the d x d products in fp32;
+ * in fp32 per block and fp64 across blocks; the pseudoinverse (blocked
+ * symmetric sweeps, or pivoted Cholesky and symmetric sweeps inverting
+ * L^T L) and the d x d products in fp32;
  * costs summed in fp64.
  * Supported: d in {64, 128}; h_kt even, 2 <= h_kt <= 16; h_kt <= h_q <= 1024;
  * d_model a multiple of 64, 64 <= d_model <= 32768; 1 <= n <= 2^26.
