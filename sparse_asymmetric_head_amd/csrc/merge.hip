@@ -40,7 +40,7 @@ struct MergePlan {
     int64_t n;
     int h_q, h_kt, d, dm, P, items, nq, nd;
     int64_t ct_q, ct_d;   // tokens per Gram block: query items, key-difference items
-    int64_t ldt;          // token stride of the channel-major keys (n rounded up to 128)
+    int64_t ldt;          // tokens of the projected keys (n rounded up to 128; kfrag_index)
     size_t off_K, off_part, off_SG, off_Sp, off_Pm, off_cost, off_rank, off_dp, off_choice,
         bytes;
 };

@@ -43,13 +43,26 @@ __device__ __forceinline__ f32x4v mfma4(float a, float b, f32x4v c) {
 struct ProjArgs {
     const uint16_t *X;  // [n][dm] bf16
     const uint16_t *W;  // [cols][dm] bf16 (row r*D + c = channel c of teacher key head r)
-    float *Kt;          // [cols][ldt] fp32, channel-major; tokens n .. ldt-1 written as zero
+    float *Kt;          // fp32 keys in key-fragment order (kfrag_index); tokens n .. ldt-1 written as zero
     int64_t n, ldt;     // ldt: n rounded up to 128
     int dm;
     int cols;
 };
 
 constexpr int kPBM = 128, kPBN = 128, kPBK = 64;    // token padding, block columns, k-stage
+
+// Key-fragment order of the projected keys: channel c (of all h_kt d) and token t
+// (of ldt) sit in the 2 KB block of 16-channel group c / 16 and 32-token group
+// t / 32; inside it, lane l = 16 q + i (channel 16 (c / 16) + i, tokens 8 q ..
+// 8 q + 7 of the group) finds its first four tokens at 16-byte slot l and the
+// next four at slot 64 + l.  A wave then reads an MFMA operand (16 channels x 32
+// tokens, as the key-difference Gram needs it) as two contiguous 1 KB loads, and
+// the projection's four-token stores of 16 consecutive channels are contiguous.
+__host__ __device__ __forceinline__ int64_t kfrag_index(int64_t c, int64_t t, int64_t ldt) {
+    const int64_t blk = (c >> 4) * (ldt >> 5) + (t >> 5);
+    const int tt = (int)(t & 31);
+    return blk * 512 + ((tt >> 2) & 1) * 256 + (16 * (tt >> 3) + (int)(c & 15)) * 4 + (tt & 3);
+}
 
 // LDS tile [rows][64 k] bf16: row = 8 chunks of 16 B, chunk c of row r stored
 // at chunk position c ^ (r & 7), so the 16 rows one MFMA operand read touches
@@ -178,7 +191,7 @@ __global__ __launch_bounds__(proj_threads(BM)) void k_kproj(ProjArgs a) {
             const f32x4v v = acc[i][j];
             const float4 o = {t + 0 < a.n ? v[0] : 0.f, t + 1 < a.n ? v[1] : 0.f,
                               t + 2 < a.n ? v[2] : 0.f, t + 3 < a.n ? v[3] : 0.f};
-            *(float4 *)(a.Kt + (int64_t)(n0 + wn * 64 + j * 16 + (lane & 15)) * a.ldt + t) = o;
+            *(float4 *)(a.Kt + kfrag_index(n0 + wn * 64 + j * 16 + (lane & 15), t, a.ldt)) = o;
         }
     }
 }
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(proj_threads(BM)) void k_kproj(ProjArgs a) {
 
 struct GramArgs {
     const uint16_t *Q;   // [n][h_q][D] bf16 calibration queries
-    const float *Kt;     // [h_kt*D][ldt] fp32 projected keys, channel-major, zero past n
+    const float *Kt;     // fp32 projected keys in key-fragment order (kfrag_index), zero past n
     int64_t ldt;         // a multiple of 128, >= n
     float *part;         // per-block partial sums: [item][chunk][D][D] of this launch's items
     int64_t n;
@@ -230,8 +243,9 @@ __device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
 //   80-byte rows make the 16-byte fragment reads conflict-free).  bf16 inputs:
 //   the products are exact.
 //  else: item p = blockIdx.y, G_p over tokens of the fp32 key difference
-//   K_a - K_b, read channel-major (a lane's 8 tokens are contiguous, no
-//   staging), split into bf16 high and low parts; hi hi + hi lo + lo hi per tile.
+//   K_a - K_b, read in key-fragment order (a lane's 8 tokens arrive in two
+//   16-byte slots of contiguous 1 KB wave loads, no staging), split into bf16
+//   high and low parts; hi hi + hi lo + lo hi per tile.
 // Loads of the next step are issued before the current step's multiplies.  The
 // block writes its tiles (and their mirror images) into the (item, chunk) partial.
 template <int D, bool IS_Q>
@@ -331,17 +345,20 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
         const int64_t ntok = t_end > t_beg ? t_end - t_beg : 0;  // a multiple of 128
         const int64_t per_wave = ntok / kGramWaves;
         const int64_t w_beg = t_beg + wave * per_wave, w_end = w_beg + per_wave;
-        const float *Ka = a.Kt + (int64_t)(ka * D + i16) * a.ldt + 8 * q4;
-        const float *Kb = a.Kt + (int64_t)(kb * D + i16) * a.ldt + 8 * q4;
-        // raw[I][0..1]: tokens t0 + 8 q4 .. +7 of channel 16 I + i16, heads a, b
+        // raw[I][0..1]: tokens t0 + 8 q4 .. +7 of channel 16 I + i16, heads a, b:
+        // 16-byte slots lane and 64 + lane of the (channel group, token group)
+        // block, so each load of the wave is 1 KB contiguous
+        const int64_t gstride = (a.ldt >> 5) * 512;   // floats per 16-channel group
+        const float *Ka = a.Kt + (int64_t)(ka * D / 16) * gstride + lane * 4;
+        const float *Kb = a.Kt + (int64_t)(kb * D / 16) * gstride + lane * 4;
         auto load = [&](int64_t t0, float4 (&ra)[NB][2], float4 (&rb)[NB][2]) {
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-                const int64_t off = (int64_t)16 * I * a.ldt + t0;
+                const int64_t off = I * gstride + (t0 >> 5) * 512;
                 ra[I][0] = *(const float4 *)(Ka + off);
-                ra[I][1] = *(const float4 *)(Ka + off + 4);
+                ra[I][1] = *(const float4 *)(Ka + off + 256);
                 rb[I][0] = *(const float4 *)(Kb + off);
-                rb[I][1] = *(const float4 *)(Kb + off + 4);
+                rb[I][1] = *(const float4 *)(Kb + off + 256);
             }
         };
         auto process = [&](const float4 (&ra)[NB][2], const float4 (&rb)[NB][2]) {
