@@ -219,9 +219,9 @@ typedef struct saga_ws_layout {
     int64_t scores_ld;     /* row stride of the scores, in elements (>= l_kv) */
     size_t seg_off;        /* int32 [B*h_q][n_seg][seg_words]: survivor records, each
                               { count, order key of the max score, then (t, score bits)
-                              pairs }; segment k = 4c + w of a row lists positions of
-                              chunk c from the groups of seg_group rows w, w+4, w+8, ...
-                              of that chunk (seg_cap positions in all) */
+                              pairs }; segment k = 4c + s of a row lists positions of
+                              chunk c from its groups of seg_group rows s, s+8, s+16,
+                              ..., then s+4, s+12, ... (seg_cap positions in all) */
     int64_t seg_words;     /* int32 words per record (multiple of 16) */
     int64_t chunk_len;     /* cache positions per streaming block */
     int64_t n_chunk;       /* blocks per key-head row: ceil(l_kv / chunk_len) */
@@ -229,8 +229,7 @@ typedef struct saga_ws_layout {
     int64_t seg_cap;       /* positions covered by one segment (chunk_len / 4) */
     int64_t seg_group;     /* rows per group of a segment: 16 times the select pass's
                               tiles per wave iteration -- 16 when ceil(B*h_k*l_kv / 256)
-                              <= 256, else 32 when it is <= 512, else 16 * 4 * 64 / d
-                              (never more than 16 * 4 * 64 / d) */
+                              <= 256, else 16 * 2 * 64 / d */
 } saga_ws_layout;
 
 /* Fill *out for this shape.  Returns SAGA_OK or a negative status. */
@@ -248,7 +247,7 @@ int saga_selection_mask(const void *ws, size_t ws_bytes, int B, int h_q, int h_k
 
 /*
  * Measurement utility, not part of the method: read the `bytes` bytes at buf
- * once with the streaming kernels' launch shape (256 workgroups of 4 waves,
+ * once with the streaming kernels' launch shape (256 workgroups of 8 waves,
  * 16-byte non-temporal loads, eight in flight per lane) and store, for each
  * workgroup i, the XOR of the 32-bit words it read in sink[i].  Its rate is
  * the achievable-read reference the streaming kernels are compared with.

@@ -30,7 +30,7 @@ constexpr int kMaxQueryHeads = 32768;
 #define SAGA_DENSE_BLOCKS 512
 #endif
 constexpr int kTargetDenseBlocks = SAGA_DENSE_BLOCKS;  // dense baseline blocks per launch
-constexpr int64_t kChunkUnit = 64 * SAGA_SELECT_U;  // chunk_len granularity: one wave-iteration stride of all 4 waves
+constexpr int64_t kChunkUnit = kSelWaves * 16 * SAGA_SELECT_U;  // chunk_len granularity: one wave-iteration stride of the select block
 constexpr int64_t kHistBlock = kHistBlockMax;  // positions per histogram/collect block
 constexpr size_t kAlign = 256;
 
@@ -69,7 +69,7 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
 }
 
 // Chunk granularity of the short-cache plan: one 16-row tile per wave
-// iteration of the 4 waves.
+// iteration of the block's waves.
 constexpr int64_t kShortUnit = kWaves * 16;
 
 // Short cache: the streaming plan would give each wave a single iteration
@@ -82,14 +82,17 @@ bool short_plan(int64_t pairs, int64_t l_kv) {
     return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= kChunkUnit;
 }
 
-// k_select tiles per wave iteration: one on the short plan; two where the
-// streaming chunks would hold two four-tile iterations per wave (32K at the
-// Llama shape); else the streaming choice (4 at d 64, 2 at d 128).
+// k_select tiles per wave iteration: one on the short plan, else the
+// streaming choice (2 at d 64, 1 at d 128).  Chunk lengths are multiples of
+// kWaves record groups either way (the record order needs it).
 int select_u(int64_t pairs, int64_t l_kv, int d) {
     if (short_plan(pairs, l_kv)) return 1;
-    const int u = d == 64 ? select_tiles<64>() : select_tiles<128>();
-    return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= 2 * kChunkUnit && u > 2 ? 2 : u;
+    return d == 64 ? select_tiles<64>() : select_tiles<128>();
 }
+static_assert(kShortUnit % (kWaves * 16) == 0, "short chunks: whole record groups per segment");
+static_assert(kChunkUnit % (kWaves * 16 * select_tiles<64>()) == 0 &&
+                  kChunkUnit % (kWaves * 16 * select_tiles<128>()) == 0,
+              "streaming chunks: whole record groups per segment");
 
 // Streaming split: about kTargetSelectBlocks blocks over all (b, key head)
 // pairs, and at most kMaxSub/kWaves chunks per row (non-decreasing in l_kv).
@@ -268,26 +271,27 @@ void launch_attend(const AttendArgs &aa, int64_t grid, bool direct15, bool sprea
 }
 
 template <int D, int NT, bool MAT>
-void launch_select_t(const SelectArgs &a, int u, int blocks, hipStream_t s) {
-    if (u == 1)
-        hipLaunchKernelGGL((k_select<D, NT, MAT, 1>), dim3(blocks), dim3(kThreads), 0, s, a);
-    else if (u == 2)
-        hipLaunchKernelGGL((k_select<D, NT, MAT, 2>), dim3(blocks), dim3(kThreads), 0, s, a);
+void launch_select_t(const SelectArgs &a, int u, int blocks, int threads, hipStream_t s) {
+    if (u == 1 || select_tiles<D>() == 1)
+        hipLaunchKernelGGL((k_select<D, NT, MAT, 1>), dim3(blocks), dim3(threads), 0, s, a);
     else
-        hipLaunchKernelGGL((k_select<D, NT, MAT, select_tiles<D>()>), dim3(blocks), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_select<D, NT, MAT, select_tiles<D>()>), dim3(blocks), dim3(threads), 0, s, a);
 }
 
 template <bool MAT>
 void launch_select(const Plan &p, const SelectArgs &a, hipStream_t s) {
     const int blocks = p.B * p.h_k * p.n_chunk;
+    // chunks of only kWaves groups (short caches) leave the upper waves
+    // without rows: launch the lower four alone
+    const int threads = p.chunk_len / p.grp > kWaves ? kSelThreads : kThreads;
     if (p.d == 64) {
-        if (p.nt == 1) launch_select_t<64, 1, MAT>(a, p.u, blocks, s);
-        else if (p.nt == 2) launch_select_t<64, 2, MAT>(a, p.u, blocks, s);
-        else launch_select_t<64, 4, MAT>(a, p.u, blocks, s);
+        if (p.nt == 1) launch_select_t<64, 1, MAT>(a, p.u, blocks, threads, s);
+        else if (p.nt == 2) launch_select_t<64, 2, MAT>(a, p.u, blocks, threads, s);
+        else launch_select_t<64, 4, MAT>(a, p.u, blocks, threads, s);
     } else {
-        if (p.nt == 1) launch_select_t<128, 1, MAT>(a, p.u, blocks, s);
-        else if (p.nt == 2) launch_select_t<128, 2, MAT>(a, p.u, blocks, s);
-        else launch_select_t<128, 4, MAT>(a, p.u, blocks, s);
+        if (p.nt == 1) launch_select_t<128, 1, MAT>(a, p.u, blocks, threads, s);
+        else if (p.nt == 2) launch_select_t<128, 2, MAT>(a, p.u, blocks, threads, s);
+        else launch_select_t<128, 4, MAT>(a, p.u, blocks, threads, s);
     }
 }
 
@@ -822,7 +826,7 @@ int saga_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *hip_st
     static_assert(kTargetSelectBlocks <= SAGA_PROBE_SINK_WORDS, "probe sink");
     const int64_t per = ceil_div(n16, kTargetSelectBlocks);
     const int blocks = (int)ceil_div(n16, per);
-    hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(kThreads), 0, (hipStream_t)hip_stream,
+    hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(kSelThreads), 0, (hipStream_t)hip_stream,
                        (const u32x4 *)buf, n16, per, sink);
     return launch_status();
 }

@@ -41,7 +41,7 @@ namespace saga {
 #define SAGA_KMAP 1  // k_select: 1 = each MFMA k-step loads contiguous 64-byte half rows
 #endif
 #ifndef SAGA_SELECT_U
-#define SAGA_SELECT_U 4  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
+#define SAGA_SELECT_U 2  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
 #endif
 // k_select's tiles per wave iteration: the streaming choice, or one tile
 // where 256-row chunks would leave compute units idle (short caches).
@@ -54,27 +54,47 @@ constexpr int select_tiles() { return SAGA_SELECT_U * 64 / D; }
 #define SAGA_NT_LOADS 1  // k_select: non-temporal (streaming) loads of the key cache
 #endif
 
-constexpr int kWaves = 4;     // waves per workgroup of the streaming kernels
+constexpr int kWaves = 4;     // waves per workgroup of the streaming kernels; segments per chunk
+constexpr int kSelWaves = 2 * kWaves;  // k_select: two waves per segment (two per SIMD)
+constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kCapW = 32;     // LDS staging slots per (wave, query head)
+// LDS staging slots per (wave, query head): fewer for groups of more than 32
+// query heads, so the staging of eight waves fits the LDS.
+template <int NT>
+constexpr int cap_w() { return NT > 2 ? 24 : 32; }
 constexpr int kMaxSub = 1024; // max segments per row
 constexpr int kHistBins = 2048;
 constexpr int kHistBlockMax = 8192;  // positions per histogram/collect block
 constexpr int kRecHead = 15;  // survivors held in a record's first 128 bytes
 
+// Record order of a chunk's positions.  A chunk of chunk_len positions is
+// G = chunk_len / grp groups of grp = 16*U rows (G a multiple of kWaves);
+// k_select wave w (of kSelWaves) takes groups w, w + 8, w + 16, ..., and
+// waves s and s + 4 share segment s: the segment lists wave s's groups, then
+// wave s + 4's.  lo_groups = ceil(G / 8) is the most groups a lower wave
+// takes, so the upper wave's list starts at entry lo_groups * grp at most.
+__host__ __device__ inline int seg_lo_groups(int chunk_len, int grp) {
+    return (chunk_len / grp + kSelWaves - 1) / kSelWaves;
+}
+// Group (within the chunk) of the k-th group of segment s in record order.
+__host__ __device__ inline int seg_group_index(int s, int k, int lo_groups) {
+    return k < lo_groups ? s + kSelWaves * k : s + kWaves + kSelWaves * (k - lo_groups);
+}
+
 // Rank of cache position t in the order the survivor records list positions
-// (a bijection on the positions): chunk; wave w of the chunk's block (the
-// segment); the wave's groups of grp = 16*U rows (wave w takes groups w,
-// w+4, ...); the 16-row tile within the group; inside a tile, output
-// register r = row % 4 first, then lane quarter row / 4 (the ballot order).
+// (a bijection on the positions): chunk; segment s = group % 4; within the
+// segment the lower wave's groups, then the upper wave's (above); the
+// 16-row tile within the group; inside a tile, output register r = row % 4
+// first, then lane quarter row / 4 (the ballot order).
 // 32-bit arithmetic: positions, chunk lengths and keys stay below 2^25
 // (l_kv * d * 2 < 2^31).
 __host__ __device__ inline int record_order_key(int t, int chunk_len, int grp) {
     const int c = t / chunk_len, o = t - c * chunk_len;
     const int gi = o / grp, i = o - gi * grp;
-    const int w = gi % kWaves, k = gi / kWaves;
+    const int s = gi % kWaves, up = (gi / kWaves) % 2, k = gi / kSelWaves;
     const int q = i % 16;
-    return c * chunk_len + w * (chunk_len / kWaves) + k * grp + (i - q) + (q % 4) * 4 + q / 4;
+    return c * chunk_len + s * (chunk_len / kWaves) +
+           (up * seg_lo_groups(chunk_len, grp) + k) * grp + (i - q) + (q % 4) * 4 + q / 4;
 }
 
 // Words per segment record for a segment capacity of cap survivors.
@@ -110,8 +130,10 @@ struct SelectArgs {
     uint32_t *state;     // [rows][4] radix state                (materialize mode: cleared here)
 };
 
-// One workgroup = (batch b, key head g, chunk of cache positions).  Each wave
-// takes 16-row tiles of K, U tiles at a time, interleaved across the 4 waves.
+// One workgroup = (batch b, key head g, chunk of cache positions), eight
+// waves (two per SIMD, so one wave's compare work overlaps the other's
+// loads).  Each wave takes groups of U 16-row tiles of K, interleaved across
+// the eight waves; waves s and s + 4 share the chunk's segment s.
 // MFMA 16x16x32 bf16: A operand = 16 K rows (M = position), B operand = the
 // group's query heads (N = head, padded to 16 per N-tile), K dim = d.  At
 // k-step s lane l supplies row l%16, d-elements s*32 + (l/16)*8 .. +8, and
@@ -127,7 +149,7 @@ struct SelectArgs {
 // segment record of that head.  The record order of the positions is the
 // bijection record_order_key below.
 template <int D, int NT, bool MATERIALIZE, int U>
-__global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     // First d-index of the 8 elements lane quarter lq supplies at MFMA
     // k-step s; the query operand uses the same map, so any permutation of
     // the d axis gives the same dot products.
@@ -144,8 +166,11 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     constexpr int CPR = D / 8;             // 16-byte columns per cache row
     constexpr int RPL = 64 / CPR;          // rows per contiguous wave load
     static_assert(KS * RPL == 16, "a tile is KS contiguous wave loads");
-    __shared__ int2 st[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
-    __shared__ u32x4 kt[SAGA_KT_LDS ? kWaves : 1][SAGA_KT_LDS ? U * 16 * CPR : 1];
+    constexpr int kCapW = cap_w<NT>();
+    __shared__ int2 st[MATERIALIZE ? 1 : kSelWaves][MATERIALIZE ? 1 : NT * 16][kCapW];
+    __shared__ u32x4 kt[SAGA_KT_LDS ? kSelWaves : 1][SAGA_KT_LDS ? U * 16 * CPR : 1];
+    // count and max key of each segment's lower wave, per query head
+    __shared__ int2 xlo[MATERIALIZE ? 1 : kWaves][MATERIALIZE ? 1 : NT * 16];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int ln = lane & 15, lq = lane >> 4;
@@ -162,8 +187,9 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
         // leave them at zero.
         const int64_t r0 = (int64_t)b * a.h_q + j_lo, nr = j_hi - j_lo;
         uint32_t *hz = a.hist + r0 * kHistBins, *sz = a.state + r0 * 4;
-        for (int64_t i = (int64_t)chunk * kThreads + threadIdx.x; i < nr * (kHistBins + 4);
-             i += (int64_t)a.n_chunk * kThreads) {
+        const int64_t nthr = blockDim.x;  // four or eight waves
+        for (int64_t i = (int64_t)chunk * nthr + threadIdx.x; i < nr * (kHistBins + 4);
+             i += (int64_t)a.n_chunk * nthr) {
             if (i < nr * kHistBins) hz[i] = 0u;
             else sz[i - nr * kHistBins] = 0u;
         }
@@ -190,7 +216,13 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) staged[nt] = flushed[nt] = 0, mkey[nt] = 0u;
 
-    const int sub = chunk * kWaves + wave;
+    // segment sw of the chunk; the upper wave (up = 1) lists its survivors
+    // after the lower wave's: until the block ends it flushes them from entry
+    // ebase = lo_groups * grp (past anything the lower wave can list) and then
+    // moves them down to follow the lower wave's count
+    const int sw = wave % kWaves, up = wave / kWaves;
+    const int sub = chunk * kWaves + sw;
+    const int ebase = up ? seg_lo_groups((int)a.chunk_len, 16 * U) * 16 * U : 0;
     const uint64_t head_mask = 0x0001000100010001ull << ln;
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const uint16_t *Kb = a.K + (int64_t)bg * a.ld_kv * D;
@@ -201,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
             const int j = j_lo + nt * 16 + ln;
             if (j < j_hi) {
                 int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
-                for (int i = lq; i < staged[nt]; i += 4) rec[1 + flushed[nt] + i] = st[wave][nt * 16 + ln][i];
+                for (int i = lq; i < staged[nt]; i += 4)
+                    rec[1 + ebase + flushed[nt] + i] = st[wave][nt * 16 + ln][i];
             }
             flushed[nt] += staged[nt];
             staged[nt] = 0;
@@ -323,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
 #endif
         }
     };
-    constexpr int64_t kStride = kWaves * 16 * U;
+    constexpr int64_t kStride = kSelWaves * 16 * U;
     int64_t t0 = t_begin + wave * 16 * U;
     if (t0 < t_end) {
         u32x4 ka[U][KS], kb[U][KS];
@@ -348,18 +381,54 @@ __global__ __launch_bounds__(kThreads) void k_select(SelectArgs a) {
     }
     if constexpr (!MATERIALIZE) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        flush();
+        uint32_t mk[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            uint32_t mk = mkey[nt];
-            uint32_t o = __shfl_xor(mk, 16);
-            mk = mk > o ? mk : o;
-            o = __shfl_xor(mk, 32);
-            mk = mk > o ? mk : o;
-            const int j = j_lo + nt * 16 + ln;
-            if (lq == 0 && j < j_hi) {
-                int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
-                rec[0] = int2{flushed[nt], (int)mk};
+            uint32_t m = mkey[nt];
+            uint32_t o = __shfl_xor(m, 16);
+            m = m > o ? m : o;
+            o = __shfl_xor(m, 32);
+            mk[nt] = m > o ? m : o;
+        }
+        // Launched with four waves (chunks of four groups) the lower waves
+        // write their records' heads themselves.
+        const bool pairs = blockDim.x > kThreads;  // block-uniform
+        if (up == 0) {  // wave-uniform: the lower wave's list is final
+            flush();
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int j = j_lo + nt * 16 + ln;
+                if (lq == 0 && pairs) xlo[sw][nt * 16 + ln] = int2{flushed[nt], (int)mk[nt]};
+                if (lq == 0 && !pairs && j < j_hi) {
+                    int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
+                    rec[0] = int2{flushed[nt], (int)mk[nt]};
+                }
+            }
+        }
+        if (!pairs) return;
+        __syncthreads();
+        if (up == 1) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int j = j_lo + nt * 16 + ln;
+                const int2 lo = xlo[sw][nt * 16 + ln];
+                if (j < j_hi) {
+                    int2 *rec = (int2 *)(a.seg + (((int64_t)b * a.h_q + j) * a.n_sub + sub) * a.seg_w);
+                    // Entries flushed from ebase move down to lo.x (<= ebase):
+                    // a round's store lands below every later round's load,
+                    // and the store waits for its own round's load.
+                    for (int i = lq; i < flushed[nt]; i += 4) {
+                        const int2 v = rec[1 + ebase + i];
+                        rec[1 + lo.x + i] = v;
+                    }
+                    for (int i = lq; i < staged[nt]; i += 4)
+                        rec[1 + lo.x + flushed[nt] + i] = st[wave][nt * 16 + ln][i];
+                    if (lq == 0) {
+                        const uint32_t lk = (uint32_t)lo.y;
+                        rec[0] = int2{lo.x + flushed[nt] + staged[nt],
+                                      (int)(lk > mk[nt] ? lk : mk[nt])};
+                    }
+                }
             }
         }
     }
@@ -803,8 +872,9 @@ __global__ __launch_bounds__(kThreads) void k_select_final(RadixArgs a) {
 
 // Refresh step selection from the materialised scores: A >= tau into the
 // same (row, segment) records k_select writes, in the same record order:
-// wave w of the block for (row, chunk) lists, for its record indices j =
-// 0, 1, ..., the position whose record_order_key within the segment is j.
+// wave w of the block for (row, chunk) lists segment w, for its record
+// indices j = 0, 1, ..., the position whose record_order_key within the
+// segment is j.
 struct CompactArgs {
     const float *A;
     int64_t ld_a, l_kv, chunk_len, grp;
@@ -825,6 +895,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     const float *Ar = a.A + (int64_t)row * a.ld_a;
     int2 *rec = (int2 *)(a.seg + ((int64_t)row * a.n_sub + sub) * a.seg_w);
     const int64_t tiles_per_grp = a.grp / 16;
+    const int lo_groups = seg_lo_groups((int)a.chunk_len, (int)a.grp);
     // 16 tiles of the segment per round, in record order; lane l takes tile
     // l / 4, rows 4 * (l % 4) .. +3 (one float4, output registers r = 0..3)
     const int tt = lane >> 2, lq = lane & 3;
@@ -836,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(CompactArgs a) {
     for (int64_t T0 = 0; T0 < n_tiles; T0 += 16) {
         const int64_t T = T0 + tt;  // tile of the segment, in record order
         const int64_t k = T / tiles_per_grp, u = T % tiles_per_grp;
-        const int64_t t = c0 + (k * kWaves + wave) * a.grp + u * 16 + lq * 4;
+        const int64_t t = c0 + (int64_t)seg_group_index(wave, (int)k, lo_groups) * a.grp + u * 16 + lq * 4;
         f32x4 v;
         if (T < n_tiles && t + 3 < t_end) {
             v = *(const f32x4 *)(Ar + t);
@@ -1267,22 +1338,22 @@ __global__ __launch_bounds__(kThreads) void k_append(AppendArgs a) {
 // are kThreads * 16 bytes apart, and folds the words it read with XOR.
 // Positions past the range are clamped to its last item and masked, so the
 // loads carry no branches.
-__global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4 *p, int64_t n16, int64_t per,
+__global__ __launch_bounds__(kSelThreads) void k_read_probe(const u32x4 *p, int64_t n16, int64_t per,
                                                           uint32_t *sink) {
-    __shared__ uint32_t red[kWaves];
+    __shared__ uint32_t red[kSelWaves];
     const int64_t beg = (int64_t)blockIdx.x * per;
     const int64_t end = min(n16, beg + per);
     uint32_t acc = 0u;
-    for (int64_t i = beg + threadIdx.x; i < end; i += kThreads * 8) {
+    for (int64_t i = beg + threadIdx.x; i < end; i += kSelThreads * 8) {
         u32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t k = i + (int64_t)u * kThreads;
+            const int64_t k = i + (int64_t)u * kSelThreads;
             v[u] = ld16_stream(p + (k < end ? k : end - 1));
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            if (i + (int64_t)u * kThreads < end) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+            if (i + (int64_t)u * kSelThreads < end) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
     }
     for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -1290,7 +1361,7 @@ __global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4 *p, int64_t
     if (threadIdx.x == 0) {
         uint32_t r = 0u;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) r ^= red[w];
+        for (int w = 0; w < kSelWaves; ++w) r ^= red[w];
         sink[blockIdx.x] = r;
     }
 }

@@ -10,6 +10,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+SEG_WAVES = 4  # segments per chunk (each shared by two of the select pass's waves)
+
+
+def stream_tiles(d):
+    """16-row tiles per wave iteration of the streaming select plan."""
+    return 2 * 64 // d
 
 
 def declared_functions():
@@ -90,14 +96,13 @@ def test_workspace_layout_consistent(L, shape):
     lay = saga.saga_workspace_layout(*shape)
     assert lay.bytes == nbytes
     assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
-    assert lay.n_seg == 4 * lay.n_chunk and lay.seg_cap * 4 == lay.chunk_len
+    assert lay.n_seg == SEG_WAVES * lay.n_chunk and lay.seg_cap * SEG_WAVES == lay.chunk_len
     # record groups of 16-row tiles: one tile when the streaming plan's chunks would be a single
-    # 256-row unit (short caches), at most two when they would be two units, else the streaming
-    # tile count (4 at d 64, 2 at d 128)
+    # 256-row unit (short caches), else the streaming tile count (2 at d 64, 1 at d 128)
     per = -(-(B * h_k * l_kv) // 256)
-    u = 1 if per <= 256 else min(2, 4 * 64 // d) if per <= 512 else 4 * 64 // d
+    u = 1 if per <= 256 else stream_tiles(d)
     assert lay.seg_group == 16 * u
-    assert lay.chunk_len % (4 * lay.seg_group) == 0
+    assert lay.chunk_len % (SEG_WAVES * lay.seg_group) == 0
     assert lay.n_seg <= 1024
     assert lay.scores_ld >= l_kv and lay.scores_ld % 4 == 0
     assert lay.seg_words % 16 == 0 and lay.seg_words >= 2 + 2 * lay.seg_cap
@@ -288,7 +293,7 @@ def test_chunking_monotone_over_lengths(L, d):
             assert lay.chunk_len >= prev, (B, h_k, l_kv)
             prev = lay.chunk_len
             assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
-            assert lay.n_seg == 4 * lay.n_chunk <= 1024
-            assert lay.seg_group in (16, 32, 64 * 64 // d) and lay.seg_group <= 64 * 64 // d
-            assert lay.chunk_len % (4 * lay.seg_group) == 0
-            assert lay.seg_cap * 4 == lay.chunk_len
+            assert lay.n_seg == SEG_WAVES * lay.n_chunk <= 1024
+            assert lay.seg_group in (16, 32) and lay.seg_group <= 16 * stream_tiles(d)
+            assert lay.chunk_len % (SEG_WAVES * lay.seg_group) == 0
+            assert lay.seg_cap * SEG_WAVES == lay.chunk_len

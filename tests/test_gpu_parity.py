@@ -406,8 +406,11 @@ def test_attend_windows_and_long_records():
     """Far more than 256 survivors per wave (the attend kernel's wave-local
     LDS window of 256 entries is refilled many times) and segments far
     beyond the fifteen survivors a record's first 128 bytes hold: a stale
-    tau of -inf selects every position."""
-    for (B, h_q, h_k, h_v, d, l_kv) in [(1, 8, 2, 4, 64, 10000), (2, 4, 1, 2, 128, 9001)]:
+    tau of -inf selects every position.  The last two shapes take the
+    streaming plan, whose upper waves flush survivors before the block ends
+    and move them behind their segment's lower wave."""
+    for (B, h_q, h_k, h_v, d, l_kv) in [(1, 8, 2, 4, 64, 10000), (2, 4, 1, 2, 128, 9001),
+                                        (1, 8, 2, 4, 64, 40000), (1, 4, 1, 2, 128, 70001)]:
         x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=31 + d, device="cuda", planted=8)
         Q, K, V = x["Q"][0], x["K"], x["V"]
         tau = torch.full((B, h_q), float("-inf"), dtype=torch.float32, device="cuda")
@@ -500,14 +503,19 @@ def ws_layout(B, h_q, h_k, h_v, d, l_kv, N):
 
 def record_order_keys(t, lay):
     """Rank of each position in the order the survivor records list them:
-    chunk, segment (wave w takes the chunk's row groups w, w+4, ...), group,
-    16-row tile, then row % 4 before row / 4 inside the tile."""
+    chunk; segment s = group % 4; within the segment first the groups s, s+8,
+    s+16, ... of the chunk, then s+4, s+12, ...; 16-row tile; then row % 4
+    before row / 4 inside the tile."""
     t = np.asarray(t, np.int64)
+    W = lay.n_seg // lay.n_chunk  # segments per chunk
+    G = lay.chunk_len // lay.seg_group  # groups per chunk
+    lo = -(-G // (2 * W))  # groups a segment lists before its second half
     c, o = t // lay.chunk_len, t % lay.chunk_len
     gi, i = o // lay.seg_group, o % lay.seg_group
-    w, k = gi % 4, gi // 4
+    s, half, k = gi % W, (gi // W) % 2, gi // (2 * W)
     q = i % 16
-    return c * lay.chunk_len + w * lay.seg_cap + k * lay.seg_group + (i - q) + (q % 4) * 4 + q // 4
+    return (c * lay.chunk_len + s * lay.seg_cap + (half * lo + k) * lay.seg_group + (i - q)
+            + (q % 4) * 4 + q // 4)
 
 
 def _pivot_trajectory(Q, K, V, N, R, invalid_first=False):
