@@ -228,8 +228,7 @@ typedef struct saga_ws_layout {
     int64_t n_seg;         /* segments per row (n_chunk * 4) */
     int64_t seg_cap;       /* positions covered by one segment (chunk_len / 4) */
     int64_t seg_group;     /* rows per group of a segment: 16 times the select pass's
-                              tiles per wave iteration -- 16 when ceil(B*h_k*l_kv / 256)
-                              <= 256, else 16 * 2 * 64 / d */
+                              tiles per wave iteration (16: one tile) */
 } saga_ws_layout;
 
 /* Fill *out for this shape.  Returns SAGA_OK or a negative status. */

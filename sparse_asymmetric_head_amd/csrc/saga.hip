@@ -31,6 +31,8 @@ constexpr int kMaxQueryHeads = 32768;
 #endif
 constexpr int kTargetDenseBlocks = SAGA_DENSE_BLOCKS;  // dense baseline blocks per launch
 constexpr int64_t kChunkUnit = kSelWaves * 16 * SAGA_SELECT_U;  // chunk_len granularity: one wave-iteration stride of the select block
+constexpr int64_t kDenseChunkUnit = 256;  // dense chunk granularity: whole wave iterations of k_dense
+static_assert(kDenseChunkUnit % (kWaves * 16 * SAGA_DENSE_U) == 0, "dense chunk unit");
 constexpr int64_t kHistBlock = kHistBlockMax;  // positions per histogram/collect block
 constexpr size_t kAlign = 256;
 
@@ -68,23 +70,21 @@ int check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, int64_t N
     return SAGA_OK;
 }
 
-// Chunk granularity of the short-cache plan: one 16-row tile per wave
-// iteration of the block's waves.
+// Chunk granularity of the short-cache plan: one 16-row tile for each of the
+// lower four waves (the upper four then have no rows and are not launched).
 constexpr int64_t kShortUnit = kWaves * 16;
 
-// Short cache: the streaming plan would give each wave a single iteration
-// (chunks of one 256-row unit), so the select pass takes one tile per wave
-// iteration and 64-row chunk units instead -- shorter iterations, and up to
-// kTargetSelectBlocks blocks where 256-row chunks would leave compute units
-// idle.  Monotone in l_kv: the short plan's chunks are never longer than 256
-// rows, the streaming plan's never shorter.
+// Short cache: chunks of one streaming unit (kChunkUnit rows) would leave
+// compute units idle, so the plan takes 64-row chunk units instead -- up to
+// kTargetSelectBlocks blocks.  Monotone in l_kv: the short plan's chunks are
+// never longer than kChunkUnit rows, the streaming plan's never shorter.
 bool short_plan(int64_t pairs, int64_t l_kv) {
     return ceil_div(pairs * l_kv, kTargetSelectBlocks) <= kChunkUnit;
 }
 
 // k_select tiles per wave iteration: one on the short plan, else the
-// streaming choice (2 at d 64, 1 at d 128).  Chunk lengths are multiples of
-// kWaves record groups either way (the record order needs it).
+// streaming choice (SAGA_SELECT_U, one by default).  Chunk lengths are
+// multiples of kWaves record groups either way (the record order needs it).
 int select_u(int64_t pairs, int64_t l_kv, int d) {
     if (short_plan(pairs, l_kv)) return 1;
     return d == 64 ? select_tiles<64>() : select_tiles<128>();
@@ -226,10 +226,10 @@ int make_dense_plan(int B, int h_q, int h_k, int h_v, int d, int64_t l_kv, Dense
     // head of each subset, start a run of h_q/h_v heads on one value head
     p->run = (p->nv > 1 && h_q % h_v == 0 && h_v % h_k == 0) ? h_q / h_v : 0;
     const int64_t pairs = (int64_t)B * h_k * p->n_vsub;
-    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetDenseBlocks), kChunkUnit) * kChunkUnit;
-    const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kChunkUnit) * kChunkUnit;
+    int64_t cl = ceil_div(ceil_div(pairs * l_kv, kTargetDenseBlocks), kDenseChunkUnit) * kDenseChunkUnit;
+    const int64_t cl_min = ceil_div(ceil_div(l_kv, 4096), kDenseChunkUnit) * kDenseChunkUnit;
     if (cl < cl_min) cl = cl_min;
-    if (cl < kChunkUnit) cl = kChunkUnit;
+    if (cl < kDenseChunkUnit) cl = kDenseChunkUnit;
     p->chunk_len = cl;
     p->n_chunk = (int)ceil_div(l_kv, cl);
     p->total = align_up((size_t)p->rows * p->n_chunk * (d + 4) * sizeof(float));

@@ -41,12 +41,14 @@ namespace saga {
 #define SAGA_KMAP 1  // k_select: 1 = each MFMA k-step loads contiguous 64-byte half rows
 #endif
 #ifndef SAGA_SELECT_U
-#define SAGA_SELECT_U 2  // k_select: 16-row tiles per wave iteration at d = 64 (half at d = 128)
+#define SAGA_SELECT_U 1  // k_select: 16-row tiles per wave iteration
 #endif
-// k_select's tiles per wave iteration: the streaming choice, or one tile
-// where 256-row chunks would leave compute units idle (short caches).
+// k_select's tiles per wave iteration on the streaming plan.
 template <int D>
-constexpr int select_tiles() { return SAGA_SELECT_U * 64 / D; }
+constexpr int select_tiles() { return SAGA_SELECT_U; }
+#ifndef SAGA_DENSE_U
+#define SAGA_DENSE_U 2  // k_dense: 16-row tiles per wave iteration at d = 64 (half at d = 128)
+#endif
 #ifndef SAGA_KT_LDS
 #define SAGA_KT_LDS 1  // k_select: contiguous key loads, moved into the MFMA layout through LDS
 #endif
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     const uint64_t lt_mask = (1ull << lane) - 1ull;
     const uint16_t *Kb = a.K + (int64_t)bg * a.ld_kv * D;
 
-    auto flush = [&]() {
+    auto flush = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int j = j_lo + nt * 16 + ln;
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     // Score, compare and stage one wave iteration (U tiles starting at t0).
     // INSIDE: the whole iteration lies inside the chunk (every iteration but
     // possibly the last), so the compare needs no position checks.
-    auto process = [&](const u32x4 (&kin)[U][KS], int64_t t0, auto inside_tag) {
+    auto process = [&](const u32x4 (&kin)[U][KS], int64_t t0, auto inside_tag) __attribute__((always_inline)) {
         constexpr bool INSIDE = decltype(inside_tag)::value;
 #if SAGA_KT_LDS
         // Row r, 16-byte column c of tile u sits at slot r*CPR + (c ^ (r & 7)):
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
     if (t0 < t_end) {
         u32x4 ka[U][KS], kb[U][KS];
         // a full iteration, or the chunk's partial last one
-        auto step = [&](const u32x4 (&k)[U][KS], int64_t t) {
+        auto step = [&](const u32x4 (&k)[U][KS], int64_t t) __attribute__((always_inline)) {
             if (t + 16 * U <= t_end)
                 process(k, t, std::true_type{});
             else
@@ -1424,7 +1426,7 @@ struct DenseArgs {
 template <int D, int GMAX, int NV, int RUN>
 __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     constexpr int KS = D / 32;
-    constexpr int U = NV == 1 ? SAGA_SELECT_U * 64 / D : 1;
+    constexpr int U = NV == 1 ? SAGA_DENSE_U * 64 / D : 1;
     constexpr int LPR = D / 8;          // lanes per V row
     constexpr int RPI = 64 / LPR;       // V rows per wave load
     constexpr int RPL = 16 / RPI;       // V rows per lane per tile

@@ -15,7 +15,7 @@ SEG_WAVES = 4  # segments per chunk (each shared by two of the select pass's wav
 
 def stream_tiles(d):
     """16-row tiles per wave iteration of the streaming select plan."""
-    return 2 * 64 // d
+    return 1
 
 
 def declared_functions():
@@ -97,10 +97,10 @@ def test_workspace_layout_consistent(L, shape):
     assert lay.bytes == nbytes
     assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
     assert lay.n_seg == SEG_WAVES * lay.n_chunk and lay.seg_cap * SEG_WAVES == lay.chunk_len
-    # record groups of 16-row tiles: one tile when the streaming plan's chunks would be a single
-    # 256-row unit (short caches), else the streaming tile count (2 at d 64, 1 at d 128)
+    # record groups of 16-row tiles: one tile on the short plan (at most 128 rows per block),
+    # else the streaming tile count (also one)
     per = -(-(B * h_k * l_kv) // 256)
-    u = 1 if per <= 256 else stream_tiles(d)
+    u = 1 if per <= 128 else stream_tiles(d)
     assert lay.seg_group == 16 * u
     assert lay.chunk_len % (SEG_WAVES * lay.seg_group) == 0
     assert lay.n_seg <= 1024
@@ -277,8 +277,8 @@ def test_merge_validates_before_launch(L):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_chunking_monotone_over_lengths(L, d):
-    """The select plan switches its chunk unit (64 rows with one tile per wave iteration on
-    short caches, 256 rows otherwise). A workspace sized for a cache's capacity serves every
+    """The select plan switches its chunk unit (64 rows on short caches, 128 rows
+    otherwise). A workspace sized for a cache's capacity serves every
     shorter length only if the chunk length never decreases as the cache grows, and every
     length must keep the record layout's invariants."""
     from sparse_asymmetric_head_amd import saga
@@ -294,6 +294,6 @@ def test_chunking_monotone_over_lengths(L, d):
             prev = lay.chunk_len
             assert lay.n_chunk * lay.chunk_len >= l_kv > (lay.n_chunk - 1) * lay.chunk_len
             assert lay.n_seg == SEG_WAVES * lay.n_chunk <= 1024
-            assert lay.seg_group in (16, 32) and lay.seg_group <= 16 * stream_tiles(d)
+            assert lay.seg_group == 16 * stream_tiles(d)
             assert lay.chunk_len % (SEG_WAVES * lay.seg_group) == 0
             assert lay.seg_cap * SEG_WAVES == lay.chunk_len
