@@ -25,8 +25,9 @@
 //   k_compact            A >= tau into the same records, then k_attend.
 // Dense GQA baseline: k_dense (split-KV online softmax) + k_dense_merge.
 //
-// Segment records: the survivors of one (row, segment) -- a segment is one
-// wave's share of a block's cache positions -- are stored as int32 words
+// Segment records: the survivors of one (row, segment) -- a segment is the
+// share of a block's cache positions taken by two of its eight waves, the
+// lower wave's list first -- are stored as int32 words
 //   [0] count, [1] order key of their largest score, [2+2i] position t_i,
 //   [3+2i] bits of score s_i,
 // padded to a multiple of 16 words (at least 32), so that the first 128
