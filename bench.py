@@ -372,6 +372,11 @@ def main() -> int:
         # A second pass over the same steps with one event between consecutive
         # steps gives the per-step distribution (refresh and non-refresh steps
         # apart); the events cost a little, so `value` comes from the pass above.
+        # The warmup steps run again first, so the second pass starts from the
+        # same state (the exact refresh at step 0) as the timed one.
+        for t in range(args.warmup):
+            step(t)
+        stream.synchronize()
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         evs[0].record(stream)
         for i, t in enumerate(range(args.warmup, args.warmup + args.steps)):
