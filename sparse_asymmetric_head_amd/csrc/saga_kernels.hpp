@@ -1054,13 +1054,16 @@ struct RefineArgs {
     int32_t *pivot;      // [rows][N] out: positions of N survivors, in record order
 };
 
-constexpr int kRefineCap = 8192;  // listed scores staged in LDS
+constexpr int kRefineCap = 12288;  // listed scores staged in LDS
 
 // One block per row.  The listed scores (up to kRefineCap staged in LDS with
-// their positions and segments, else read from the records on every pass)
-// go through radix digits of their order keys, from the highest bit in which
-// they differ, until the bucket holding rank N is small enough to rank its
-// keys against each other directly; that gives the exact key of rank N.
+// their positions and segments; more than that first go through one radix
+// digit read from the records, and only the keys at or above the lower edge
+// of the bucket holding rank N are staged; if even those are too many, the
+// records are read on every pass) go through radix digits of their order
+// keys, from the highest bit in which they differ, until the bucket holding
+// rank N is small enough to rank its keys against each other directly; that
+// gives the exact key of rank N.
 // The survivors (score >= tau) are then walked in record
 // order: the first N positions go to pivot, and every record is rewritten in
 // place to its survivors (same order; the max key stays right, since a record
@@ -1128,7 +1131,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     auto entry_ptr = [&](int sgi, int i) {
         return (const int2 *)(rb + (int64_t)sgi * a.seg_w) + 1 + (i - soff[sgi]);
     };
-    const bool staged = total <= kRefineCap;
+    bool staged = total <= kRefineCap;
     if (staged) {
         // the segment of every flattened entry, written by the thread that
         // owns the segment, so each staging load needs one LDS read
@@ -1157,20 +1160,101 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         }
         __syncthreads();
     }
-    auto key_at = [&](int i) {
-        return staged ? ekey[i] : fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
+    // fn(i, key) for the listed entries i = i0, i0 + di, ... below i1; from the
+    // records (too many to stage) SU loads go out together before any is used
+    auto for_keys = [&](int i0, int i1, int di, auto &&fn) __attribute__((always_inline)) {
+        if (staged) {
+            for (int i = i0; i < i1; i += di) fn(i, ekey[i]);
+            return;
+        }
+        for (int base = i0; base < i1; base += di * SU) {
+            uint32_t k[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = min(i1 - 1, base + u * di);
+                k[u] = fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u)
+                if (base + u * di < i1) fn(base + u * di, k[u]);
+        }
     };
+    if (!staged) {
+        // Too many listed to stage: one radix digit over the records finds
+        // the bucket that holds rank N; the keys at or above its lower edge
+        // (every key above tau among them) are staged in record order and
+        // the rest of the search runs on them.
+        uint32_t fmn = 0xffffffffu, fmx = 0u;
+        for_keys(tid, total, kThreads, [&](int, uint32_t k) {
+            fmn = fmn < k ? fmn : k;
+            fmx = fmx > k ? fmx : k;
+        });
+        fmn = ~wave_max_u32_dpp(~fmn);
+        fmx = wave_max_u32_dpp(fmx);
+        if (lane == 0) {
+            rmn[wave] = fmn;
+            rmx[wave] = fmx;
+        }
+        for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            fmn = fmn < rmn[w] ? fmn : rmn[w];
+            fmx = fmx > rmx[w] ? fmx : rmx[w];
+        }
+        if (fmn != fmx) {  // block-uniform; equal keys take the record path below
+            const int fhi = 31 - __clz(fmn ^ fmx);
+            const int flo = fhi > 10 ? fhi - 10 : 0;
+            const uint32_t fdm = (2u << (fhi - flo)) - 1u;  // digit = bits flo..fhi
+            for_keys(tid, total, kThreads, [&](int, uint32_t k) { atomicAdd(&h[(k >> flo) & fdm], 1u); });
+            __syncthreads();
+            find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
+            // the bucket's lower edge: the common bits above fhi, the digit, zeros below
+            const uint32_t high = fhi == 31 ? 0u : (fmn & ~((2u << fhi) - 1u));
+            const uint32_t edge = high | ((uint32_t)sel_bin << flo);
+            const int per = (total + kThreads - 1) / kThreads;
+            const int f0 = min(total, tid * per), f1 = min(total, f0 + per);
+            int fc = 0;
+            for_keys(f0, f1, 1, [&](int, uint32_t k) { fc += k >= edge; });
+            int ftot;
+            int fo = block_excl_scan<kWaves>(fc, red, &ftot);
+            if (ftot <= kRefineCap) {  // block-uniform
+                for (int base = f0; base < f1; base += SU) {  // SU entries' loads together
+                    int2 v[SU];
+                    int sg[SU];
+#pragma unroll
+                    for (int u = 0; u < SU; ++u) {
+                        const int i = min(f1 - 1, base + u);
+                        sg[u] = seg_of(i);
+                        v[u] = *entry_ptr(sg[u], i);
+                    }
+#pragma unroll
+                    for (int u = 0; u < SU; ++u) {
+                        const uint32_t k = fkey(__int_as_float(v[u].y));
+                        if (base + u < f1 && k >= edge) {
+                            epos[fo] = v[u].x;
+                            ekey[fo] = k;
+                            eseg[fo] = (uint16_t)sg[u];
+                            ++fo;
+                        }
+                    }
+                }
+                total = ftot;
+                staged = true;
+            }
+        }
+        __syncthreads();  // every read of rmn / rmx and h above is done
+    }
 
     // The listed keys agree above their highest differing bit hi.  Radix
     // digits of up to 11 bits go down from there (2048-bin LDS histograms)
     // until the bucket holding the wanted rank has at most kThreads keys,
     // which are then ranked against each other, or until every bit is fixed.
     uint32_t kmn = 0xffffffffu, kmx = 0u;
-    for (int i = tid; i < total; i += kThreads) {
-        const uint32_t k = key_at(i);
+    for_keys(tid, total, kThreads, [&](int, uint32_t k) {
         kmn = kmn < k ? kmn : k;
         kmx = kmx > k ? kmx : k;
-    }
+    });
     kmn = ~wave_max_u32_dpp(~kmn);
     kmx = wave_max_u32_dpp(kmx);
     if (lane == 0) {
@@ -1198,10 +1282,9 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
             __syncthreads();  // every read of the previous digit's histogram is done
             for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
             __syncthreads();
-            for (int i = tid; i < total; i += kThreads) {
-                const uint32_t k = key_at(i);
+            for_keys(tid, total, kThreads, [&](int, uint32_t k) {
                 if (agrees(k, pfx, hi)) atomicAdd(&h[(k >> lo) & dm], 1u);
-            }
+            });
             __syncthreads();
             find_bin_desc(h, kHistBins, rank, &sel_bin, &above, red);
             const uint32_t bin = (uint32_t)sel_bin;
@@ -1215,10 +1298,9 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         } else {
             // the cnt keys that agree with pfx above hi (any order), each
             // ranked against the others
-            for (int i = tid; i < total; i += kThreads) {
-                const uint32_t k = key_at(i);
+            for_keys(tid, total, kThreads, [&](int, uint32_t k) {
                 if (agrees(k, pfx, hi)) cand[atomicAdd(&ncand, 1)] = k;
-            }
+            });
             __syncthreads();
             if (tid < cnt) {
                 const uint32_t mine = cand[tid];
@@ -1240,20 +1322,30 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     const int per = (total + kThreads - 1) / kThreads;
     const int i0 = min(total, tid * per), i1 = min(total, i0 + per);
     int cnt = 0;
-    for (int i = i0; i < i1; ++i) {
-        if (key_at(i) >= tkey) {
+    for_keys(i0, i1, 1, [&](int i, uint32_t k) {
+        if (k >= tkey) {
             ++cnt;
             if (staged) atomicAdd(&pcnt[eseg[i]], 1);
         }
-    }
+    });
     int tot_pass;
     const int r0 = block_excl_scan<kWaves>(cnt, red, &tot_pass);
     int r = r0;
     int32_t *P = a.pivot + (int64_t)row * a.N;
-    for (int i = i0; i < i1 && r < a.N; ++i) {
-        if (key_at(i) >= tkey) {
-            P[r] = staged ? epos[i] : entry_ptr(seg_of(i), i)->x;
-            ++r;
+    if (staged) {
+        for (int i = i0; i < i1 && r < a.N; ++i)
+            if (ekey[i] >= tkey) P[r++] = epos[i];
+    } else {
+        for (int base = i0; base < i1 && r < a.N; base += SU) {  // SU entries' loads together
+            int2 v[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = min(i1 - 1, base + u);
+                v[u] = *entry_ptr(seg_of(i), i);
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u)
+                if (base + u < i1 && r < a.N && fkey(__int_as_float(v[u].y)) >= tkey) P[r++] = v[u].x;
         }
     }
     if (staged) {
