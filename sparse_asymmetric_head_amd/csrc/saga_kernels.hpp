@@ -1054,7 +1054,7 @@ struct RefineArgs {
     int32_t *pivot;      // [rows][N] out: positions of N survivors, in record order
 };
 
-constexpr int kRefineCap = 12288;  // listed scores staged in LDS
+constexpr int kRefineCap = 5120;  // listed scores staged in LDS (two blocks fit a CU)
 
 // One block per row.  The listed scores (up to kRefineCap staged in LDS with
 // their positions and segments; more than that first go through one radix
