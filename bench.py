@@ -311,34 +311,35 @@ def main() -> int:
 
     # refresh modes of saga_decode_step_pivot: 0 compare with tau, 1 full
     # exact refresh (records the pivot), 2 exact refresh from the pivot
-    def layer_pass(mode: int):
+    def layer_pass(mode: int, q):
         for l in range(L):
-            saga.saga_decode_step_pivot(qbuf[l], Ks[l], Vs[l], N, taus[l], pivots[l], mode,
+            saga.saga_decode_step_pivot(q[l], Ks[l], Vs[l], N, taus[l], pivots[l], mode,
                                         Os[l], cnts[l], ws)
 
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        qbuf.copy_(Qall[0])
-        layer_pass(1)  # eager first call: loads the kernels; first refresh of every layer
-        layer_pass(0)
+        layer_pass(1, Qall[0])  # eager first call: loads the kernels; first refresh of every layer
+        layer_pass(0, Qall[0])
     stream.synchronize()
+    # One graph per (query step, refresh) pair, each reading that step's
+    # resident queries: a step then replays one graph and copies nothing.
     graphs = {}
     if not args.no_graph:
-        for refresh in (True, False):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                layer_pass(2 if refresh else 0)
-            graphs[refresh] = g
-        log("graphs captured")
+        for i in range(T):
+            for refresh in ((i % R == 0,) if T % R == 0 else (True, False)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    layer_pass(2 if refresh else 0, Qall[i])
+                graphs[(i, refresh)] = g
+        log(f"graphs captured ({len(graphs)})")
 
     def step(t: int):
-        qbuf.copy_(Qall[t % T])
         refresh = (t % R) == 0
         if graphs:
-            graphs[refresh].replay()
+            graphs[(t % T, refresh)].replay()
         else:
-            layer_pass(2 if refresh else 0)
+            layer_pass(2 if refresh else 0, Qall[t % T])
 
     sel_counts = []
     with torch.cuda.stream(stream):
