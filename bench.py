@@ -141,6 +141,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama32-1b-128k-16L")
+    ap.add_argument("--B", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--l-kv", type=int, default=0, help="override the workload's context length")
     ap.add_argument("--R", type=int, default=0, help="override the workload's refresh period")
     ap.add_argument("--N", type=int, default=0, help="override the workload's N")
@@ -218,7 +219,8 @@ def resolve_workload(args):
     if cfg is None:
         return None
     ci = wl.config_index(cfg)
-    over = {k: v for k, v in (("l_kv", args.l_kv), ("R", args.R), ("N", args.N)) if v > 0}
+    over = {k: v for k, v in (("B", args.B), ("l_kv", args.l_kv), ("R", args.R), ("N", args.N))
+            if v > 0}
     if over:  # the same seeded recipe at another size or refresh period (a sweep point)
         cfg = cfg.with_(**over)
     k_bytes = cfg.B * cfg.h_k * cfg.l_kv * cfg.d * 2

@@ -26,6 +26,9 @@ constexpr int kTargetSelectBlocks = SAGA_SELECT_BLOCKS;  // streaming blocks per
 // Head-index products (g * h_q, j * h_v) stay below 2^30 in the kernels' 32-bit
 // arithmetic.
 constexpr int kMaxQueryHeads = 32768;
+#ifndef SAGA_ATTEND_ROW
+#define SAGA_ATTEND_ROW 1  // k_attend_row where the column-split grid is two blocks per CU or more
+#endif
 #ifndef SAGA_DENSE_BLOCKS
 #define SAGA_DENSE_BLOCKS 512
 #endif
@@ -352,6 +355,14 @@ int run_attend(const Plan &p, const void *V, float *O, int32_t *counts, char *ws
     aa.O = O;
     aa.counts = counts;
     const int64_t grid = attend_grid(p.rows, p.d);
+    if (SAGA_ATTEND_ROW && grid >= 2 * (int64_t)device_cus()) {
+        // the column split would put two or more blocks on every compute unit: a row per block
+        if (p.d == 64)
+            hipLaunchKernelGGL(k_attend_row<64>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
+        else
+            hipLaunchKernelGGL(k_attend_row<128>, dim3(p.rows), dim3(kAttendThreads), 0, s, aa);
+        return launch_status();
+    }
     const bool direct15 = grid <= device_cus();
     const bool spread = p.N > (int64_t)kRecHead * p.n_sub;
     if (p.d == 64)

@@ -19,6 +19,8 @@
 //                        fifteen of a segment straight from the record head,
 //                        the rest through a wave-local list in LDS), softmax
 //                        weights, fp32 accumulation, O.
+//   k_attend_row         the same with one block per row, for launches whose
+//                        column split would put two blocks or more on a CU.
 // Refresh (every R steps) instead runs:
 //   k_select<.., true>   same score pass, writes fp32 A
 //   k_hist / k_select1 / k_collect / k_select_final   exact radix select
@@ -469,7 +471,9 @@ __host__ __device__ constexpr int64_t attend_grid(int64_t rows, int d) {
 }
 
 constexpr int kWaveWin = 256;  // tail survivors staged per wave and window
-// Attend launch choices, made per launch by the host:
+// Attend launch choices, made per launch by the host (grids of two blocks per
+// CU or more take k_attend_row below instead, unless that kernel is compiled
+// out):
 // DIRECT  survivors per segment gathered straight from the record head: 15
 //         (every one the head holds) when one block per CU covers the grid;
 //         8 where blocks must share CUs (103 instead of 136 VGPRs, so two
@@ -699,6 +703,167 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
         }
         a.O[(int64_t)row * D + csl * kAttendCols + tid] = sl > 0.f ? so / sl : 0.f;
         if (tid == 0 && csl == 0 && a.counts) a.counts[row] = total;
+    }
+}
+
+// Row-per-block attend, for launches whose column split (d/16 blocks per row)
+// would put two blocks or more on every compute unit (the host's choice):
+// there the column-split blocks run in latency-bound rounds, each re-reading
+// the row's records, and a row's whole gather in one block wins (between one
+// and two blocks per CU the column split's two dependent round trips, against
+// three here, still win on cold caches).  One block of eight waves per row: the segment counts and max keys
+// give the row maximum M and, by a block scan, each segment's place in the
+// row's list of survivors; windows of kRowWin survivors are then staged in LDS
+// (the thread that owns a segment writes its index for each of its entries,
+// so every entry is read once, and its weight exp(s - M) computed once), and
+// gathered with d/8 lanes per value row, so each load instruction moves whole
+// 128- or 256-byte rows, U of them per lane group in flight.  Sums run in a
+// fixed order: lanes over their entries, lane groups by xor-shuffles, waves in
+// wave order.  Same clamping of counts and positions as k_attend.
+constexpr int kRowWin = 2048;  // survivors staged per window
+
+template <int D>
+__global__ __launch_bounds__(kAttendThreads) void k_attend_row(AttendArgs a) {
+    constexpr int NW = kAttendWaves;
+    constexpr int SPT = kMaxSub / kAttendThreads;  // segments per thread (2)
+    constexpr int LPR = D / 8;                     // lanes per value row, 16 bytes each
+    constexpr int RPW = kWave / LPR;               // value rows per wave load instruction
+    constexpr int U = 8;                           // value-row loads in flight per lane
+    constexpr int EPI = NW * RPW * U;              // survivors per block iteration
+    static_assert(SPT * kAttendThreads == kMaxSub, "segment split");
+    __shared__ int soff[kMaxSub + 1];
+    __shared__ uint16_t eseg[kRowWin];
+    __shared__ int epos[kRowWin];
+    __shared__ float ew[kRowWin];
+    __shared__ float wpart[NW][D];
+    __shared__ float wl[NW];
+    __shared__ uint32_t wmk[NW];
+    __shared__ int red[NW];
+
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
+    // counts (clamped to the segment capacity) and max keys of segments
+    // tid * SPT .. tid * SPT + SPT - 1
+    int c[SPT], mine = 0;
+    uint32_t mk = 0u;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int sg = tid * SPT + i;
+        const int2 hv = sg < a.n_sub ? *(const int2 *)(rb + (int64_t)sg * a.seg_w) : int2{0, 0};
+        const int n = min(max(hv.x, 0), a.sub_cap);
+        c[i] = n;
+        mine += n;
+        if (n > 0) mk = mk > (uint32_t)hv.y ? mk : (uint32_t)hv.y;
+    }
+    const int b = row / a.h_q, j = row % a.h_q;
+    const int vh = j * a.h_v / a.h_q;  // j * h_v < 2^30 (h_q <= 32768)
+    const int piece = lane % LPR, grp = lane / LPR;
+    const uint16_t *Vb = a.V + ((int64_t)b * a.h_v + vh) * a.ld_kv * D + piece * 8;
+    const uint32_t lkv_last = (uint32_t)(a.l_kv - 1);  // positions are unsigned-compared with it
+
+    int total;
+    const int pre0 = block_excl_scan<NW>(mine, red, &total);
+    mk = wave_max_u32_dpp(mk);
+    if (lane == 0) wmk[wave] = mk;
+    {
+        int o = pre0;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int sg = tid * SPT + i;
+            if (sg < a.n_sub) soff[sg] = o;
+            o += c[i];
+        }
+    }
+    __syncthreads();
+    uint32_t MK = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) MK = MK > wmk[w] ? MK : wmk[w];
+    const float M = fkey_inv(MK);  // the row maximum (only used when total > 0)
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    float lsum = 0.f;
+    for (int w0 = 0; w0 < total; w0 += kRowWin) {  // block-uniform
+        const int W = min(total - w0, kRowWin);
+        int o = pre0;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int k1 = min(o + c[i], w0 + W);
+            for (int k = max(o, w0); k < k1; ++k) eseg[k - w0] = (uint16_t)(tid * SPT + i);
+            o += c[i];
+        }
+        __syncthreads();
+        // position and weight of every entry of the window; SU loads in flight
+        constexpr int SU = 4;
+        for (int base = 0; base < W; base += kAttendThreads * SU) {
+            int2 v[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = min(W - 1, base + u * kAttendThreads + tid);
+                const int sg = eseg[i];
+                v[u] = ((const int2 *)(rb + (int64_t)sg * a.seg_w))[1 + (w0 + i - soff[sg])];
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = base + u * kAttendThreads + tid;
+                if (i < W) {
+                    const bool in = (uint32_t)v[u].x <= lkv_last;
+                    const float p = in ? expf(__int_as_float(v[u].y) - M) : 0.f;
+                    epos[i] = in ? v[u].x : -1;
+                    ew[i] = p;
+                    lsum += p;
+                }
+            }
+        }
+        __syncthreads();
+        for (int e0 = 0; e0 < W; e0 += EPI) {
+            int tt[U];
+            u32x4 vv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + (u * NW + wave) * RPW + grp;
+                tt[u] = e < W ? epos[e] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                vv[u] = (uint32_t)tt[u] <= lkv_last ? ld16(Vb + (int64_t)tt[u] * D)
+                                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if ((uint32_t)tt[u] <= lkv_last) {
+                    const float p = ew[e0 + (u * NW + wave) * RPW + grp];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] += p * bf_lo(vv[u][i]);
+                        acc[2 * i + 1] += p * bf_hi(vv[u][i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the window's LDS is refilled next
+    }
+    // lane groups of the wave (same piece), then waves in wave order
+#pragma unroll
+    for (int o = LPR; o < kWave; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o);
+    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane < LPR) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wpart[wave][piece * 8 + i] = acc[i];
+    }
+    if (lane == 0) wl[wave] = lsum;
+    __syncthreads();
+    if (tid < D) {
+        float so = 0.f, sl = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            so += wpart[w][tid];
+            sl += wl[w];
+        }
+        a.O[(int64_t)row * D + tid] = sl > 0.f ? so / sl : 0.f;
+        if (tid == 0 && a.counts) a.counts[row] = total;
     }
 }
 

@@ -84,7 +84,7 @@ def test_workload_names_carry_overrides_and_rotation():
     import argparse
 
     def args(**kw):
-        a = dict(config="llama32-1b-128k-16L", l_kv=0, R=0, N=0, caches=0)
+        a = dict(config="llama32-1b-128k-16L", B=0, l_kv=0, R=0, N=0, caches=0)
         a.update(kw)
         return argparse.Namespace(**a)
 
@@ -95,6 +95,8 @@ def test_workload_names_carry_overrides_and_rotation():
     cfg, ci, name, L, shape = bench.resolve_workload(args(l_kv=4096, R=4))
     assert name == "llama32-1b-128k-16L l_kv=4096 R=4" and shape["R"] == 4
     assert bench.traffic_file(name).endswith("traffic_llama32-1b-128k-16L_l_kv4096_R4.json")
+    cfg, ci, name, L, shape = bench.resolve_workload(args(B=4))
+    assert name == "llama32-1b-128k-16L B=4" and shape["B"] == 4 and cfg.B == 4
     assert bench.resolve_workload(args(config="nope")) is None
 
 

@@ -73,8 +73,9 @@ SMALL = [
     (3, 4, 2, 3, 128, 17, 5, 2, 3, 2),         # l_kv shorter than one tile
     (1, 4, 2, 2, 64, 1, 1, 1, 2, 0),           # a single cache position
     (1, 32768, 512, 1024, 64, 40, 6, 2, 2, 0),  # the largest head count, groups of 64
-    (4, 32, 4, 16, 64, 2000, 600, 2, 3, 16),   # many rows, few long segments (attend spreads them)
+    (4, 32, 4, 16, 64, 2000, 600, 2, 3, 16),   # 128 rows, few long segments: a block per row in attend
     (1, 8, 2, 4, 128, 1200, 900, 2, 3, 8),     # d = 128, few rows, long segments
+    (16, 32, 2, 32, 128, 2000, 200, 2, 3, 16), # 512 rows: a block per row in the attend kernel
 ]
 
 
@@ -463,6 +464,47 @@ def test_attend_mixed_counts_and_many_segments():
         assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL
 
 
+def test_attend_row_per_block():
+    """Launches whose column split would put two attend blocks or more on
+    every compute unit (256 and 512 rows here) take the row-per-block attend
+    kernel: every position selected (more than
+    its 2048-survivor LDS window, so the window is refilled), about a third of
+    each row, and per-row thresholds from a few survivors to half the row, all
+    against the oracle on the GPU's selection; repeated calls are bitwise
+    equal."""
+    for (B, h_q, h_k, h_v, d, l_kv) in [(16, 32, 2, 32, 128, 3000), (8, 32, 4, 16, 64, 5001)]:
+        print(f"[parity] attend rows B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} l_kv={l_kv}",
+              flush=True)
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=77 + d, device="cuda", planted=8)
+        Q, K, V = x["Q"][0], x["K"], x["V"]
+        A = oracle.scores(bits(Q), bits(K), h_k)
+        qs = [0.999, 0.66, 0.995, 0.5]
+        t_mixed = np.empty((B, h_q), np.float32)
+        for bb in range(B):
+            for j in range(h_q):
+                t_mixed[bb, j] = np.quantile(A[bb, j], qs[(bb * h_q + j) % len(qs)])
+        thresholds = [np.full((B, h_q), -np.inf, np.float32),
+                      np.quantile(A, 0.66, axis=-1).astype(np.float32), t_mixed]
+        for k, t in enumerate(thresholds):
+            tau = torch.from_numpy(t).cuda()
+            O, cnt, ws = _step(Q, K, V, 16, tau, False)
+            m = read_mask(ws, (B, h_q, h_k, h_v, d, l_kv), 16)
+            if k == 0:
+                assert (cnt == l_kv).all()
+            else:
+                for bb in range(B):
+                    for j in range(h_q):
+                        check_selection(m[bb, j], A[bb, j], float(t[bb, j]), f"b={bb} j={j}")
+            Og, cg = oracle.given_mask(bits(Q), bits(K), bits(V), h_k, h_v, m)
+            assert np.array_equal(cg, cnt.cpu().numpy())
+            assert rel_err(O.cpu().numpy().astype(np.float64), Og) <= OUT_RTOL, f"threshold {k}"
+            O2 = torch.empty_like(O)
+            c2 = torch.empty_like(cnt)
+            saga.saga_attend(V, B, h_q, h_k, 16, O2, c2, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(O, O2) and torch.equal(cnt, c2)
+
+
 def test_read_probe_checksum():
     """The measurement probe reads every 16-byte item of its buffer exactly
     once: the XOR of its per-workgroup folds equals the XOR of all words."""
@@ -762,15 +804,17 @@ def test_pivot_refresh_stress_batch16_sampled():
 
 def test_attend_on_fresh_workspace_is_empty():
     """saga_attend on a freshly initialised workspace (every record empty) gives
-    O = 0 and counts = 0."""
-    B, h_q, h_k, h_v, d, l_kv, N = 2, 8, 2, 4, 64, 5000, 40
-    x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=3, device="cuda")
-    ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
-    O = torch.full((B, h_q, d), float("nan"), device="cuda")
-    cnt = torch.full((B, h_q), -1, dtype=torch.int32, device="cuda")
-    saga.saga_attend(x["V"], B, h_q, h_k, N, O, cnt, ws)
-    torch.cuda.synchronize()
-    assert (cnt == 0).all() and (O == 0).all()
+    O = 0 and counts = 0, with the column-split kernel (16 rows) and the
+    row-per-block kernel (512 rows)."""
+    for (B, h_q, h_k, h_v, d, l_kv, N) in [(2, 8, 2, 4, 64, 5000, 40),
+                                           (16, 32, 2, 32, 128, 3000, 40)]:
+        x = wl.make_random(B, h_q, h_k, h_v, d, l_kv, seed=3, device="cuda")
+        ws = saga.alloc_workspace(saga.saga_workspace_bytes(B, h_q, h_k, h_v, d, l_kv, N))
+        O = torch.full((B, h_q, d), float("nan"), device="cuda")
+        cnt = torch.full((B, h_q), -1, dtype=torch.int32, device="cuda")
+        saga.saga_attend(x["V"], B, h_q, h_k, N, O, cnt, ws)
+        torch.cuda.synchronize()
+        assert (cnt == 0).all() and (O == 0).all()
 
 
 def test_workspace_reused_for_larger_batch_refreshes_exactly():
