@@ -594,6 +594,7 @@ PIVOT_CASES = [
     (2, 6, 4, 5, 64, 3001, 37, 2, 5, 8, 0.05),
     (1, 8, 2, 4, 64, 30000, 64, 2, 5, 0, 3.0),   # the query changes a lot between refreshes
     (1, 32768, 512, 1024, 64, 300, 8, 2, 4, 0, 0.05),  # the largest head count
+    (4, 32, 4, 16, 64, 20000, 256, 3, 7, 32, 0.05),   # 128 rows: a block per row in attend
 ]
 
 
@@ -644,6 +645,7 @@ CACHE_CASES = [
     (1, 8, 2, 4, 64, 32760, 12, 128, 3),   # the chunking changes at 32768 positions
     (2, 12, 1, 4, 128, 3001, 9, 50, 4),
     (1, 32, 4, 16, 64, 32762, 10, 256, 4),  # Llama shape across the 32K select-plan change
+    (4, 32, 4, 16, 64, 5000, 8, 64, 4),     # 128 rows: a block per row in attend
 ]
 
 
