@@ -1253,6 +1253,112 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     int32_t *rb = a.seg + (int64_t)row * a.n_sub * a.seg_w;
 
+    int total = 0;
+    bool staged = false;
+    uint32_t kmn = 0xffffffffu, kmx = 0u;  // least and largest listed key
+    // segment of flattened entry i (soff is non-decreasing)
+    auto seg_of = [&](int i) {
+        int lo = 0, hi = a.n_sub - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (soff[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    auto entry_ptr = [&](int sgi, int i) {
+        return (const int2 *)(rb + (int64_t)sgi * a.seg_w) + 1 + (i - soff[sgi]);
+    };
+
+    // Rows of at most kThreads segments whose listing fits the LDS: a thread
+    // per segment reads the record head (count, max key, first kRecHead
+    // entries) in one 128-byte read, the block scan places the segment, and
+    // the thread stages its entries (reading any past the head, SU at a time)
+    // with their keys' least and largest value -- one read round instead of
+    // counts, then entries, then a pass for the key range.
+    bool fast = false;
+    if (a.n_sub <= kThreads) {  // block-uniform
+        const int sgi = tid;
+        u32x4 hd[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            hd[q] = sgi < a.n_sub ? ld16(rb + (int64_t)sgi * a.seg_w + q * 4) : u32x4{0u, 0u, 0u, 0u};
+        const int n = min(max((int)hd[0][0], 0), (int)a.sub_cap);
+        const int o = block_excl_scan<kWaves>(n, red, &total);
+        if (total > 0 && total <= kRefineCap) {  // block-uniform
+            fast = staged = true;
+            uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+            for (int k = 0; k < kRecHead; ++k)
+                if (k < n) {
+                    const uint32_t key = fkey(__uint_as_float(hd[(3 + 2 * k) / 4][(3 + 2 * k) % 4]));
+                    epos[o + k] = (int)hd[(2 + 2 * k) / 4][(2 + 2 * k) % 4];
+                    ekey[o + k] = key;
+                    eseg[o + k] = (uint16_t)sgi;
+                    mn = mn < key ? mn : key;
+                    mx = mx > key ? mx : key;
+                }
+            const int2 *es = (const int2 *)(rb + (int64_t)sgi * a.seg_w) + 1;
+            for (int k0 = kRecHead; k0 < n; k0 += SU) {
+                int2 v[SU];
+#pragma unroll
+                for (int u = 0; u < SU; ++u) v[u] = es[min(n - 1, k0 + u)];
+#pragma unroll
+                for (int u = 0; u < SU; ++u)
+                    if (k0 + u < n) {
+                        const uint32_t key = fkey(__int_as_float(v[u].y));
+                        epos[o + k0 + u] = v[u].x;
+                        ekey[o + k0 + u] = key;
+                        eseg[o + k0 + u] = (uint16_t)sgi;
+                        mn = mn < key ? mn : key;
+                        mx = mx > key ? mx : key;
+                    }
+            }
+            if (sgi < a.n_sub) {
+                soff[sgi] = o;
+                pcnt[sgi] = 0;
+            }
+            if (tid == 0) {
+                soff[a.n_sub] = total;
+                sel_bin = 0;
+                above = 0u;
+                ncand = 0;
+            }
+            mn = ~wave_max_u32_dpp(~mn);
+            mx = wave_max_u32_dpp(mx);
+            if (lane == 0) {
+                rmn[wave] = mn;
+                rmx[wave] = mx;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                kmn = kmn < rmn[w] ? kmn : rmn[w];
+                kmx = kmx > rmx[w] ? kmx : rmx[w];
+            }
+        }
+    }
+    // fn(i, key) for the listed entries i = i0, i0 + di, ... below i1; from the
+    // records (too many to stage) SU loads go out together before any is used
+    auto for_keys = [&](int i0, int i1, int di, auto &&fn) __attribute__((always_inline)) {
+        if (staged) {
+            for (int i = i0; i < i1; i += di) fn(i, ekey[i]);
+            return;
+        }
+        for (int base = i0; base < i1; base += di * SU) {
+            uint32_t k[SU];
+#pragma unroll
+            for (int u = 0; u < SU; ++u) {
+                const int i = min(i1 - 1, base + u * di);
+                k[u] = fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
+            }
+#pragma unroll
+            for (int u = 0; u < SU; ++u)
+                if (base + u * di < i1) fn(base + u * di, k[u]);
+        }
+    };
+
+    if (!fast) {
     // segment counts -> offsets of the flattened list
     int c[SPT], mine = 0;
 #pragma unroll
@@ -1263,7 +1369,6 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         c[i] = n;
         mine += n;
     }
-    int total;
     const int pre0 = block_excl_scan<kWaves>(mine, red, &total);
     int pre = pre0;
 #pragma unroll
@@ -1283,20 +1388,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     }
     __syncthreads();
     if (total == 0) return;  // block-uniform; no survivors listed (cannot happen for N >= 1)
-    // segment of flattened entry i (soff is non-decreasing)
-    auto seg_of = [&](int i) {
-        int lo = 0, hi = a.n_sub - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (soff[mid] <= i) lo = mid;
-            else hi = mid - 1;
-        }
-        return lo;
-    };
-    auto entry_ptr = [&](int sgi, int i) {
-        return (const int2 *)(rb + (int64_t)sgi * a.seg_w) + 1 + (i - soff[sgi]);
-    };
-    bool staged = total <= kRefineCap;
+    staged = total <= kRefineCap;
     if (staged) {
         // the segment of every flattened entry, written by the thread that
         // owns the segment, so each staging load needs one LDS read
@@ -1325,25 +1417,6 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         }
         __syncthreads();
     }
-    // fn(i, key) for the listed entries i = i0, i0 + di, ... below i1; from the
-    // records (too many to stage) SU loads go out together before any is used
-    auto for_keys = [&](int i0, int i1, int di, auto &&fn) __attribute__((always_inline)) {
-        if (staged) {
-            for (int i = i0; i < i1; i += di) fn(i, ekey[i]);
-            return;
-        }
-        for (int base = i0; base < i1; base += di * SU) {
-            uint32_t k[SU];
-#pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int i = min(i1 - 1, base + u * di);
-                k[u] = fkey(__int_as_float(entry_ptr(seg_of(i), i)->y));
-            }
-#pragma unroll
-            for (int u = 0; u < SU; ++u)
-                if (base + u * di < i1) fn(base + u * di, k[u]);
-        }
-    };
     if (!staged) {
         // Too many listed to stage: one radix digit over the records finds
         // the bucket that holds rank N; the keys at or above its lower edge
@@ -1411,20 +1484,16 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         __syncthreads();  // every read of rmn / rmx and h above is done
     }
 
-    // The listed keys agree above their highest differing bit hi.  Radix
-    // digits of up to 11 bits go down from there (2048-bin LDS histograms)
-    // until the bucket holding the wanted rank has at most kThreads keys,
-    // which are then ranked against each other, or until every bit is fixed.
-    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    uint32_t fmn = 0xffffffffu, fmx = 0u;
     for_keys(tid, total, kThreads, [&](int, uint32_t k) {
-        kmn = kmn < k ? kmn : k;
-        kmx = kmx > k ? kmx : k;
+        fmn = fmn < k ? fmn : k;
+        fmx = fmx > k ? fmx : k;
     });
-    kmn = ~wave_max_u32_dpp(~kmn);
-    kmx = wave_max_u32_dpp(kmx);
+    fmn = ~wave_max_u32_dpp(~fmn);
+    fmx = wave_max_u32_dpp(fmx);
     if (lane == 0) {
-        rmn[wave] = kmn;
-        rmx[wave] = kmx;
+        rmn[wave] = fmn;
+        rmx[wave] = fmx;
     }
     __syncthreads();
 #pragma unroll
@@ -1432,6 +1501,12 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         kmn = kmn < rmn[w] ? kmn : rmn[w];
         kmx = kmx > rmx[w] ? kmx : rmx[w];
     }
+    }  // !fast
+
+    // The listed keys agree above their highest differing bit hi.  Radix
+    // digits of up to 11 bits go down from there (2048-bin LDS histograms)
+    // until the bucket holding the wanted rank has at most kThreads keys,
+    // which are then ranked against each other, or until every bit is fixed.
     if (tid == 0) sel_key = kmn;  // (the bound lists at least N keys; this is never kept)
     // keys that agree with p above bit h (h = -1: equal keys)
     auto agrees = [](uint32_t k, uint32_t p, int h) { return ((uint64_t)(k ^ p) >> (h + 1)) == 0; };
