@@ -1277,6 +1277,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     // with their keys' least and largest value -- one read round instead of
     // counts, then entries, then a pass for the key range.
     bool fast = false;
+    int f_off = 0, f_n = 0;  // fast: this thread's segment's entries in the staged list
     if (a.n_sub <= kThreads) {  // block-uniform
         const int sgi = tid;
         u32x4 hd[8];
@@ -1287,6 +1288,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         const int o = block_excl_scan<kWaves>(n, red, &total);
         if (total > 0 && total <= kRefineCap) {  // block-uniform
             fast = staged = true;
+            f_off = o, f_n = n;
             uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
             for (int k = 0; k < kRecHead; ++k)
@@ -1557,6 +1559,30 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
         }
     }
     if (tid == 0) a.tau[row] = fkey_inv(tkey);
+
+    if (fast) {
+        // the thread's segment: its survivors' rank in record order (one scan),
+        // the first N of the row to pivot, and its record rewritten in place
+        // from the staged copy
+        int cnt = 0;
+        for (int k = 0; k < f_n; ++k) cnt += ekey[f_off + k] >= tkey;
+        int tot_pass;
+        int r = block_excl_scan<kWaves>(cnt, red, &tot_pass);
+        int32_t *P = a.pivot + (int64_t)row * a.N;
+        int2 *dst = (int2 *)(rb + (int64_t)tid * a.seg_w) + 1;
+        int kept = 0;
+        for (int k = 0; k < f_n; ++k) {
+            const uint32_t key = ekey[f_off + k];
+            if (key >= tkey) {
+                const int t = epos[f_off + k];
+                if (r < a.N) P[r] = t;
+                dst[kept++] = int2{t, __float_as_int(fkey_inv(key))};
+                ++r;
+            }
+        }
+        if (tid < a.n_sub) rb[(int64_t)tid * a.seg_w] = kept;  // new count; the key word stays
+        return;
+    }
 
     // survivors per segment, their record-order ranks, the first N -> pivot
     const int per = (total + kThreads - 1) / kThreads;
