@@ -595,6 +595,9 @@ PIVOT_CASES = [
     (1, 8, 2, 4, 64, 30000, 64, 2, 5, 0, 3.0),   # the query changes a lot between refreshes
     (1, 32768, 512, 1024, 64, 300, 8, 2, 4, 0, 0.05),  # the largest head count
     (4, 32, 4, 16, 64, 20000, 256, 3, 7, 32, 0.05),   # 128 rows: a block per row in attend
+    # 256 segments of 64 positions and N = 2048: the refine stages a thread per segment and
+    # reads the entries past each record head (more than fifteen listed per segment)
+    (1, 16, 4, 8, 64, 16384, 2048, 2, 5, 32, 0.05),
 ]
 
 
