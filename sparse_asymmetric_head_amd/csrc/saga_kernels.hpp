@@ -1361,69 +1361,131 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
     };
 
     if (!fast) {
-    // segment counts -> offsets of the flattened list
-    int c[SPT], mine = 0;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-        const int sgi = tid * SPT + i;
-        int n = sgi < a.n_sub ? rb[(int64_t)sgi * a.seg_w] : 0;
-        n = n < 0 ? 0 : (n > a.sub_cap ? (int)a.sub_cap : n);
-        c[i] = n;
-        mine += n;
-    }
-    const int pre0 = block_excl_scan<kWaves>(mine, red, &total);
-    int pre = pre0;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-        const int sgi = tid * SPT + i;
-        if (sgi < a.n_sub) {
-            soff[sgi] = pre;
-            pcnt[sgi] = 0;
-        }
-        pre += c[i];
-    }
-    if (tid == 0) {
-        soff[a.n_sub] = total;
-        sel_bin = 0;
-        above = 0u;
-        ncand = 0;
-    }
-    __syncthreads();
-    if (total == 0) return;  // block-uniform; no survivors listed (cannot happen for N >= 1)
-    staged = total <= kRefineCap;
-    if (staged) {
-        // the segment of every flattened entry, written by the thread that
-        // owns the segment, so each staging load needs one LDS read
-        int o = pre0;
+        // segment counts -> offsets of the flattened list
+        int c[SPT], mine = 0;
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
-            for (int k = 0; k < c[i]; ++k) eseg[o + k] = (uint16_t)(tid * SPT + i);
-            o += c[i];
+            const int sgi = tid * SPT + i;
+            int n = sgi < a.n_sub ? rb[(int64_t)sgi * a.seg_w] : 0;
+            n = n < 0 ? 0 : (n > a.sub_cap ? (int)a.sub_cap : n);
+            c[i] = n;
+            mine += n;
+        }
+        const int pre0 = block_excl_scan<kWaves>(mine, red, &total);
+        int pre = pre0;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const int sgi = tid * SPT + i;
+            if (sgi < a.n_sub) {
+                soff[sgi] = pre;
+                pcnt[sgi] = 0;
+            }
+            pre += c[i];
+        }
+        if (tid == 0) {
+            soff[a.n_sub] = total;
+            sel_bin = 0;
+            above = 0u;
+            ncand = 0;
         }
         __syncthreads();
-        for (int base = 0; base < total; base += kThreads * SU) {
-            int2 v[SU];
+        if (total == 0) return;  // block-uniform; no survivors listed (cannot happen for N >= 1)
+        staged = total <= kRefineCap;
+        if (staged) {
+            // the segment of every flattened entry, written by the thread that
+            // owns the segment, so each staging load needs one LDS read
+            int o = pre0;
 #pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int i = min(total - 1, base + u * kThreads + tid);
-                v[u] = *entry_ptr(eseg[i], i);
+            for (int i = 0; i < SPT; ++i) {
+                for (int k = 0; k < c[i]; ++k) eseg[o + k] = (uint16_t)(tid * SPT + i);
+                o += c[i];
             }
+            __syncthreads();
+            for (int base = 0; base < total; base += kThreads * SU) {
+                int2 v[SU];
 #pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int i = base + u * kThreads + tid;
-                if (i < total) {
-                    epos[i] = v[u].x;
-                    ekey[i] = fkey(__int_as_float(v[u].y));
+                for (int u = 0; u < SU; ++u) {
+                    const int i = min(total - 1, base + u * kThreads + tid);
+                    v[u] = *entry_ptr(eseg[i], i);
+                }
+#pragma unroll
+                for (int u = 0; u < SU; ++u) {
+                    const int i = base + u * kThreads + tid;
+                    if (i < total) {
+                        epos[i] = v[u].x;
+                        ekey[i] = fkey(__int_as_float(v[u].y));
+                    }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
-    }
-    if (!staged) {
-        // Too many listed to stage: one radix digit over the records finds
-        // the bucket that holds rank N; the keys at or above its lower edge
-        // (every key above tau among them) are staged in record order and
-        // the rest of the search runs on them.
+        if (!staged) {
+            // Too many listed to stage: one radix digit over the records finds
+            // the bucket that holds rank N; the keys at or above its lower edge
+            // (every key above tau among them) are staged in record order and
+            // the rest of the search runs on them.
+            uint32_t fmn = 0xffffffffu, fmx = 0u;
+            for_keys(tid, total, kThreads, [&](int, uint32_t k) {
+                fmn = fmn < k ? fmn : k;
+                fmx = fmx > k ? fmx : k;
+            });
+            fmn = ~wave_max_u32_dpp(~fmn);
+            fmx = wave_max_u32_dpp(fmx);
+            if (lane == 0) {
+                rmn[wave] = fmn;
+                rmx[wave] = fmx;
+            }
+            for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                fmn = fmn < rmn[w] ? fmn : rmn[w];
+                fmx = fmx > rmx[w] ? fmx : rmx[w];
+            }
+            if (fmn != fmx) {  // block-uniform; equal keys take the record path below
+                const int fhi = 31 - __clz(fmn ^ fmx);
+                const int flo = fhi > 10 ? fhi - 10 : 0;
+                const uint32_t fdm = (2u << (fhi - flo)) - 1u;  // digit = bits flo..fhi
+                for_keys(tid, total, kThreads, [&](int, uint32_t k) { atomicAdd(&h[(k >> flo) & fdm], 1u); });
+                __syncthreads();
+                find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
+                // the bucket's lower edge: the common bits above fhi, the digit, zeros below
+                const uint32_t high = fhi == 31 ? 0u : (fmn & ~((2u << fhi) - 1u));
+                const uint32_t edge = high | ((uint32_t)sel_bin << flo);
+                const int per = (total + kThreads - 1) / kThreads;
+                const int f0 = min(total, tid * per), f1 = min(total, f0 + per);
+                int fc = 0;
+                for_keys(f0, f1, 1, [&](int, uint32_t k) { fc += k >= edge; });
+                int ftot;
+                int fo = block_excl_scan<kWaves>(fc, red, &ftot);
+                if (ftot <= kRefineCap) {  // block-uniform
+                    for (int base = f0; base < f1; base += SU) {  // SU entries' loads together
+                        int2 v[SU];
+                        int sg[SU];
+#pragma unroll
+                        for (int u = 0; u < SU; ++u) {
+                            const int i = min(f1 - 1, base + u);
+                            sg[u] = seg_of(i);
+                            v[u] = *entry_ptr(sg[u], i);
+                        }
+#pragma unroll
+                        for (int u = 0; u < SU; ++u) {
+                            const uint32_t k = fkey(__int_as_float(v[u].y));
+                            if (base + u < f1 && k >= edge) {
+                                epos[fo] = v[u].x;
+                                ekey[fo] = k;
+                                eseg[fo] = (uint16_t)sg[u];
+                                ++fo;
+                            }
+                        }
+                    }
+                    total = ftot;
+                    staged = true;
+                }
+            }
+            __syncthreads();  // every read of rmn / rmx and h above is done
+        }
+
         uint32_t fmn = 0xffffffffu, fmx = 0u;
         for_keys(tid, total, kThreads, [&](int, uint32_t k) {
             fmn = fmn < k ? fmn : k;
@@ -1435,74 +1497,12 @@ __global__ __launch_bounds__(kThreads) void k_refine(RefineArgs a) {
             rmn[wave] = fmn;
             rmx[wave] = fmx;
         }
-        for (int i = tid; i < kHistBins; i += kThreads) h[i] = 0u;
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            fmn = fmn < rmn[w] ? fmn : rmn[w];
-            fmx = fmx > rmx[w] ? fmx : rmx[w];
+            kmn = kmn < rmn[w] ? kmn : rmn[w];
+            kmx = kmx > rmx[w] ? kmx : rmx[w];
         }
-        if (fmn != fmx) {  // block-uniform; equal keys take the record path below
-            const int fhi = 31 - __clz(fmn ^ fmx);
-            const int flo = fhi > 10 ? fhi - 10 : 0;
-            const uint32_t fdm = (2u << (fhi - flo)) - 1u;  // digit = bits flo..fhi
-            for_keys(tid, total, kThreads, [&](int, uint32_t k) { atomicAdd(&h[(k >> flo) & fdm], 1u); });
-            __syncthreads();
-            find_bin_desc(h, kHistBins, (uint32_t)a.N, &sel_bin, &above, red);
-            // the bucket's lower edge: the common bits above fhi, the digit, zeros below
-            const uint32_t high = fhi == 31 ? 0u : (fmn & ~((2u << fhi) - 1u));
-            const uint32_t edge = high | ((uint32_t)sel_bin << flo);
-            const int per = (total + kThreads - 1) / kThreads;
-            const int f0 = min(total, tid * per), f1 = min(total, f0 + per);
-            int fc = 0;
-            for_keys(f0, f1, 1, [&](int, uint32_t k) { fc += k >= edge; });
-            int ftot;
-            int fo = block_excl_scan<kWaves>(fc, red, &ftot);
-            if (ftot <= kRefineCap) {  // block-uniform
-                for (int base = f0; base < f1; base += SU) {  // SU entries' loads together
-                    int2 v[SU];
-                    int sg[SU];
-#pragma unroll
-                    for (int u = 0; u < SU; ++u) {
-                        const int i = min(f1 - 1, base + u);
-                        sg[u] = seg_of(i);
-                        v[u] = *entry_ptr(sg[u], i);
-                    }
-#pragma unroll
-                    for (int u = 0; u < SU; ++u) {
-                        const uint32_t k = fkey(__int_as_float(v[u].y));
-                        if (base + u < f1 && k >= edge) {
-                            epos[fo] = v[u].x;
-                            ekey[fo] = k;
-                            eseg[fo] = (uint16_t)sg[u];
-                            ++fo;
-                        }
-                    }
-                }
-                total = ftot;
-                staged = true;
-            }
-        }
-        __syncthreads();  // every read of rmn / rmx and h above is done
-    }
-
-    uint32_t fmn = 0xffffffffu, fmx = 0u;
-    for_keys(tid, total, kThreads, [&](int, uint32_t k) {
-        fmn = fmn < k ? fmn : k;
-        fmx = fmx > k ? fmx : k;
-    });
-    fmn = ~wave_max_u32_dpp(~fmn);
-    fmx = wave_max_u32_dpp(fmx);
-    if (lane == 0) {
-        rmn[wave] = fmn;
-        rmx[wave] = fmx;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        kmn = kmn < rmn[w] ? kmn : rmn[w];
-        kmx = kmx > rmx[w] ? kmx : rmx[w];
-    }
     }  // !fast
 
     // The listed keys agree above their highest differing bit hi.  Radix
