@@ -117,6 +117,30 @@ __device__ __forceinline__ float row_sum_mod(float v) {
     return v;
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// u of lane l ^ 16, through the gfx950 row-pair swap (no LDS): for a lane in
+// 16-lane row R the swap's first result comes from row R & ~1, its second from
+// row R | 1.
+__device__ __forceinline__ unsigned from_xor16(unsigned u) {
+    const u32x2 h = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return (threadIdx.x & 16) ? h[0] : h[1];
+}
+// u of lane l ^ 32, through the half swap: for a lane in row R the first
+// result comes from row R & 1, the second from row 2 + (R & 1).
+__device__ __forceinline__ unsigned from_xor32(unsigned u) {
+    const u32x2 f = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return (threadIdx.x & 32) ? f[0] : f[1];
+}
+// v plus v of lane l ^ 16 (or ^ 32): the same sum as with __shfl_xor, one
+// commutative add of the same two values.
+__device__ __forceinline__ float add_xor16(float v) {
+    return v + __uint_as_float(from_xor16(__float_as_uint(v)));
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    return v + __uint_as_float(from_xor32(__float_as_uint(v)));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS traffic).
 __device__ __forceinline__ int wave_incl_scan(int x) {

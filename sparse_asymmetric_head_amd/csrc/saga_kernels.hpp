@@ -390,9 +390,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             uint32_t m = mkey[nt];
-            uint32_t o = __shfl_xor(m, 16);
+            uint32_t o = from_xor16(m);
             m = m > o ? m : o;
-            o = __shfl_xor(m, 32);
+            o = from_xor32(m);
             mk[nt] = m > o ? m : o;
         }
         // Launched with four waves (chunks of four groups) the lower waves
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<2>(acc[i]);
     l = row_sum_mod<2>(l);
-    cnt = wave_sum_i32(cnt);
+    cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
     if (lane == 0) {
         wmx[wave] = m_run;
         wcnt[wave] = cnt;
@@ -677,15 +677,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     for (int q = 0; q < kAttendWaves; ++q) M = fmaxf(M, wmx[q]);
     const float f = cnt > 0 ? expf(m_run - M) : 0.f;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float v = acc[i] * f;
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        acc[i] = v;
-    }
-    l *= f;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    for (int i = 0; i < 8; ++i) acc[i] = add_xor32(add_xor16(acc[i] * f));
+    l = add_xor32(add_xor16(l * f));
     if (lane < 2) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) wpart[wave][h * 8 + i] = acc[i];
@@ -843,12 +836,25 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_row(AttendArgs a) {
         }
         __syncthreads();  // the window's LDS is refilled next
     }
-    // lane groups of the wave (same piece), then waves in wave order
+    // lane groups of the wave (same piece), then waves in wave order; each
+    // step adds the value of lane l ^ o (within 16-lane rows by DPP, across
+    // them by the row swaps; only l ^ 4 goes through LDS)
+    auto add_xor = [](float v, int o) __attribute__((always_inline)) {
+        switch (o) {
+            case 1: return v + dppf<kDppSwapPairs>(v);
+            case 2: return v + dppf<kDppQuadXor2>(v);
+            case 8: return v + dppf<kDppRowRor8>(v);  // rotating a 16-lane row by 8 is l ^ 8
+            case 16: return add_xor16(v);
+            case 32: return add_xor32(v);
+            default: return v + __shfl_xor(v, o);
+        }
+    };
 #pragma unroll
     for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], o);
-    for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+        for (int i = 0; i < 8; ++i) acc[i] = add_xor(acc[i], o);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lsum = add_xor(lsum, o);
     if (lane < LPR) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) wpart[wave][piece * 8 + i] = acc[i];
