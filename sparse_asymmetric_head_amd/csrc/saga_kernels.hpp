@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
     }
     // Every wave learns the row maximum, rescales its own sums to it in
     // registers and adds its lanes of each column (DPP within 16-lane rows,
-    // then xor-shuffles across rows, a fixed order); one thread per column
+    // then the gfx950 row swaps across rows, a fixed order); one thread per column
     // then adds the eight waves' sums in wave order.
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = row_sum_mod<2>(acc[i]);
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend(AttendArgs a) {
 // so every entry is read once, and its weight exp(s - M) computed once), and
 // gathered with d/8 lanes per value row, so each load instruction moves whole
 // 128- or 256-byte rows, U of them per lane group in flight.  Sums run in a
-// fixed order: lanes over their entries, lane groups by xor-shuffles, waves in
+// fixed order: lanes over their entries, lane groups by DPP and row swaps, waves in
 // wave order.  Same clamping of counts and positions as k_attend.
 constexpr int kRowWin = 2048;  // survivors staged per window
 
@@ -1197,8 +1197,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
         const float sc = s * a.scale - (e * a.scale * kPivotMargin + 1e-30f);
         if (i < a.N) mn = fminf(mn, sc);
     }
-    mn = -wave_max(-mn);
-    bad = wave_sum_i32(bad);
+    mn = fkey_inv(~wave_max_u32_dpp(~fkey(mn)));  // the wave's least (keys order as the floats)
+    bad = ballot(bad != 0) != 0ull;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
         wmin[wave] = mn;
