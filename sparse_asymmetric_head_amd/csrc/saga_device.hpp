@@ -141,6 +141,19 @@ __device__ __forceinline__ float add_xor32(float v) {
     return v + __uint_as_float(from_xor32(__float_as_uint(v)));
 }
 
+// v plus v of lane l ^ O: within 16-lane rows by DPP (a rotation of a row by
+// 8 is l ^ 8), across them by the row swaps; only O = 4 goes through LDS.
+template <int O>
+__device__ __forceinline__ float add_xor(float v) {
+    static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "add_xor");
+    if constexpr (O == 1) return v + dppf<kDppSwapPairs>(v);
+    else if constexpr (O == 2) return v + dppf<kDppQuadXor2>(v);
+    else if constexpr (O == 8) return v + dppf<kDppRowRor8>(v);
+    else if constexpr (O == 16) return add_xor16(v);
+    else if constexpr (O == 32) return add_xor32(v);
+    else return v + __shfl_xor(v, O);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS traffic).
 __device__ __forceinline__ int wave_incl_scan(int x) {

@@ -837,24 +837,13 @@ __global__ __launch_bounds__(kAttendThreads) void k_attend_row(AttendArgs a) {
         __syncthreads();  // the window's LDS is refilled next
     }
     // lane groups of the wave (same piece), then waves in wave order; each
-    // step adds the value of lane l ^ o (within 16-lane rows by DPP, across
-    // them by the row swaps; only l ^ 4 goes through LDS)
-    auto add_xor = [](float v, int o) __attribute__((always_inline)) {
-        switch (o) {
-            case 1: return v + dppf<kDppSwapPairs>(v);
-            case 2: return v + dppf<kDppQuadXor2>(v);
-            case 8: return v + dppf<kDppRowRor8>(v);  // rotating a 16-lane row by 8 is l ^ 8
-            case 16: return add_xor16(v);
-            case 32: return add_xor32(v);
-            default: return v + __shfl_xor(v, o);
-        }
-    };
+    // step adds the value of lane l ^ o (add_xor: no LDS but for l ^ 4)
 #pragma unroll
-    for (int o = LPR; o < kWave; o <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = add_xor(acc[i], o);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) lsum = add_xor(lsum, o);
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (LPR <= 8) acc[i] = add_xor<8>(acc[i]);
+        acc[i] = add_xor<32>(add_xor<16>(acc[i]));
+    }
+    lsum = add_xor<1>(add_xor<2>(add_xor<4>(add_xor<8>(add_xor<16>(add_xor<32>(lsum))))));
     if (lane < LPR) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) wpart[wave][piece * 8 + i] = acc[i];
@@ -1889,8 +1878,8 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
                 tmax = fmaxf(tmax, sc[u][r]);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmaxf(tmax, __uint_as_float(from_xor16(__float_as_uint(tmax))));
+        tmax = fmaxf(tmax, __uint_as_float(from_xor32(__float_as_uint(tmax))));
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = exp2f(m_run - m_new);
         float psum = 0.f;
@@ -1902,8 +1891,7 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
                 psum += p;
                 p_lds[wave][u * 16 + lq * 4 + r][ln] = p;
             }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
+        psum = add_xor<32>(add_xor<16>(psum));
         l_run = l_run * alpha + psum;
         m_run = m_new;
         if (lq == 0) al_lds[wave][ln] = alpha;
@@ -1972,11 +1960,12 @@ __global__ __launch_bounds__(kThreads) void k_dense(DenseArgs a) {
     }
     // combine the lanes of a wave that hold the same columns
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int h = 0; h < GMAX; ++h)
 #pragma unroll
-        for (int h = 0; h < GMAX; ++h)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[h][i] += __shfl_xor(o[h][i], off);
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (LPR <= 8) o[h][i] = add_xor<8>(o[h][i]);
+            o[h][i] = add_xor<32>(add_xor<16>(o[h][i]));
+        }
     if (lq == 0) {
         wm[wave][ln] = m_run;
         wl[wave][ln] = l_run;
