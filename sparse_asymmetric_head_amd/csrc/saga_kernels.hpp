@@ -1141,32 +1141,42 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
     __shared__ int wbad[NW];
     const int row = blockIdx.x, b = row / a.h_q, j = row % a.h_q;
     const int g = j * a.h_k / a.h_q;  // j * h_k < 2^30 (h_q <= 32768)
-    float qf[D];
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 v = ld16(a.Q + (int64_t)row * D + c * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qf[c * 8 + 2 * i] = bf_lo(v[i]);
-            qf[c * 8 + 2 * i + 1] = bf_hi(v[i]);
-        }
-    }
-    const uint16_t *Kg = a.K + ((int64_t)b * a.h_k + g) * a.ld_kv * D;
+    // Each thread takes the row's 16-byte parts in its own rotated order, for
+    // the query and the key row alike: the addresses then differ across
+    // lanes, so the query row comes in vector loads issued with the position
+    // loads (at one address for the whole block it was read by two dependent
+    // scalar loads before anything else went out).  Any order of the d
+    // products is covered by the margin below.
+    // The positions of a round are loaded a round ahead, the first ones before
+    // the query, so the query's loads wait behind nothing.
     const int32_t *P = a.pivot + (int64_t)row * a.N;
+    auto positions = [&](int64_t i0, int &p, int &prev) {
+        const int64_t i = i0 + threadIdx.x;
+        const int64_t ii = i < a.N ? i : a.N - 1;
+        p = P[ii];
+        prev = ii > 0 ? P[ii - 1] : -1;
+    };
+    int p_next, prev_next;
+    positions(0, p_next, prev_next);
+    const int rot = threadIdx.x % (D / 8);
+    u32x4 qv[D / 8];
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) qv[c] = ld16(a.Q + (int64_t)row * D + ((c + rot) % (D / 8)) * 8);
+    const uint16_t *Kg = a.K + ((int64_t)b * a.h_k + g) * a.ld_kv * D;
     float mn = INFINITY;
     int bad = 0;
     for (int64_t i0 = 0; i0 < a.N; i0 += kAttendThreads) {
         const int64_t i = i0 + threadIdx.x;
         const int64_t ii = i < a.N ? i : a.N - 1;
-        const int p = P[ii];
-        const int prev = ii > 0 ? P[ii - 1] : -1;
+        const int p = p_next, prev = prev_next;
         const bool in = p >= 0 && p < a.l_kv;
         // The key row goes out as soon as p is known to be inside the cache;
         // a pivot that fails the order check makes the bound -inf anyway.
         const uint16_t *kr = Kg + (int64_t)(in ? p : 0) * D;
         u32x4 kv[D / 8];
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) kv[c] = ld16(kr + c * 8);
+        for (int c = 0; c < D / 8; ++c) kv[c] = ld16(kr + ((c + rot) % (D / 8)) * 8);
+        if (i0 + kAttendThreads < a.N) positions(i0 + kAttendThreads, p_next, prev_next);
         const int cl = (int)a.chunk_len, gp = (int)a.grp;
         const int kp = in ? record_order_key(p, cl, gp) : -1;
         const int kq = ii == 0 ? -1
@@ -1178,8 +1188,8 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
         for (int c = 0; c < D / 8; ++c)
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) {
-                const float p0 = qf[c * 8 + 2 * i2] * bf_lo(kv[c][i2]);
-                const float p1 = qf[c * 8 + 2 * i2 + 1] * bf_hi(kv[c][i2]);
+                const float p0 = bf_lo(qv[c][i2]) * bf_lo(kv[c][i2]);
+                const float p1 = bf_hi(qv[c][i2]) * bf_hi(kv[c][i2]);
                 s += p0 + p1;
                 e += fabsf(p0) + fabsf(p1);
             }
