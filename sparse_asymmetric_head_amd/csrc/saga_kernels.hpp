@@ -1141,12 +1141,14 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
     __shared__ int wbad[NW];
     const int row = blockIdx.x, b = row / a.h_q, j = row % a.h_q;
     const int g = j * a.h_k / a.h_q;  // j * h_k < 2^30 (h_q <= 32768)
-    // Each thread takes the row's 16-byte parts in its own rotated order, for
-    // the query and the key row alike: the addresses then differ across
-    // lanes, so the query row comes in vector loads issued with the position
-    // loads (at one address for the whole block it was read by two dependent
-    // scalar loads before anything else went out).  Any order of the d
-    // products is covered by the margin below.
+    // At d = 64 each thread takes the row's 16-byte parts in its own rotated
+    // order, for the query and the key row alike: the addresses then differ
+    // across lanes, so the query row comes in vector loads issued with the
+    // position loads (at one address for the whole block it was read by two
+    // dependent scalar loads before anything else went out).  Any order of the
+    // d products is covered by the margin below.  (At d = 128 the rotated
+    // vector loads made the kernel slower, 10.3 -> 12.8 us on the Qwen shape;
+    // there the row stays at one address.)
     // The positions of a round are loaded a round ahead, the first ones before
     // the query, so the query's loads wait behind nothing.
     const int32_t *P = a.pivot + (int64_t)row * a.N;
@@ -1158,7 +1160,7 @@ __global__ __launch_bounds__(kAttendThreads) void k_pivot(PivotArgs a) {
     };
     int p_next, prev_next;
     positions(0, p_next, prev_next);
-    const int rot = threadIdx.x % (D / 8);
+    const int rot = D == 64 ? threadIdx.x % (D / 8) : 0;
     u32x4 qv[D / 8];
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) qv[c] = ld16(a.Q + (int64_t)row * D + ((c + rot) % (D / 8)) * 8);
